@@ -1,0 +1,180 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) W4A4 MXFP4 linear and A16WFP4 BMM.
+ *
+ * Sources cited below:
+ *   P1  web page "[AMD] Add opt-in AITER ASM FP4 GEMM for Quark dense linear"
+ *       (sgl-project/sglang pull request 39598): Modifications, Accuracy Tests.
+ *   P2  web page "[sglang] SGLang, AMD GPU에서 Quark 모델의 FP4 GEMM 성능 최적화:
+ *       AITER ASM 활용" (analysis of that pull request with its diff), section
+ *       "2. AITER ASM FP4 GEMM 통합" (scale swizzle, activation-scale padding,
+ *       registered quantisation and GEMM ops, apply_weights).
+ *   P3  web page "[AMD] [GLM5] use tuned MXFP4 kernels for MLA absorbed BMM"
+ *       (sgl-project/sglang pull request 34317): Motivation, Modifications.
+ *   OCP-MX  OCP Microscaling Formats (MX) Specification v1.0: E2M1 elements,
+ *       E8M0 scales, conversion of a 32-value vector into one MX block.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or synchronises; each call validates its
+ *     arguments on the host, enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL is the default stream) and returns.
+ *   - Returns MXFP4_OK (0) or an mxfp4_status code; on error nothing is
+ *     enqueued.  Argument checks run before any HIP call, so they also work
+ *     on a host without a GPU.
+ *   - bf16 is IEEE binary32 truncated to its top 16 bits.  Packed FP4 holds
+ *     two E2M1 codes per byte, element 2j in the low nibble of byte j (the
+ *     float4_e2m1fn_x2 packing named in P2 §2).  Scales are E8M0 bytes,
+ *     value 2^(b-127); 0xFF (NaN) is never written, padding is 0x7F (1.0).
+ *   - K must be a positive multiple of 32 (one scale per 1x32 block).
+ *
+ * Layouts (all byte offsets; the library's own design for gfx950's
+ * 16x16x128 block-scaled FP4 MFMA):
+ *   GEMM scale layout, R rows, C = K/32 blocks, Kt = ceil(K/128),
+ *   G = ceil(Kt/4), Rp = 16*ceil(R/16):
+ *     scale (r, c): t = c/4, kb = c%4, g = t/4, j = t%4,
+ *     offset = ((r/16)*G + g)*256 + (kb*16 + r%16)*4 + j;  size Rp*G*16.
+ *   Preshuffled weight layout, per batch entry, N rows, Np = 16*ceil(N/16):
+ *     pair (n, k), k even: s = n/16, r = n%16, t = k/128, kb = (k%128)/32,
+ *     offset = ((b*Np/16 + s)*Kt + t)*1024 + (kb*16 + r)*16 + (k%32)/2;
+ *     size B*Np*Kt*64; padding bytes are 0x00.  Its scales use the GEMM
+ *     scale layout per batch entry, entries concatenated.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP4_OK = 0,
+  MXFP4_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  MXFP4_ERR_SHAPE = 2,     /* a size <= 0 (or < 0 where 0 is allowed), K % 32   */
+  MXFP4_ERR_ALIGN = 3,     /* pointer or stride not aligned as documented       */
+  MXFP4_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
+  MXFP4_ERR_DEVICE = 5,    /* the current HIP device is not gfx950              */
+  MXFP4_ERR_LAUNCH = 6,    /* a HIP launch failed                               */
+  MXFP4_ERR_ARG = 7        /* an enum argument is out of range                  */
+} mxfp4_status;
+
+enum { MXFP4_SCALES_ROWMAJOR = 0, MXFP4_SCALES_GEMM = 1 };
+enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_F32 = 1 };
+
+/* Static string naming a status code (never NULL). */
+const char* mxfp4_status_str(int status);
+
+/* ABI version: major * 100 + minor. */
+int mxfp4_abi_version(void);
+
+/* Bytes of a scale buffer for `rows` x K in `layout`: rows*K/32 for ROWMAJOR,
+ * the padded GEMM-layout size otherwise.  0 on invalid arguments. */
+size_t mxfp4_scale_bytes(int64_t rows, int64_t K, int layout);
+
+/* Bytes of the preshuffled weight data / its scales for `batch` matrices of
+ * N x K.  0 on invalid arguments. */
+size_t mxfp4_weight_bytes(int64_t batch, int64_t N, int64_t K);
+size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K);
+
+/* Workspace bytes mxfp4_gemm_a4w4 needs for this shape (may be 0). */
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Per-1x32 MXFP4 quantisation (P1 §Modifications: activations are quantised
+ * per 1x32 before the FP4 GEMM; P2 §2: the quantisation op returns packed
+ * FP4 [rows, K/2] and E8M0 scales; the scheme quantises weights the same
+ * way).  Arithmetic per OCP-MX, reading as follows: per block amax, scale
+ * byte b = max(E(amax) - 2, 0) with E the biased exponent field of amax,
+ * element |v| / 2^(b-127) rounded to the nearest E2M1 magnitude with ties to
+ * the even code and saturation at 6, sign bit copied from v.
+ *
+ *   x       bf16 [M, K], row stride ldx ELEMENTS (ldx >= K, ldx % 8 == 0,
+ *           x 16-byte aligned)
+ *   q       packed FP4 [M, K/2], row stride ldq BYTES (ldq >= K/2,
+ *           ldq % 4 == 0, q 4-byte aligned)
+ *   scales  ROWMAJOR: [M, K/32] bytes, row stride K/32;
+ *           GEMM: the GEMM scale layout for M rows, padding rows and blocks
+ *           written with 0x7F (P2 §2: pad with 1.0 because whole tiles are
+ *           read and 0xFF is NaN).  Size: mxfp4_scale_bytes(M, K, layout).
+ *   M >= 0 (M == 0 enqueues nothing), K > 0, K % 32 == 0.
+ */
+int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx,
+                     void* q, int64_t ldq, void* scales, int scale_layout,
+                     void* stream);
+
+/*
+ * Load-time weight preshuffle (P1 §Modifications and P2 §2: weights and
+ * their E8M0 scales are rearranged once after loading into the layout the
+ * FP4 GEMM reads).  Permutation only; the layout is this library's own.
+ *
+ *   w_fp4     packed FP4 [batch, N, K/2], contiguous, 16-byte aligned
+ *   w_scales  ROWMAJOR scales [batch, N, K/32], contiguous
+ *   w_out     mxfp4_weight_bytes(batch, N, K) bytes, 16-byte aligned
+ *   ws_out    mxfp4_weight_scale_bytes(batch, N, K) bytes, 4-byte aligned
+ *   batch >= 1, N >= 1, K > 0, K % 32 == 0.
+ */
+int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
+                            int64_t batch, int64_t N, int64_t K,
+                            void* w_out, void* ws_out, void* stream);
+
+/*
+ * W4A4 block-scaled FP4 GEMM with optional bias (P2 §2, apply_weights and
+ * the registered GEMM op: Y[M, N] = dq(A) dq(W)^T in the NT form of a linear
+ * layer, output (M, N), bias added after; P1 §Accuracy Tests: equal to a
+ * separately dequantised reference).  Computed as
+ *   out[m, n] = round(sum_k dq(A)[m,k] dq(W)[n,k] + bias[n])
+ * with fp32 accumulation and one round-to-nearest-even cast for bf16.
+ *
+ *   a_fp4     packed FP4 activations [M, K/2], row stride lda BYTES
+ *             (lda >= K/2, lda % 16 == 0, pointer 16-byte aligned)
+ *   a_scales  activation scales in the GEMM scale layout for M rows
+ *   w_pre     preshuffled weights (1 batch entry), ws_pre their scales
+ *   bias      bf16 [N] or NULL
+ *   out       [M, N], row stride ldo ELEMENTS, bf16 or fp32 per out_dtype
+ *             (ldo >= N; 4-byte aligned)
+ *   workspace may be NULL when mxfp4_gemm_workspace_bytes() returns 0.
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
+ */
+int mxfp4_gemm_a4w4(const void* a_fp4, int64_t lda, const void* a_scales,
+                    const void* w_pre, const void* ws_pre, const void* bias,
+                    void* out, int64_t ldo, int out_dtype,
+                    int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * A16WFP4 batched GEMM (P3 §Motivation and §Modifications: the MLA absorbed
+ * K/V projection weights stay in packed MXFP4, the batched products take
+ * bf16 activations, and the V-up result is written batch-major).  For each
+ * b < B:
+ *   out[b, m, n] = round(sum_k x[b, m, k] * dq(W)[b, n, k])
+ * with exact bf16 activations, fp32 accumulation and one RNE cast for bf16.
+ *
+ *   x      bf16, element (b, m, k) at x[b*sxb + m*sxm + k] (ELEMENTS;
+ *          sxb, sxm % 8 == 0, pointer 16-byte aligned)
+ *   w_pre  preshuffled weights of `B` matrices N x K, ws_pre their scales
+ *   out    element (b, m, n) at out[b*sob + m*som + n] (ELEMENTS; sob, som
+ *          even, pointer 4-byte aligned).  [B, M, N]: sob = M*N, som = N;
+ *          batch-major [M, B, N]: sob = N, som = B*N.
+ *   B >= 1, M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
+ */
+int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm,
+                const void* w_pre, const void* ws_pre,
+                void* out, int64_t sob, int64_t som, int out_dtype,
+                int64_t B, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Test hook, not part of the method: force the GEMM kernel used by
+ * mxfp4_gemm_a4w4 -- 1 = the small-M streaming kernel (M <= 64 only; larger
+ * M still uses the tiled kernel), 2 = the LDS-tiled kernel, 0 = choose by M
+ * (the default).  Process-wide and not synchronised with calls in flight on
+ * other threads.  Returns MXFP4_ERR_ARG for other values.
+ */
+int mxfp4_debug_set_gemm_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,237 @@
+"""W4A4 MXFP4 linear and A16WFP4 batched GEMM for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libmxfp4.so`` (C ABI in ``include/mxfp4.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only allocates output tensors with torch, passes raw device pointers and the
+current HIP stream, and turns status codes into exceptions.  There is no
+fallback: if the library is missing or the device is not gfx950, calls fail.
+
+Entry points (same names as the C ABI):
+
+* :func:`mxfp4_quant_1x32` -- bf16 [M, K] -> packed FP4 [M, K/2] + E8M0 scales
+* :func:`mxfp4_preshuffle_weight` -- quantised weights -> preshuffled layout
+* :func:`mxfp4_gemm_a4w4` -- W4A4 GEMM with optional bias, bf16/fp32 out
+* :func:`a16wfp4_bmm` -- bf16 [B, M, K] x MXFP4 [B, N, K] batched GEMM
+
+Convenience: :func:`quantize_weight` (quant + preshuffle, once at load) and
+:func:`linear` (quant of the activations + GEMM).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxfp4.so")
+
+MXFP4_SCALES_ROWMAJOR = 0
+MXFP4_SCALES_GEMM = 1
+MXFP4_OUT_BF16 = 0
+MXFP4_OUT_F32 = 1
+
+_c_i64 = ctypes.c_int64
+_c_vp = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "mxfp4_status_str": (ctypes.c_char_p, [_c_int]),
+    "mxfp4_abi_version": (_c_int, []),
+    "mxfp4_scale_bytes": (_c_size, [_c_i64, _c_i64, _c_int]),
+    "mxfp4_weight_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_weight_scale_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_gemm_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_quant_1x32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_int, _c_vp]),
+    "mxfp4_preshuffle_weight": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "mxfp4_gemm_a4w4": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
+                                 _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
+    "a16wfp4_bmm": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int,
+                             _c_i64, _c_i64, _c_i64, _c_i64, _c_vp]),
+    "mxfp4_debug_set_gemm_path": (_c_int, [_c_int]),
+}
+
+_lib_handle = None
+
+
+class MXFP4Error(RuntimeError):
+    """A libmxfp4 call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfp4.so (built in place by ``python -m mxfp4_block_scaled_quant_amd.build``)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mxfp4_block_scaled_quant_amd.build` (hipcc, gfx950)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = lib().mxfp4_status_str(status).decode()
+        raise MXFP4Error(fn, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_cuda(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
+
+
+def scale_bytes(rows: int, K: int, layout: int) -> int:
+    return int(lib().mxfp4_scale_bytes(rows, K, layout))
+
+
+def weight_bytes(batch: int, N: int, K: int) -> int:
+    return int(lib().mxfp4_weight_bytes(batch, N, K))
+
+
+def weight_scale_bytes(batch: int, N: int, K: int) -> int:
+    return int(lib().mxfp4_weight_scale_bytes(batch, N, K))
+
+
+def set_gemm_path(path: int) -> None:
+    """Test hook: 1 forces the small-M kernel (M <= 64), 2 the tiled kernel, 0 = by M."""
+    _check("mxfp4_debug_set_gemm_path", lib().mxfp4_debug_set_gemm_path(path))
+
+
+def mxfp4_quant_1x32(x: torch.Tensor, scale_layout: int = MXFP4_SCALES_GEMM,
+                     q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """Quantise bf16 rows [M, K] per 1x32 block.  Returns (q uint8 [M, K/2], scales uint8 1-D).
+
+    ``scales`` is [M*K/32] row-major for MXFP4_SCALES_ROWMAJOR, or the padded
+    GEMM layout (``scale_bytes(M, K, MXFP4_SCALES_GEMM)`` bytes).
+    """
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit stride along K")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(scale_bytes(M, K, scale_layout), dtype=torch.uint8, device=x.device)
+    _check("mxfp4_quant_1x32", lib().mxfp4_quant_1x32(
+        _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales), scale_layout,
+        _stream(x.device)))
+    return q, scales
+
+
+def mxfp4_preshuffle_weight(w_fp4: torch.Tensor, w_scales: torch.Tensor, N: int, K: int,
+                            batch: int = 1):
+    """Row-major packed FP4 weights + row-major scales -> (w_pre, ws_pre) uint8 1-D."""
+    _require_cuda(w_fp4, "w_fp4")
+    if not (w_fp4.is_contiguous() and w_scales.is_contiguous()):
+        raise ValueError("w_fp4 and w_scales must be contiguous")
+    if w_fp4.numel() != batch * N * K // 2 or w_scales.numel() != batch * N * K // 32:
+        raise ValueError("w_fp4 / w_scales sizes do not match (batch, N, K)")
+    w_pre = torch.empty(weight_bytes(batch, N, K), dtype=torch.uint8, device=w_fp4.device)
+    ws_pre = torch.empty(weight_scale_bytes(batch, N, K), dtype=torch.uint8, device=w_fp4.device)
+    _check("mxfp4_preshuffle_weight", lib().mxfp4_preshuffle_weight(
+        _ptr(w_fp4), _ptr(w_scales), batch, N, K, _ptr(w_pre), _ptr(ws_pre), _stream(w_fp4.device)))
+    return w_pre, ws_pre
+
+
+def mxfp4_gemm_a4w4(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre: torch.Tensor,
+                    ws_pre: torch.Tensor, N: int, K: int, bias: Optional[torch.Tensor] = None,
+                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """out[M, N] = dq(A) dq(W)^T (+ bias), bf16 or fp32."""
+    _require_cuda(a_fp4, "a_fp4")
+    M = a_fp4.shape[0]
+    if a_fp4.dim() != 2 or a_fp4.stride(1) != 1 or a_fp4.shape[1] != K // 2:
+        raise ValueError("a_fp4 must be [M, K/2] uint8 with unit stride along K")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
+        raise ValueError("bias must be bf16 [N]")
+    code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_fp4.device)
+    ws_bytes = int(lib().mxfp4_gemm_workspace_bytes(M, N, K))
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_fp4.device) if ws_bytes else None
+    _check("mxfp4_gemm_a4w4", lib().mxfp4_gemm_a4w4(
+        _ptr(a_fp4), a_fp4.stride(0), _ptr(a_scales), _ptr(w_pre), _ptr(ws_pre), _ptr(bias),
+        _ptr(out), out.stride(0), code, M, N, K, _ptr(workspace), ws_bytes, _stream(a_fp4.device)))
+    return out
+
+
+def a16wfp4_bmm(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: int,
+                out: Optional[torch.Tensor] = None, batch_major: bool = False,
+                out_dtype: torch.dtype = torch.bfloat16):
+    """x bf16 [B, M, K] (unit stride along K) x MXFP4 weights [B, N, K].
+
+    Returns [B, M, N], or [M, B, N] when ``batch_major`` (a caller-supplied
+    ``out`` may be any strided view with unit stride along N).
+    """
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("x must be a 3-D bf16 tensor with unit stride along K")
+    B, M, K = x.shape
+    code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
+    if out is None:
+        if batch_major:
+            out = torch.empty((M, B, N), dtype=out_dtype, device=x.device)
+        else:
+            out = torch.empty((B, M, N), dtype=out_dtype, device=x.device)
+    if batch_major:
+        sob, som = out.stride(1), out.stride(0)
+    else:
+        sob, som = out.stride(0), out.stride(1)
+    if out.stride(-1) != 1:
+        raise ValueError("out must have unit stride along N")
+    _check("a16wfp4_bmm", lib().a16wfp4_bmm(
+        _ptr(x), x.stride(0), x.stride(1), _ptr(w_pre), _ptr(ws_pre), _ptr(out), sob, som, code,
+        B, M, N, K, _stream(x.device)))
+    return out
+
+
+@dataclass
+class MXFP4Weight:
+    """Preshuffled MXFP4 weight of ``batch`` matrices N x K (device tensors)."""
+    w_pre: torch.Tensor
+    ws_pre: torch.Tensor
+    N: int
+    K: int
+    batch: int = 1
+
+
+def quantize_weight(w: torch.Tensor) -> MXFP4Weight:
+    """Load-time path: bf16 weight [N, K] or [B, N, K] -> quantise per 1x32 -> preshuffle."""
+    _require_cuda(w, "w")
+    w3 = w if w.dim() == 3 else w.unsqueeze(0)
+    B, N, K = w3.shape
+    flat = w3.reshape(B * N, K)
+    q, s = mxfp4_quant_1x32(flat, MXFP4_SCALES_ROWMAJOR)
+    w_pre, ws_pre = mxfp4_preshuffle_weight(q, s, N, K, batch=B)
+    return MXFP4Weight(w_pre, ws_pre, N, K, B)
+
+
+def linear(x: torch.Tensor, weight: MXFP4Weight, bias: Optional[torch.Tensor] = None,
+           out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """W4A4 linear: quantise bf16 activations [..., K] per 1x32, then the FP4 GEMM."""
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    q, s = mxfp4_quant_1x32(x2, MXFP4_SCALES_GEMM)
+    y = mxfp4_gemm_a4w4(q, s, weight.w_pre, weight.ws_pre, weight.N, weight.K, bias, out_dtype)
+    return y.reshape(*lead, weight.N)

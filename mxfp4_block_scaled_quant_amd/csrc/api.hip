@@ -1,0 +1,193 @@
+// C ABI of libmxfp4 (declared in include/mxfp4.h): argument validation, size
+// queries, device check and dispatch to the gfx950 kernels.  Validation runs
+// entirely on the host before any HIP call, so a rejected call enqueues
+// nothing and works on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/mxfp4.h"
+#include "mxfp4_launch.h"
+
+namespace mxfp4 {
+
+static std::atomic<int> g_gemm_path{0};
+void set_gemm_path_override(int path) { g_gemm_path.store(path); }
+int get_gemm_path_override() { return g_gemm_path.load(); }
+
+namespace {
+
+constexpr int64_t kMaxBuf = 0x7FFFFFFFll;  // buffer-resource offsets stay below 2^31
+constexpr int64_t kMaxK = 1 << 20;         // keeps per-tile 32-bit offsets far from wrapping
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t gemm_scale_bytes(int64_t rows, int64_t K) {
+  const int64_t kt = cdiv(K, 128), g = cdiv(kt, 4);
+  return cdiv(rows, 16) * g * 256;
+}
+int64_t weight_bytes_one(int64_t N, int64_t K) { return cdiv(N, 16) * cdiv(K, 128) * 1024; }
+
+// 0 = unknown, 1 = gfx950, 2 = other; per device ordinal.
+int g_dev_kind[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXFP4_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return MXFP4_ERR_DEVICE;
+  if (g_dev_kind[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXFP4_ERR_DEVICE;
+    g_dev_kind[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return g_dev_kind[dev] == 1 ? MXFP4_OK : MXFP4_ERR_DEVICE;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_LAUNCH; }
+
+}  // namespace
+}  // namespace mxfp4
+
+using namespace mxfp4;
+
+extern "C" {
+
+const char* mxfp4_status_str(int status) {
+  switch (status) {
+    case MXFP4_OK: return "ok";
+    case MXFP4_ERR_NULL: return "a required pointer is NULL";
+    case MXFP4_ERR_SHAPE: return "invalid shape (sizes must be positive and K a multiple of 32)";
+    case MXFP4_ERR_ALIGN: return "pointer or stride misaligned";
+    case MXFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXFP4_ERR_DEVICE: return "current HIP device is not gfx950 (MI355X)";
+    case MXFP4_ERR_LAUNCH: return "HIP kernel launch failed";
+    case MXFP4_ERR_ARG: return "enum argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int mxfp4_abi_version(void) { return 100; }
+
+size_t mxfp4_scale_bytes(int64_t rows, int64_t K, int layout) {
+  if (rows < 0 || K <= 0 || K % 32) return 0;
+  if (layout == MXFP4_SCALES_ROWMAJOR) return (size_t)(rows * (K / 32));
+  if (layout == MXFP4_SCALES_GEMM) return (size_t)gemm_scale_bytes(rows, K);
+  return 0;
+}
+
+size_t mxfp4_weight_bytes(int64_t batch, int64_t N, int64_t K) {
+  if (batch <= 0 || N <= 0 || K <= 0 || K % 32) return 0;
+  return (size_t)(batch * weight_bytes_one(N, K));
+}
+
+size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K) {
+  if (batch <= 0 || N <= 0 || K <= 0 || K % 32) return 0;
+  return (size_t)(batch * gemm_scale_bytes(N, K));
+}
+
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  (void)M; (void)N; (void)K;
+  return 0;
+}
+
+int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
+                     void* scales, int scale_layout, void* stream) {
+  if (scale_layout != MXFP4_SCALES_ROWMAJOR && scale_layout != MXFP4_SCALES_GEMM) return MXFP4_ERR_ARG;
+  if (M < 0 || K <= 0 || K % 32 || M > kMaxBuf || K > kMaxK) return MXFP4_ERR_SHAPE;
+  if (ldx < K || ldq < K / 2) return MXFP4_ERR_SHAPE;
+  if (mxfp4_scale_bytes(M, K, scale_layout) > (size_t)kMaxBuf) return MXFP4_ERR_SHAPE;
+  if (M == 0) return MXFP4_OK;  // nothing to read or write in either layout
+  if (!x || !q || !scales) return MXFP4_ERR_NULL;
+  if (!aligned(x, 16) || ldx % 8 || !aligned(q, 4) || ldq % 4) return MXFP4_ERR_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  return launched(launch_quant_1x32(x, M, K, ldx, q, ldq, scales, scale_layout, (hipStream_t)stream));
+}
+
+int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales, int64_t batch, int64_t N,
+                            int64_t K, void* w_out, void* ws_out, void* stream) {
+  if (batch <= 0 || N <= 0 || K <= 0 || K % 32) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf || N > kMaxBuf ||
+      K > kMaxK)
+    return MXFP4_ERR_SHAPE;
+  if (!w_fp4 || !w_scales || !w_out || !ws_out) return MXFP4_ERR_NULL;
+  if (!aligned(w_fp4, 16) || !aligned(w_out, 16) || !aligned(ws_out, 4)) return MXFP4_ERR_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  return launched(launch_preshuffle(w_fp4, w_scales, batch, N, K, w_out, ws_out, (hipStream_t)stream));
+}
+
+int mxfp4_gemm_a4w4(const void* a_fp4, int64_t lda, const void* a_scales, const void* w_pre,
+                    const void* ws_pre, const void* bias, void* out, int64_t ldo, int out_dtype,
+                    int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
+  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf) return MXFP4_ERR_SHAPE;
+  if (lda < K / 2 || ldo < N) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
+      gemm_scale_bytes(M, K) > kMaxBuf || 256 * lda > kMaxBuf || 64 * lda > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (workspace_bytes < mxfp4_gemm_workspace_bytes(M, N, K)) return MXFP4_ERR_WORKSPACE;
+  if (M == 0) return MXFP4_OK;
+  if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out) return MXFP4_ERR_NULL;
+  if (!aligned(a_fp4, 16) || lda % 16 || !aligned(a_scales, 4) || !aligned(w_pre, 16) ||
+      !aligned(ws_pre, 4) || !aligned(out, 4) || (bias && !aligned(bias, 2)))
+    return MXFP4_ERR_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  GemmArgs p;
+  p.a = (const uint8_t*)a_fp4;
+  p.lda = lda;
+  p.as = (const uint8_t*)a_scales;
+  p.w = (const uint8_t*)w_pre;
+  p.ws = (const uint8_t*)ws_pre;
+  p.bias = (const uint16_t*)bias;
+  p.out = out;
+  p.ldo = ldo;
+  p.out_f32 = out_dtype == MXFP4_OUT_F32;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.Kt = (int)cdiv(K, 128);
+  p.G = (int)cdiv(p.Kt, 4);
+  p.Ns = (int)cdiv(N, 16);
+  int path = get_gemm_path_override();
+  if (path == 0) path = M <= 64 ? 1 : 2;
+  if (path == 1 && M > 64) path = 2;  // the decode kernel covers at most 64 rows
+  hipStream_t s = (hipStream_t)stream;
+  return launched(path == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+}
+
+int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, const void* ws_pre,
+                void* out, int64_t sob, int64_t som, int out_dtype, int64_t B, int64_t M,
+                int64_t N, int64_t K, void* stream) {
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
+  if (B <= 0 || M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || B > 65535 ||
+      M > kMaxBuf || N > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (sxm < K || sxb < 0 || sob < 0 || som < 0) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
+      (64 * sxm + K) * 2 > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (M == 0) return MXFP4_OK;
+  if (!x || !w_pre || !ws_pre || !out) return MXFP4_ERR_NULL;
+  if (!aligned(x, 16) || sxb % 8 || sxm % 8 || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
+      !aligned(out, 4) || sob % 2 || som % 2)
+    return MXFP4_ERR_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  return launched(launch_bmm_a16w4(x, sxb, sxm, w_pre, ws_pre, out, sob, som,
+                                   out_dtype == MXFP4_OUT_F32, B, M, N, K, (hipStream_t)stream));
+}
+
+// Test hook: force the decode (1) or prefill (2) GEMM kernel, 0 = by M.
+int mxfp4_debug_set_gemm_path(int path) {
+  if (path < 0 || path > 2) return MXFP4_ERR_ARG;
+  set_gemm_path_override(path);
+  return MXFP4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal launchers behind the C ABI (include/mxfp4.h).  Arguments are
+// already validated by the caller; each returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+// Validated, device-side view of one W4A4 GEMM call.
+struct GemmArgs {
+  const uint8_t* a;    // packed FP4 activations [M, K/2], row stride lda bytes
+  int64_t lda;
+  const uint8_t* as;   // activation scales, GEMM scale layout
+  const uint8_t* w;    // preshuffled weights
+  const uint8_t* ws;   // weight scales, GEMM scale layout
+  const uint16_t* bias;  // bf16 [N] or nullptr
+  void* out;           // [M, N], row stride ldo elements
+  int64_t ldo;
+  int out_f32;
+  int M, N, K, Kt, G, Ns;  // Kt = ceil(K/128), G = ceil(Kt/4), Ns = ceil(N/16)
+};
+
+hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
+hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream);
+
+hipError_t launch_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q,
+                             int64_t ldq, void* scales, int layout, hipStream_t stream);
+
+hipError_t launch_preshuffle(const void* w_fp4, const void* w_scales, int64_t batch, int64_t N,
+                             int64_t K, void* w_out, void* ws_out, hipStream_t stream);
+
+hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void* w,
+                            const void* ws, void* out, int64_t sob, int64_t som, int out_f32,
+                            int64_t B, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Kernel-selection overrides used only by the tests and the benchmark to
+// exercise each GEMM path on every shape: 0 = automatic by M, 1 = decode
+// kernel, 2 = prefill kernel.
+void set_gemm_path_override(int path);
+int get_gemm_path_override();
+
+}  // namespace mxfp4

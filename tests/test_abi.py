@@ -1,0 +1,144 @@
+"""The C ABI library loads, exports every declared symbol, answers size
+queries like the oracle's layout geometry, and rejects bad arguments on the
+host before any HIP call (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from oracle import layout as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+import mxfp4_block_scaled_quant_amd as mx  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        pytest.fail("libmxfp4.so is not built (python -m mxfp4_block_scaled_quant_amd.build)")
+    return mx.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"mxfp4_quant_1x32", "mxfp4_preshuffle_weight", "mxfp4_gemm_a4w4",
+            "a16wfp4_bmm"} <= set(names)
+    raw = ctypes.CDLL(mx.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared but not exported"
+    assert set(names) <= set(mx._SIGNATURES), "binding lacks a declared function"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.mxfp4_abi_version() == 100
+    for s in range(8):
+        assert lib.mxfp4_status_str(s)
+    assert lib.mxfp4_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (16, 5120), (37, 4128), (300, 256), (8192, 14336)])
+def test_scale_bytes_match_oracle_geometry(lib, rows, K):
+    assert lib.mxfp4_scale_bytes(rows, K, 0) == rows * K // 32
+    assert lib.mxfp4_scale_bytes(rows, K, 1) == L.gemm_scale_geometry(rows, K)[3]
+
+
+@pytest.mark.parametrize("B,N,K", [(1, 96, 4128), (1, 34816, 5120), (16, 512, 192), (16, 256, 512)])
+def test_weight_bytes_match_oracle_geometry(lib, B, N, K):
+    assert lib.mxfp4_weight_bytes(B, N, K) == B * L.weight_geometry(N, K)[2]
+    assert lib.mxfp4_weight_scale_bytes(B, N, K) == B * L.gemm_scale_geometry(N, K)[3]
+
+
+def test_size_queries_reject_bad_shapes(lib):
+    assert lib.mxfp4_scale_bytes(4, 48, 0) == 0
+    assert lib.mxfp4_scale_bytes(4, 64, 7) == 0
+    assert lib.mxfp4_weight_bytes(0, 16, 64) == 0
+    assert lib.mxfp4_gemm_workspace_bytes(16, 1024, 5120) == 0
+
+
+# Fake, suitably aligned addresses: every call below fails validation before
+# anything could dereference them.
+P = ctypes.c_void_p(0x100000)
+P_ODD = ctypes.c_void_p(0x100004)
+
+
+def test_quant_validation(lib):
+    f = lib.mxfp4_quant_1x32
+    assert f(P, 4, 64, 64, P, 32, P, 5, None) == 7             # bad layout
+    assert f(P, 4, 48, 48, P, 24, P, 0, None) == 2             # K % 32
+    assert f(P, -1, 64, 64, P, 32, P, 0, None) == 2            # M < 0
+    assert f(P, 4, 64, 32, P, 32, P, 0, None) == 2             # ldx < K
+    assert f(P, 4, 64, 64, P, 16, P, 0, None) == 2             # ldq < K/2
+    assert f(None, 4, 64, 64, P, 32, P, 1, None) == 1          # NULL x
+    assert f(P_ODD, 4, 64, 64, P, 32, P, 1, None) == 3         # x misaligned
+    assert f(P, 4, 64, 68, P, 32, P, 1, None) == 3             # ldx % 8
+    assert f(None, 0, 64, 64, None, 32, None, 1, None) == 0    # M == 0: nothing to do
+
+
+def test_preshuffle_validation(lib):
+    f = lib.mxfp4_preshuffle_weight
+    assert f(P, P, 1, 16, 40, P, P, None) == 2
+    assert f(P, P, 0, 16, 64, P, P, None) == 2
+    assert f(None, P, 1, 16, 64, P, P, None) == 1
+    assert f(P_ODD, P, 1, 16, 64, P, P, None) == 3
+
+
+def test_gemm_validation(lib):
+    f = lib.mxfp4_gemm_a4w4
+    ok = dict(a=P, lda=32, as_=P, w=P, ws=P, bias=None, out=P, ldo=16, dt=0, M=4, N=16, K=64)
+
+    def call(**kw):
+        d = dict(ok)
+        d.update(kw)
+        return f(d["a"], d["lda"], d["as_"], d["w"], d["ws"], d["bias"], d["out"], d["ldo"],
+                 d["dt"], d["M"], d["N"], d["K"], None, 0, None)
+
+    assert call(dt=3) == 7
+    assert call(K=48, lda=32) == 2
+    assert call(N=0) == 2
+    assert call(lda=16) == 2        # lda < K/2
+    assert call(ldo=8) == 2         # ldo < N
+    assert call(w=None) == 1
+    assert call(lda=40) == 3        # lda % 16
+    assert call(a=P_ODD) == 3
+    assert call(M=0, a=None) == 0   # nothing to do
+
+
+def test_bmm_validation(lib):
+    f = lib.a16wfp4_bmm
+
+    def call(x=P, sxb=64 * 192, sxm=192, w=P, ws=P, out=P, sob=64 * 512, som=512, dt=0,
+             B=16, M=64, N=512, K=192):
+        return f(x, sxb, sxm, w, ws, out, sob, som, dt, B, M, N, K, None)
+
+    assert call(dt=2) == 7
+    assert call(K=100) == 2
+    assert call(B=0) == 2
+    assert call(sxm=100) == 2
+    assert call(x=None) == 1
+    assert call(sxm=196) == 3
+    assert call(som=511) == 3
+    assert call(M=0, x=None) == 0
+
+
+def test_valid_call_without_gpu_reports_device(lib):
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: fake pointers must not reach a kernel")
+    assert lib.mxfp4_quant_1x32(P, 4, 64, 64, P, 32, P, 1, None) == 5
+    assert lib.mxfp4_gemm_a4w4(P, 32, P, P, P, None, P, 16, 0, 4, 16, 64, None, 0, None) == 5
+
+
+def test_debug_path_hook(lib):
+    assert lib.mxfp4_debug_set_gemm_path(3) == 7
+    assert lib.mxfp4_debug_set_gemm_path(0) == 0

@@ -1,0 +1,90 @@
+"""GPU parity: a16wfp4_bmm against the oracle (MLA absorbed K-up / V-up on one
+GPU's 16 heads, plus ragged shapes), both output layouts."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_block_scaled_quant_amd as mx
+from mxfp4_block_scaled_quant_amd import inputs
+from oracle import linalg as G
+from oracle import quant as Q
+from tests.helpers import (check_bf16_cast, check_f32_tolerance, dev_bf16, host_bf16_bits,
+                           need_gpu, tolerance_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(prob, batch_major):
+    B, M, K = prob["x"].shape
+    N = prob["w"].shape[1]
+    x = dev_bf16(prob["x"])
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    y32 = mx.a16wfp4_bmm(x, W.w_pre, W.ws_pre, N, batch_major=batch_major, out_dtype=torch.float32)
+    y16 = mx.a16wfp4_bmm(x, W.w_pre, W.ws_pre, N, batch_major=batch_major)
+    torch.cuda.synchronize()
+    y32, y16 = y32.cpu().numpy(), host_bf16_bits(y16)
+    if batch_major:                      # [M, B, N] -> [B, M, N]
+        y32, y16 = y32.transpose(1, 0, 2), y16.transpose(1, 0, 2)
+    return y32, y16
+
+
+def _check(prob, y32, y16, rows=None):
+    x = prob["x"] if rows is None else prob["x"][:, rows]
+    qw, sw = Q.quant_1x32(prob["w"])
+    o, S = G.bmm_a16wfp4(x, qw, sw)
+    if rows is not None:
+        y32, y16 = y32[:, rows], y16[:, rows]
+    check_f32_tolerance(y32, o, S)
+    check_bf16_cast(y16, o, tolerance_bound(S))
+    assert np.array_equal(y16, G.to_bf16(y32.astype(np.float64)))
+
+
+CASES = [
+    # name, B, M, N, K, batch_major
+    ("kup_M1", 16, 1, 512, 192, False),
+    ("kup_M64", 16, 64, 512, 192, False),
+    ("kup_M256", 16, 256, 512, 192, False),
+    ("vup_M1", 16, 1, 256, 512, True),
+    ("vup_M64", 16, 64, 256, 512, True),
+    ("vup_M256", 16, 256, 256, 512, True),
+    ("ragged_3x37x96x160", 3, 37, 96, 160, False),
+    ("ragged_2x70x30x4128", 2, 70, 30, 4128, True),
+]
+
+
+@pytest.mark.parametrize("name,B,M,N,K,bm", CASES, ids=[c[0] for c in CASES])
+def test_bmm(name, B, M, N, K, bm):
+    need_gpu()
+    prob = inputs.bmm_problem(B, M, N, K, 4)
+    y32, y16 = _run(prob, bm)
+    _check(prob, y32, y16)
+
+
+@pytest.mark.parametrize("name,N,K,bm", [("kup_M4096", 512, 192, False), ("vup_M4096", 256, 512, True)])
+def test_bmm_full_size_sampled_rows(name, N, K, bm):
+    need_gpu()
+    prob = inputs.bmm_problem(16, 4096, N, K, 4)
+    y32, y16 = _run(prob, bm)
+    rows = np.unique(np.concatenate([[0, 4095], np.random.default_rng(1).choice(4096, 62, replace=False)]))
+    _check(prob, y32, y16, rows=rows)
+
+
+def test_bmm_exact_mxfp4_activations_match_gemm():
+    # Cross-path identity: activations that are MXFP4 numbers give the same
+    # product through the BMM as through quant + W4A4 GEMM (within tolerance
+    # of each other, both against the oracle).
+    need_gpu()
+    B, M, N, K = 4, 48, 64, 256
+    prob = inputs.bmm_problem(B, M, N, K, 5)
+    qx, sx = Q.quant_1x32(prob["x"])
+    from oracle import formats as F
+    prob["x"] = F.f64_to_bf16(Q.dequant(qx, sx))
+    y32, _ = _run(prob, False)
+    for b in range(B):
+        W = mx.quantize_weight(dev_bf16(prob["w"][b]))
+        q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"][b]))
+        g = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, N, K, None, torch.float32).cpu().numpy()
+        ref, S = G.gemm_a4w4_from_quant(qx[b], sx[b], *Q.quant_1x32(prob["w"][b]))
+        check_f32_tolerance(g, ref, S)
+        check_f32_tolerance(y32[b], ref, S)

@@ -1,0 +1,147 @@
+"""GPU parity: the W4A4 linear (quant -> mxfp4_gemm_a4w4) against the oracle.
+
+Bar: before the bf16 cast (fp32 output) |y - y_ref| <= 2^-18 (sum|a_i b_i| +
+|bias|) per element; after the cast within 1 bf16 ulp of the rounded oracle,
+or, where cancellation makes the pre-cast band wider than that, the rounding
+of a value inside the band; the bf16 output equals the RNE of the kernel's
+fp32 result; no NaN; identical bytes run to run.  Small shapes are checked element by element; the full
+decode / prefill sweeps at sampled rows and columns (the oracle quantises
+only the sampled rows of A and W, which is exact since quantisation is per
+row)."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_block_scaled_quant_amd as mx
+from mxfp4_block_scaled_quant_amd import inputs
+from oracle import formats as F
+from oracle import linalg as G
+from tests.helpers import (check_bf16_cast, check_f32_tolerance, dev_bf16, host_bf16_bits,
+                           need_gpu, tolerance_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(prob, path, weight=None):
+    x = dev_bf16(prob["x"])
+    M, K = prob["x"].shape
+    N = prob["w"].shape[0]
+    W = weight if weight is not None else mx.quantize_weight(dev_bf16(prob["w"]))
+    b = dev_bf16(prob["bias"]) if prob["bias"] is not None else None
+    mx.set_gemm_path(path)
+    try:
+        q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM)
+        y32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, N, K, b, torch.float32)
+        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, N, K, b, torch.bfloat16)
+    finally:
+        mx.set_gemm_path(0)
+    torch.cuda.synchronize()
+    return y32.cpu().numpy(), host_bf16_bits(y16)
+
+
+def _check(prob, y32, y16, rows=None, cols=None):
+    x = prob["x"] if rows is None else prob["x"][rows]
+    w = prob["w"] if cols is None else prob["w"][cols]
+    bias = prob["bias"]
+    if bias is not None and cols is not None:
+        bias = bias[cols]
+    y_ref, S = G.gemm_a4w4(x, w, bias)
+    if rows is not None:
+        y32, y16 = y32[rows], y16[rows]
+    if cols is not None:
+        y32, y16 = y32[:, cols], y16[:, cols]
+    babs = None if bias is None else np.abs(F.bf16_to_f64(bias))[None, :]
+    worst = check_f32_tolerance(y32, y_ref, S, babs)
+    check_bf16_cast(y16, y_ref, tolerance_bound(S, babs))
+    # the bf16 output is the single RNE cast of the kernel's own fp32 result
+    assert np.array_equal(y16, G.to_bf16(y32.astype(np.float64)))
+    return worst
+
+
+SMALL = [
+    # name, M, N, K, problem kwargs
+    ("linear_16x1024x5120", 16, 1024, 5120, dict(seed=0, outliers=True)),
+    ("edge_37x96x4128", 37, 96, 4128, dict(seed=5, edge=True)),
+    ("edge_37x96x4128_bias", 37, 96, 4128, dict(seed=5, edge=True, with_bias=True)),
+    ("edge_300x128x256", 300, 128, 256, dict(seed=5, edge=True)),
+    ("edge_300x128x256_bias", 300, 128, 256, dict(seed=5, edge=True, with_bias=True)),
+    ("tiles_300x520x1056", 300, 520, 1056, dict(seed=6, outliers=True, with_bias=True)),
+    ("decode_64x300x640", 64, 300, 640, dict(seed=6, with_bias=True)),
+    ("tiny_1x16x32", 1, 16, 32, dict(seed=9)),
+    ("tiny_5x17x96", 5, 17, 96, dict(seed=9, with_bias=True)),
+    ("ragged_257x257x2080", 257, 257, 2080, dict(seed=10, outliers=True)),
+]
+
+
+@pytest.mark.parametrize("path", [1, 2], ids=["smallM", "tiled"])
+@pytest.mark.parametrize("name,M,N,K,kw", SMALL, ids=[c[0] for c in SMALL])
+def test_linear_small_shapes(name, M, N, K, kw, path):
+    need_gpu()
+    if path == 1 and M > 64:
+        pytest.skip("the small-M kernel covers M <= 64")
+    prob = inputs.linear_problem(M, N, K, **kw)
+    y32, y16 = _run(prob, path)
+    _check(prob, y32, y16)
+
+
+def test_linear_deterministic():
+    need_gpu()
+    prob = inputs.linear_problem(300, 520, 1056, 6, outliers=True, with_bias=True)
+    for path in (1, 2):
+        p = dict(prob)
+        if path == 1:
+            p["x"] = prob["x"][:64]
+        a = _run(p, path)
+        b = _run(p, path)
+        assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+        assert np.array_equal(a[1], b[1])
+
+
+_WEIGHTS = {}
+
+
+def _weight(N, K, seed):
+    key = (N, K, seed)
+    if key not in _WEIGHTS:
+        _WEIGHTS.clear()
+        w = inputs.weights(N, K, seed)
+        _WEIGHTS[key] = (w, mx.quantize_weight(dev_bf16(w)))
+    return _WEIGHTS[key]
+
+
+NK = [(14336, 5120), (5120, 14336), (34816, 5120)]
+
+
+def _sample(n, k, seed):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], r.choice(n, min(n, k), replace=False)]))
+
+
+@pytest.mark.parametrize("N,K", NK, ids=[f"{n}x{k}" for n, k in NK])
+def test_decode_sweep_full_size(N, K):
+    # M in {1, 4, 16, 32, 64}, bias ~ N(0, 0.1), no outliers; the launch the
+    # benchmark times (automatic kernel choice by M).
+    need_gpu()
+    w, W = _weight(N, K, 2)
+    cols = _sample(N, 96, N)
+    b = inputs.bias(N, 2)
+    for M in (1, 4, 16, 32, 64):
+        x = inputs.activations(M, K, 2)
+        prob = {"x": x, "w": w, "bias": b}
+        y32, y16 = _run(prob, 0, weight=W)
+        _check(prob, y32, y16, cols=cols)
+
+
+@pytest.mark.parametrize("N,K", NK, ids=[f"{n}x{k}" for n, k in NK])
+def test_prefill_sweep_full_size(N, K):
+    # M in {512, 2048, 8192}, 1% outlier channels x20, no bias.
+    need_gpu()
+    w, W = _weight(N, K, 3)
+    cols = _sample(N, 64, N + 1)
+    for M in (512, 2048, 8192):
+        x = inputs.activations(M, K, 3, outliers=True)
+        prob = {"x": x, "w": w, "bias": None}
+        y32, y16 = _run(prob, 0, weight=W)
+        rows = _sample(M, 64, M)
+        _check(prob, y32, y16, rows=rows, cols=cols)
