@@ -1,0 +1,390 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X W4A4 MXFP4 linear (and the prefill / A16WFP4 BMM sweeps).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-prefill] [--no-bmm]
+
+Headline (the metric's M <= 16 decode regime): one step is one pass over the
+decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
+(5120, 14336), (34816, 5120)} -- for each shape, per-1x32 quantisation of the
+bf16 activations (GEMM scale layout, 0x7F padding) and the block-scaled FP4
+GEMM with a bf16 bias and bf16 output, against weights quantised and
+preshuffled once at load time.  value = sum of the pipeline's algorithmic
+bytes over the step / step time (GB/s).  Inputs are resident in HBM before the
+timed region.  Each launch reads a different copy of its weights (>= 1 GiB of
+copies per shape) so the 256 MB Infinity Cache and the L2s cannot serve them.
+Steps are replayed from HIP graphs (one graph per step position in the copy
+rotation), bracketed by HIP events on the capture/replay stream.
+
+Also reported (same JSON line): the dominant kernel's roofline (decode GEMM,
+timed in its own graph-replayed loop), the full decode sweep (M up to 64), the
+prefill sweep (M in {512, 2048, 8192}: TFLOP/s and fraction of the 10.1
+PFLOP/s dense FP4 peak), the A16WFP4 BMM sweep (MLA K-up / V-up on 16 heads),
+and the CPU oracle timed on a bounded sample of the headline workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_FP4 = 10.1e15         # MI355X dense FP4 MFMA, flop/s
+PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, flop/s
+
+DECODE_NK = [(14336, 5120), (5120, 14336), (34816, 5120)]
+HEADLINE_M = [1, 4, 16]
+DECODE_M = [1, 4, 16, 32, 64]
+PREFILL_M = [512, 2048, 8192]
+BMM_CASES = [("K-up", 512, 192, False), ("V-up", 256, 512, True)]   # (name, N, K, batch_major)
+BMM_M = [1, 64, 256, 4096]
+BMM_HEADS = 16
+ROTATE_BYTES = 1 << 30
+MIN_LAUNCHES = 32          # launches per timed graph (amortises graph-launch overhead)
+
+METRIC = "W4A4 MXFP4 GEMM TFLOPS & % FP4 peak (M≥2048); GB/s & % HBM at M≤16"
+
+
+def gemm_bytes(M, N, K, bias):
+    """Algorithmic bytes of one GEMM launch: W + scales, A + scales, out, bias."""
+    return N * K * 17 / 32 + M * K * 17 / 32 + 2 * M * N + (2 * N if bias else 0)
+
+
+def pipeline_bytes(M, N, K, bias):
+    """Algorithmic bytes of quant + GEMM: bf16 x replaces packed A + scales."""
+    return N * K * 17 / 32 + 2 * M * K + 2 * M * N + (2 * N if bias else 0)
+
+
+def quant_bytes(M, K):
+    return 2 * M * K + 17 * M * K / 32
+
+
+def bmm_bytes(B, M, N, K):
+    return B * (2 * M * K + N * K * 17 / 32 + 2 * M * N)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copies_for(nbytes):
+    return max(2, -(-ROTATE_BYTES // int(nbytes)))
+
+
+class Timer:
+    """HIP-event timing of graph replays on the current stream."""
+
+    def __init__(self):
+        self.stream = torch.cuda.current_stream()
+
+    def capture(self, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def time_graphs(self, graphs, reps, warmup=2):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3      # seconds per replay
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-bmm", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the W4A4 linear and the BMM run on a single MI355X "
+              "and this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import mxfp4_block_scaled_quant_amd as mx
+    from mxfp4_block_scaled_quant_amd import inputs
+
+    mx.lib()   # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a gfx950 GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = Timer()
+
+    def dev_bf16(bits):
+        return inputs.bits_to_torch_bf16(bits).to(dev)
+
+    # ---------------- load time: weights quantised + preshuffled, rotated copies
+    t_load = time.time()
+    weights = {}
+    preshuffle_s = {}
+    for (N, K) in DECODE_NK:
+        w = dev_bf16(inputs.weights(N, K, 2))
+        torch.cuda.synchronize()
+        t0 = time.time()
+        W = mx.quantize_weight(w)
+        torch.cuda.synchronize()
+        preshuffle_s[(N, K)] = time.time() - t0
+        R = copies_for(W.w_pre.numel() + W.ws_pre.numel())
+        copies = [W] + [mx.MXFP4Weight(W.w_pre.clone(), W.ws_pre.clone(), N, K) for _ in range(R - 1)]
+        weights[(N, K)] = copies
+        del w
+    torch.cuda.synchronize()
+
+    log(f"weights quantised + preshuffled, {sum(len(v) for v in weights.values())} rotation copies")
+    # ---------------- headline: decode sweep M <= 16, quant + GEMM + bias
+    cases = []
+    for (N, K) in DECODE_NK:
+        b = dev_bf16(inputs.bias(N, 2))
+        for M in HEADLINE_M:
+            x = dev_bf16(inputs.activations(M, K, 2))
+            q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            s = torch.empty(mx.scale_bytes(M, K, mx.MXFP4_SCALES_GEMM), dtype=torch.uint8, device=dev)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            cases.append(dict(M=M, N=N, K=K, x=x, q=q, s=s, out=out, bias=b))
+
+    def launch_case(c, copy):
+        mx.mxfp4_quant_1x32(c["x"], mx.MXFP4_SCALES_GEMM, q=c["q"], scales=c["s"])
+        mx.mxfp4_gemm_a4w4(c["q"], c["s"], copy.w_pre, copy.ws_pre, c["N"], c["K"], c["bias"],
+                           torch.bfloat16, out=c["out"])
+
+    # One graph per step position of the rotation cycle: launch i of shape (N,K)
+    # uses copy (i mod R); the cycle repeats after lcm over shapes of R/3 steps.
+    per_step = {nk: sum(1 for c in cases if (c["N"], c["K"]) == nk) for nk in DECODE_NK}
+    cycle = 1
+    for nk in DECODE_NK:
+        R = len(weights[nk])
+        k = R // np.gcd(R, per_step[nk])
+        cycle = int(np.lcm(cycle, k))
+    counters = {nk: 0 for nk in DECODE_NK}
+    step_graphs = []
+
+    def one_step():
+        for c in cases:
+            nk = (c["N"], c["K"])
+            copy = weights[nk][counters[nk] % len(weights[nk])]
+            counters[nk] += 1
+            launch_case(c, copy)
+
+    for _ in range(cycle):
+        step_graphs.append(T.capture(one_step))
+
+    for i in range(args.warmup):
+        step_graphs[i % cycle].replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step_graphs[i % cycle].replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    step_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    step_bytes = sum(pipeline_bytes(c["M"], c["N"], c["K"], True) for c in cases)
+    value_gbs = step_bytes / step_s / 1e9
+
+    log(f"headline: {step_s * 1e6:.2f} us/step, {value_gbs:.1f} GB/s")
+    # ---------------- dominant kernel: the decode GEMM alone, per shape
+    def per_launch_time(launch, nvariants, reps_target):
+        """Mean time of one launch: a graph of >= MIN_LAUNCHES back-to-back
+        launches (cycling over `nvariants` input copies) replayed and timed
+        with events, so graph-launch overhead is amortised."""
+        n = nvariants * -(-MIN_LAUNCHES // nvariants)
+
+        def body():
+            for i in range(n):
+                launch(i % nvariants)
+
+        g = T.capture(body)
+        reps = max(2, reps_target // n)
+        return T.time_graphs([g], reps) / n
+
+    def gemm_only_time(M, N, K, x_q, x_s, bias, out, copies, reps_target=400):
+        def launch(i):
+            cp = copies[i]
+            mx.mxfp4_gemm_a4w4(x_q, x_s, cp.w_pre, cp.ws_pre, N, K, bias, torch.bfloat16, out=out)
+        return per_launch_time(launch, len(copies), reps_target)
+
+    def quant_time(x, q, s, reps_target=400):
+        return per_launch_time(lambda i: mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM, q=q, scales=s),
+                               1, reps_target)
+
+    decode_rows = []
+    for (N, K) in DECODE_NK:
+        b = dev_bf16(inputs.bias(N, 2))
+        for M in DECODE_M:
+            x = dev_bf16(inputs.activations(M, K, 2))
+            q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            t = gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
+            gb = gemm_bytes(M, N, K, True)
+            tq = quant_time(x, q, s)
+            decode_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 3),
+                                    gemm_GBps=round(gb / t / 1e9, 1),
+                                    hbm_frac=round(gb / t / PEAK_HBM, 4),
+                                    quant_us=round(tq * 1e6, 3),
+                                    tflops=round(2 * M * N * K / t / 1e12, 2)))
+    head_rows = [r for r in decode_rows if r["M"] in HEADLINE_M]
+    dom_bytes = sum(gemm_bytes(r["M"], r["N"], r["K"], True) for r in head_rows)
+    dom_time = sum(r["gemm_us"] for r in head_rows) * 1e-6
+    achieved = dom_bytes / len(head_rows) / (dom_time / len(head_rows))
+
+    log("decode sweep done")
+    # ---------------- prefill sweep (GEMM, TFLOP/s vs the FP4 peak)
+    prefill_rows = []
+    if not args.no_prefill:
+        for (N, K) in DECODE_NK:
+            for M in PREFILL_M:
+                x = dev_bf16(inputs.activations(M, K, 3, outliers=True))
+                q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM)
+                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                cps = weights[(N, K)][:4]
+                t = gemm_only_time(M, N, K, q, s, None, out, cps, reps_target=40)
+                tq = quant_time(x, q, s, reps_target=64)
+                fl = 2 * M * N * K
+                prefill_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 2),
+                                         tflops=round(fl / t / 1e12, 1),
+                                         fp4_peak_frac=round(fl / t / PEAK_FP4, 4),
+                                         quant_us=round(tq * 1e6, 2),
+                                         quant_GBps=round(quant_bytes(M, K) / tq / 1e9, 1)))
+                del x, q, s, out
+        torch.cuda.empty_cache()
+    big = [r for r in prefill_rows if r["M"] >= 2048]
+    prefill_summary = None
+    if big:
+        fl = sum(2 * r["M"] * r["N"] * r["K"] for r in big)
+        tt = sum(r["gemm_us"] for r in big) * 1e-6
+        prefill_summary = dict(tflops_M_ge_2048=round(fl / tt / 1e12, 1),
+                               fp4_peak_frac=round(fl / tt / PEAK_FP4, 4), shapes=prefill_rows)
+
+    log("prefill sweep done")
+    # ---------------- A16WFP4 BMM sweep (MLA absorbed K-up / V-up, 16 heads)
+    bmm_rows = []
+    if not args.no_bmm:
+        for name, N, K, bm in BMM_CASES:
+            w = dev_bf16(inputs.bmm_problem(BMM_HEADS, 1, N, K, 4)["w"].reshape(BMM_HEADS * N, K))
+            W = mx.quantize_weight(w.reshape(BMM_HEADS, N, K))
+            for M in BMM_M:
+                x = dev_bf16(inputs.bmm_problem(BMM_HEADS, M, N, K, 4)["x"])
+                # rotate activation copies once they are large enough to matter
+                R = 1 if x.numel() * 2 < (8 << 20) else min(48, copies_for(x.numel() * 2))
+                xs = [x] + [x.clone() for _ in range(R - 1)]
+                out = (torch.empty((M, BMM_HEADS, N), dtype=torch.bfloat16, device=dev) if bm
+                       else torch.empty((BMM_HEADS, M, N), dtype=torch.bfloat16, device=dev))
+
+                t = per_launch_time(lambda i: mx.a16wfp4_bmm(xs[i], W.w_pre, W.ws_pre, N, out=out,
+                                                             batch_major=bm), R, 400)
+                by = bmm_bytes(BMM_HEADS, M, N, K)
+                fl = 2 * BMM_HEADS * M * N * K
+                bmm_rows.append(dict(op=name, M=M, N=N, K=K, us=round(t * 1e6, 3),
+                                     GBps=round(by / t / 1e9, 1), hbm_frac=round(by / t / PEAK_HBM, 4),
+                                     tflops=round(fl / t / 1e12, 2)))
+                del xs, x, out
+            torch.cuda.empty_cache()
+
+    log("bmm sweep done")
+    # ---------------- CPU oracle on a bounded sample of the headline workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inputs)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode-sweep W4A4 MXFP4 linear at M<=16: per-1x32 quant of bf16 "
+                        "activations + block-scaled FP4 GEMM + bf16 bias, bf16 out",
+            "M": HEADLINE_M, "NK": DECODE_NK,
+            "step": "9 shapes x (quant + GEMM), weights preshuffled at load, rotated copies",
+            "hbm_frac": round(value_gbs * 1e9 / PEAK_HBM, 4),
+        },
+        "roofline": {
+            "kernel": "gemm_decode_kernel (W4A4 GEMM, M<=16, mean over the 9 headline shapes)",
+            "bound": "hbm",
+            "achieved": round(achieved / 1e9, 1),
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM, 4),
+            "traffic": None,
+            "launch_us": round(dom_time / len(head_rows) * 1e6, 3),
+            "bytes_per_launch": round(dom_bytes / len(head_rows)),
+        },
+        "cpu_baseline": cpu,
+        "decode_sweep": decode_rows,
+        "prefill": prefill_summary,
+        "bmm": bmm_rows or None,
+        "preshuffle_load_s": {f"{n}x{k}": round(v, 4) for (n, k), v in preshuffle_s.items()},
+        "setup_s": round(time.time() - t_load, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inputs):
+    """The oracle, as it stands, on a bounded sample: each headline shape with
+    the first 256 output columns.  Weight quantisation is load time (untimed),
+    as on the GPU; the timed work per shape is quant(x) + dequantise + fp64
+    matmul + bias."""
+    from oracle import linalg as OL
+    from oracle import quant as OQ
+    try:
+        import threadpoolctl
+        threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:
+        threads = os.cpu_count()
+    NS = 256
+    total_bytes, total_s = 0.0, 0.0
+    for (N, K) in DECODE_NK:
+        w = inputs.weights(N, K, 2)[:NS]
+        qw, sw = OQ.quant_1x32(w)
+        b = inputs.bias(N, 2)[:NS]
+        for M in HEADLINE_M:
+            x = inputs.activations(M, K, 2)
+            t0 = time.perf_counter()
+            reps = 0
+            while True:
+                qa, sa = OQ.quant_1x32(x)
+                y, _ = OL.gemm_a4w4_from_quant(qa, sa, qw, sw, b)
+                OL.to_bf16(y)
+                reps += 1
+                if time.perf_counter() - t0 > 0.5:
+                    break
+            total_s += (time.perf_counter() - t0) / reps
+            total_bytes += pipeline_bytes(M, NS, K, True)
+    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"headline shapes (M in {HEADLINE_M}, (N,K) in {DECODE_NK}) restricted to the "
+                      f"first {NS} output columns; numpy fp64, BLAS threads {threads}; "
+                      f"weight quantisation untimed (load time)"}
+
+
+if __name__ == "__main__":
+    main()
