@@ -157,15 +157,15 @@ def main():
         b = dev_bf16(inputs.bias(N, 2))
         for M in HEADLINE_M:
             x = dev_bf16(inputs.activations(M, K, 2))
-            q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-            s = torch.empty(mx.scale_bytes(M, K, mx.MXFP4_SCALES_GEMM), dtype=torch.uint8, device=dev)
+            q = torch.empty(mx.data_bytes(M, K, mx.MXFP4_LAYOUT_GEMM), dtype=torch.uint8, device=dev)
+            s = torch.empty(mx.scale_bytes(M, K, mx.MXFP4_LAYOUT_GEMM), dtype=torch.uint8, device=dev)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             cases.append(dict(M=M, N=N, K=K, x=x, q=q, s=s, out=out, bias=b))
 
     def launch_case(c, copy):
-        mx.mxfp4_quant_1x32(c["x"], mx.MXFP4_SCALES_GEMM, q=c["q"], scales=c["s"])
-        mx.mxfp4_gemm_a4w4(c["q"], c["s"], copy.w_pre, copy.ws_pre, c["N"], c["K"], c["bias"],
-                           torch.bfloat16, out=c["out"])
+        mx.mxfp4_quant_1x32(c["x"], mx.MXFP4_LAYOUT_GEMM, q=c["q"], scales=c["s"])
+        mx.mxfp4_gemm_a4w4(c["q"], c["s"], copy.w_pre, copy.ws_pre, c["M"], c["N"], c["K"],
+                           c["bias"], torch.bfloat16, out=c["out"])
 
     # One graph per step position of the rotation cycle: launch i of shape (N,K)
     # uses copy (i mod R); the cycle repeats after lcm over shapes of R/3 steps.
@@ -220,11 +220,11 @@ def main():
     def gemm_only_time(M, N, K, x_q, x_s, bias, out, copies, reps_target=400):
         def launch(i):
             cp = copies[i]
-            mx.mxfp4_gemm_a4w4(x_q, x_s, cp.w_pre, cp.ws_pre, N, K, bias, torch.bfloat16, out=out)
+            mx.mxfp4_gemm_a4w4(x_q, x_s, cp.w_pre, cp.ws_pre, M, N, K, bias, torch.bfloat16, out=out)
         return per_launch_time(launch, len(copies), reps_target)
 
     def quant_time(x, q, s, reps_target=400):
-        return per_launch_time(lambda i: mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM, q=q, scales=s),
+        return per_launch_time(lambda i: mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM, q=q, scales=s),
                                1, reps_target)
 
     decode_rows = []
@@ -232,7 +232,7 @@ def main():
         b = dev_bf16(inputs.bias(N, 2))
         for M in DECODE_M:
             x = dev_bf16(inputs.activations(M, K, 2))
-            q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM)
+            q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             t = gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
             gb = gemm_bytes(M, N, K, True)
@@ -254,7 +254,7 @@ def main():
         for (N, K) in DECODE_NK:
             for M in PREFILL_M:
                 x = dev_bf16(inputs.activations(M, K, 3, outliers=True))
-                q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM)
+                q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
                 out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 cps = weights[(N, K)][:4]
                 t = gemm_only_time(M, N, K, q, s, None, out, cps, reps_target=40)

@@ -29,15 +29,19 @@
  *
  * Layouts (all byte offsets; the library's own design for gfx950's
  * 16x16x128 block-scaled FP4 MFMA):
- *   GEMM scale layout, R rows, C = K/32 blocks, Kt = ceil(K/128),
- *   G = ceil(Kt/4), Rp = 16*ceil(R/16):
+ *   GEMM data layout (quantised activations and preshuffled weights alike),
+ *   R rows, Kt = ceil(K/128), per batch entry b of Rp = 16*ceil(R/16) rows:
+ *     pair (r, k), k even: s = r/16, t = k/128, kb = (k%128)/32,
+ *     offset = ((b*Rp/16 + s)*Kt + t)*1024 + (kb*16 + r%16)*16 + (k%32)/2,
+ *     element k in the low nibble; padding bytes (rows >= R, k >= K) 0x00.
+ *     A 1 KiB unit (s, t) is a 16-row x 128-K tile whose 16-byte slot
+ *     kb*16 + r%16 is that row's whole 1x32 block kb: the operand of MFMA
+ *     lane kb*16 + r%16.  Size B*Rp*Kt*64.
+ *   GEMM scale layout, G = ceil(Kt/4):
  *     scale (r, c): t = c/4, kb = c%4, g = t/4, j = t%4,
- *     offset = ((r/16)*G + g)*256 + (kb*16 + r%16)*4 + j;  size Rp*G*16.
- *   Preshuffled weight layout, per batch entry, N rows, Np = 16*ceil(N/16):
- *     pair (n, k), k even: s = n/16, r = n%16, t = k/128, kb = (k%128)/32,
- *     offset = ((b*Np/16 + s)*Kt + t)*1024 + (kb*16 + r)*16 + (k%32)/2;
- *     size B*Np*Kt*64; padding bytes are 0x00.  Its scales use the GEMM
- *     scale layout per batch entry, entries concatenated.
+ *     offset = ((r/16)*G + g)*256 + (kb*16 + r%16)*4 + j;  size Rp*G*16,
+ *     batch entries concatenated; padding bytes 0x7F.
+ *   ROWMAJOR: packed FP4 [R, K/2] (row stride given) and scales [R, K/32].
  */
 #ifndef MXFP4_H
 #define MXFP4_H
@@ -60,7 +64,7 @@ typedef enum {
   MXFP4_ERR_ARG = 7        /* an enum argument is out of range                  */
 } mxfp4_status;
 
-enum { MXFP4_SCALES_ROWMAJOR = 0, MXFP4_SCALES_GEMM = 1 };
+enum { MXFP4_LAYOUT_ROWMAJOR = 0, MXFP4_LAYOUT_GEMM = 1 };
 enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_F32 = 1 };
 
 /* Static string naming a status code (never NULL). */
@@ -69,8 +73,10 @@ const char* mxfp4_status_str(int status);
 /* ABI version: major * 100 + minor. */
 int mxfp4_abi_version(void);
 
-/* Bytes of a scale buffer for `rows` x K in `layout`: rows*K/32 for ROWMAJOR,
- * the padded GEMM-layout size otherwise.  0 on invalid arguments. */
+/* Bytes of the packed FP4 data / the scales for `rows` x K in `layout`:
+ * rows*K/2 and rows*K/32 for ROWMAJOR, the padded GEMM-layout sizes
+ * otherwise.  0 on invalid arguments. */
+size_t mxfp4_data_bytes(int64_t rows, int64_t K, int layout);
 size_t mxfp4_scale_bytes(int64_t rows, int64_t K, int layout);
 
 /* Bytes of the preshuffled weight data / its scales for `batch` matrices of
@@ -84,7 +90,7 @@ size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 /*
  * Per-1x32 MXFP4 quantisation (P1 §Modifications: activations are quantised
  * per 1x32 before the FP4 GEMM; P2 §2: the quantisation op returns packed
- * FP4 [rows, K/2] and E8M0 scales; the scheme quantises weights the same
+ * FP4 and one E8M0 scale per block; the scheme quantises weights the same
  * way).  Arithmetic per OCP-MX, reading as follows: per block amax, scale
  * byte b = max(E(amax) - 2, 0) with E the biased exponent field of amax,
  * element |v| / 2^(b-127) rounded to the nearest E2M1 magnitude with ties to
@@ -92,12 +98,15 @@ size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *
  *   x       bf16 [M, K], row stride ldx ELEMENTS (ldx >= K, ldx % 8 == 0,
  *           x 16-byte aligned)
- *   q       packed FP4 [M, K/2], row stride ldq BYTES (ldq >= K/2,
- *           ldq % 4 == 0, q 4-byte aligned)
- *   scales  ROWMAJOR: [M, K/32] bytes, row stride K/32;
- *           GEMM: the GEMM scale layout for M rows, padding rows and blocks
- *           written with 0x7F (P2 §2: pad with 1.0 because whole tiles are
- *           read and 0xFF is NaN).  Size: mxfp4_scale_bytes(M, K, layout).
+ *   layout  ROWMAJOR: q is [M, K/2] with row stride ldq BYTES (ldq >= K/2,
+ *             ldq % 4 == 0, q 4-byte aligned); scales [M, K/32].
+ *           GEMM: q and scales in the GEMM layouts above
+ *             (mxfp4_data_bytes / mxfp4_scale_bytes bytes; ldq ignored;
+ *             q 16-byte aligned, scales 4-byte aligned); every padding byte
+ *             is written (0x00 data, 0x7F scales: P2 §2 pads scale tiles with
+ *             1.0 because whole tiles are read and 0xFF is NaN).  This is the
+ *             form mxfp4_gemm_a4w4 reads, and for a weight it is bytewise the
+ *             output of mxfp4_preshuffle_weight.
  *   M >= 0 (M == 0 enqueues nothing), K > 0, K % 32 == 0.
  */
 int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx,
@@ -107,7 +116,10 @@ int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx,
 /*
  * Load-time weight preshuffle (P1 §Modifications and P2 §2: weights and
  * their E8M0 scales are rearranged once after loading into the layout the
- * FP4 GEMM reads).  Permutation only; the layout is this library's own.
+ * FP4 GEMM reads).  Permutation only, from already quantised ROWMAJOR bytes
+ * (e.g. a checkpoint's) into the GEMM layouts, batch entries each padded to
+ * a multiple of 16 rows.  A bf16 weight can instead be quantised straight
+ * into the GEMM layout with mxfp4_quant_1x32.
  *
  *   w_fp4     packed FP4 [batch, N, K/2], contiguous, 16-byte aligned
  *   w_scales  ROWMAJOR scales [batch, N, K/32], contiguous
@@ -127,17 +139,17 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
  *   out[m, n] = round(sum_k dq(A)[m,k] dq(W)[n,k] + bias[n])
  * with fp32 accumulation and one round-to-nearest-even cast for bf16.
  *
- *   a_fp4     packed FP4 activations [M, K/2], row stride lda BYTES
- *             (lda >= K/2, lda % 16 == 0, pointer 16-byte aligned)
- *   a_scales  activation scales in the GEMM scale layout for M rows
- *   w_pre     preshuffled weights (1 batch entry), ws_pre their scales
+ *   a_fp4, a_scales  activations in the GEMM layouts (from mxfp4_quant_1x32
+ *             with MXFP4_LAYOUT_GEMM), 16- and 4-byte aligned
+ *   w_pre, ws_pre    weights in the same layouts (one batch entry)
  *   bias      bf16 [N] or NULL
  *   out       [M, N], row stride ldo ELEMENTS, bf16 or fp32 per out_dtype
  *             (ldo >= N; 4-byte aligned)
  *   workspace may be NULL when mxfp4_gemm_workspace_bytes() returns 0.
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
+ * Results are identical run to run (no atomics; fixed reduction order).
  */
-int mxfp4_gemm_a4w4(const void* a_fp4, int64_t lda, const void* a_scales,
+int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales,
                     const void* w_pre, const void* ws_pre, const void* bias,
                     void* out, int64_t ldo, int out_dtype,
                     int64_t M, int64_t N, int64_t K,

@@ -29,8 +29,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxfp4.so")
 
-MXFP4_SCALES_ROWMAJOR = 0
-MXFP4_SCALES_GEMM = 1
+MXFP4_LAYOUT_ROWMAJOR = 0
+MXFP4_LAYOUT_GEMM = 1
 MXFP4_OUT_BF16 = 0
 MXFP4_OUT_F32 = 1
 
@@ -42,13 +42,14 @@ _c_size = ctypes.c_size_t
 _SIGNATURES = {
     "mxfp4_status_str": (ctypes.c_char_p, [_c_int]),
     "mxfp4_abi_version": (_c_int, []),
+    "mxfp4_data_bytes": (_c_size, [_c_i64, _c_i64, _c_int]),
     "mxfp4_scale_bytes": (_c_size, [_c_i64, _c_i64, _c_int]),
     "mxfp4_weight_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_weight_scale_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_gemm_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_quant_1x32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_int, _c_vp]),
     "mxfp4_preshuffle_weight": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
-    "mxfp4_gemm_a4w4": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
+    "mxfp4_gemm_a4w4": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
                                  _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
     "a16wfp4_bmm": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int,
                              _c_i64, _c_i64, _c_i64, _c_i64, _c_vp]),
@@ -102,6 +103,10 @@ def _require_cuda(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
 
 
+def data_bytes(rows: int, K: int, layout: int) -> int:
+    return int(lib().mxfp4_data_bytes(rows, K, layout))
+
+
 def scale_bytes(rows: int, K: int, layout: int) -> int:
     return int(lib().mxfp4_scale_bytes(rows, K, layout))
 
@@ -119,24 +124,28 @@ def set_gemm_path(path: int) -> None:
     _check("mxfp4_debug_set_gemm_path", lib().mxfp4_debug_set_gemm_path(path))
 
 
-def mxfp4_quant_1x32(x: torch.Tensor, scale_layout: int = MXFP4_SCALES_GEMM,
+def mxfp4_quant_1x32(x: torch.Tensor, layout: int = MXFP4_LAYOUT_GEMM,
                      q: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
-    """Quantise bf16 rows [M, K] per 1x32 block.  Returns (q uint8 [M, K/2], scales uint8 1-D).
+    """Quantise bf16 rows [M, K] per 1x32 block.  Returns (q, scales) uint8 tensors.
 
-    ``scales`` is [M*K/32] row-major for MXFP4_SCALES_ROWMAJOR, or the padded
-    GEMM layout (``scale_bytes(M, K, MXFP4_SCALES_GEMM)`` bytes).
+    MXFP4_LAYOUT_GEMM (default): both 1-D in the GEMM layouts (what
+    :func:`mxfp4_gemm_a4w4` reads).  MXFP4_LAYOUT_ROWMAJOR: q [M, K/2] (any
+    row stride) and scales [M*K/32].
     """
     _require_cuda(x, "x")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bf16 tensor with unit stride along K")
     M, K = x.shape
     if q is None:
-        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        if layout == MXFP4_LAYOUT_ROWMAJOR:
+            q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        else:
+            q = torch.empty(data_bytes(M, K, layout), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty(scale_bytes(M, K, scale_layout), dtype=torch.uint8, device=x.device)
+        scales = torch.empty(scale_bytes(M, K, layout), dtype=torch.uint8, device=x.device)
+    ldq = q.stride(0) if (layout == MXFP4_LAYOUT_ROWMAJOR and q.dim() == 2) else K // 2
     _check("mxfp4_quant_1x32", lib().mxfp4_quant_1x32(
-        _ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scales), scale_layout,
-        _stream(x.device)))
+        _ptr(x), M, K, x.stride(0), _ptr(q), ldq, _ptr(scales), layout, _stream(x.device)))
     return q, scales
 
 
@@ -156,13 +165,11 @@ def mxfp4_preshuffle_weight(w_fp4: torch.Tensor, w_scales: torch.Tensor, N: int,
 
 
 def mxfp4_gemm_a4w4(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre: torch.Tensor,
-                    ws_pre: torch.Tensor, N: int, K: int, bias: Optional[torch.Tensor] = None,
+                    ws_pre: torch.Tensor, M: int, N: int, K: int,
+                    bias: Optional[torch.Tensor] = None,
                     out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
-    """out[M, N] = dq(A) dq(W)^T (+ bias), bf16 or fp32."""
+    """out[M, N] = dq(A) dq(W)^T (+ bias), bf16 or fp32; A and W in the GEMM layouts."""
     _require_cuda(a_fp4, "a_fp4")
-    M = a_fp4.shape[0]
-    if a_fp4.dim() != 2 or a_fp4.stride(1) != 1 or a_fp4.shape[1] != K // 2:
-        raise ValueError("a_fp4 must be [M, K/2] uint8 with unit stride along K")
     if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
         raise ValueError("bias must be bf16 [N]")
     code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
@@ -171,7 +178,7 @@ def mxfp4_gemm_a4w4(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre: torch.Te
     ws_bytes = int(lib().mxfp4_gemm_workspace_bytes(M, N, K))
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_fp4.device) if ws_bytes else None
     _check("mxfp4_gemm_a4w4", lib().mxfp4_gemm_a4w4(
-        _ptr(a_fp4), a_fp4.stride(0), _ptr(a_scales), _ptr(w_pre), _ptr(ws_pre), _ptr(bias),
+        _ptr(a_fp4), _ptr(a_scales), _ptr(w_pre), _ptr(ws_pre), _ptr(bias),
         _ptr(out), out.stride(0), code, M, N, K, _ptr(workspace), ws_bytes, _stream(a_fp4.device)))
     return out
 
@@ -217,13 +224,21 @@ class MXFP4Weight:
 
 
 def quantize_weight(w: torch.Tensor) -> MXFP4Weight:
-    """Load-time path: bf16 weight [N, K] or [B, N, K] -> quantise per 1x32 -> preshuffle."""
+    """Load-time path: bf16 weight [N, K] or [B, N, K] -> MXFP4 in the GEMM layouts.
+
+    One matrix (or N a multiple of 16) is quantised straight into the GEMM
+    layout; otherwise row-major quantisation is followed by the preshuffle,
+    which pads each batch entry to 16 rows.
+    """
     _require_cuda(w, "w")
     w3 = w if w.dim() == 3 else w.unsqueeze(0)
     B, N, K = w3.shape
     flat = w3.reshape(B * N, K)
-    q, s = mxfp4_quant_1x32(flat, MXFP4_SCALES_ROWMAJOR)
-    w_pre, ws_pre = mxfp4_preshuffle_weight(q, s, N, K, batch=B)
+    if B == 1 or N % 16 == 0:
+        w_pre, ws_pre = mxfp4_quant_1x32(flat, MXFP4_LAYOUT_GEMM)
+    else:
+        q, s = mxfp4_quant_1x32(flat, MXFP4_LAYOUT_ROWMAJOR)
+        w_pre, ws_pre = mxfp4_preshuffle_weight(q, s, N, K, batch=B)
     return MXFP4Weight(w_pre, ws_pre, N, K, B)
 
 
@@ -232,6 +247,7 @@ def linear(x: torch.Tensor, weight: MXFP4Weight, bias: Optional[torch.Tensor] = 
     """W4A4 linear: quantise bf16 activations [..., K] per 1x32, then the FP4 GEMM."""
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1])
-    q, s = mxfp4_quant_1x32(x2, MXFP4_SCALES_GEMM)
-    y = mxfp4_gemm_a4w4(q, s, weight.w_pre, weight.ws_pre, weight.N, weight.K, bias, out_dtype)
+    q, s = mxfp4_quant_1x32(x2, MXFP4_LAYOUT_GEMM)
+    y = mxfp4_gemm_a4w4(q, s, weight.w_pre, weight.ws_pre, x2.shape[0], weight.N, weight.K,
+                        bias, out_dtype)
     return y.reshape(*lead, weight.N)

@@ -29,7 +29,8 @@ int64_t gemm_scale_bytes(int64_t rows, int64_t K) {
   const int64_t kt = cdiv(K, 128), g = cdiv(kt, 4);
   return cdiv(rows, 16) * g * 256;
 }
-int64_t weight_bytes_one(int64_t N, int64_t K) { return cdiv(N, 16) * cdiv(K, 128) * 1024; }
+int64_t gemm_data_bytes(int64_t rows, int64_t K) { return cdiv(rows, 16) * cdiv(K, 128) * 1024; }
+int64_t weight_bytes_one(int64_t N, int64_t K) { return gemm_data_bytes(N, K); }
 
 // 0 = unknown, 1 = gfx950, 2 = other; per device ordinal.
 int g_dev_kind[64];
@@ -71,10 +72,17 @@ const char* mxfp4_status_str(int status) {
 
 int mxfp4_abi_version(void) { return 100; }
 
+size_t mxfp4_data_bytes(int64_t rows, int64_t K, int layout) {
+  if (rows < 0 || K <= 0 || K % 32) return 0;
+  if (layout == MXFP4_LAYOUT_ROWMAJOR) return (size_t)(rows * (K / 2));
+  if (layout == MXFP4_LAYOUT_GEMM) return (size_t)gemm_data_bytes(rows, K);
+  return 0;
+}
+
 size_t mxfp4_scale_bytes(int64_t rows, int64_t K, int layout) {
   if (rows < 0 || K <= 0 || K % 32) return 0;
-  if (layout == MXFP4_SCALES_ROWMAJOR) return (size_t)(rows * (K / 32));
-  if (layout == MXFP4_SCALES_GEMM) return (size_t)gemm_scale_bytes(rows, K);
+  if (layout == MXFP4_LAYOUT_ROWMAJOR) return (size_t)(rows * (K / 32));
+  if (layout == MXFP4_LAYOUT_GEMM) return (size_t)gemm_scale_bytes(rows, K);
   return 0;
 }
 
@@ -94,17 +102,22 @@ size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
-                     void* scales, int scale_layout, void* stream) {
-  if (scale_layout != MXFP4_SCALES_ROWMAJOR && scale_layout != MXFP4_SCALES_GEMM) return MXFP4_ERR_ARG;
+                     void* scales, int layout, void* stream) {
+  if (layout != MXFP4_LAYOUT_ROWMAJOR && layout != MXFP4_LAYOUT_GEMM) return MXFP4_ERR_ARG;
   if (M < 0 || K <= 0 || K % 32 || M > kMaxBuf || K > kMaxK) return MXFP4_ERR_SHAPE;
-  if (ldx < K || ldq < K / 2) return MXFP4_ERR_SHAPE;
-  if (mxfp4_scale_bytes(M, K, scale_layout) > (size_t)kMaxBuf) return MXFP4_ERR_SHAPE;
+  if (ldx < K) return MXFP4_ERR_SHAPE;
+  if (layout == MXFP4_LAYOUT_ROWMAJOR && ldq < K / 2) return MXFP4_ERR_SHAPE;
+  if (mxfp4_scale_bytes(M, K, layout) > (size_t)kMaxBuf ||
+      (layout == MXFP4_LAYOUT_GEMM && mxfp4_data_bytes(M, K, layout) > (size_t)kMaxBuf))
+    return MXFP4_ERR_SHAPE;
   if (M == 0) return MXFP4_OK;  // nothing to read or write in either layout
   if (!x || !q || !scales) return MXFP4_ERR_NULL;
-  if (!aligned(x, 16) || ldx % 8 || !aligned(q, 4) || ldq % 4) return MXFP4_ERR_ALIGN;
+  if (!aligned(x, 16) || ldx % 8) return MXFP4_ERR_ALIGN;
+  if (layout == MXFP4_LAYOUT_ROWMAJOR && (!aligned(q, 4) || ldq % 4)) return MXFP4_ERR_ALIGN;
+  if (layout == MXFP4_LAYOUT_GEMM && (!aligned(q, 16) || !aligned(scales, 4))) return MXFP4_ERR_ALIGN;
   int st = check_device();
   if (st) return st;
-  return launched(launch_quant_1x32(x, M, K, ldx, q, ldq, scales, scale_layout, (hipStream_t)stream));
+  return launched(launch_quant_1x32(x, M, K, ldx, q, ldq, scales, layout, (hipStream_t)stream));
 }
 
 int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales, int64_t batch, int64_t N,
@@ -120,27 +133,27 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales, int64_t bat
   return launched(launch_preshuffle(w_fp4, w_scales, batch, N, K, w_out, ws_out, (hipStream_t)stream));
 }
 
-int mxfp4_gemm_a4w4(const void* a_fp4, int64_t lda, const void* a_scales, const void* w_pre,
+int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
                     const void* ws_pre, const void* bias, void* out, int64_t ldo, int out_dtype,
                     int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                     void* stream) {
   if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
-  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf) return MXFP4_ERR_SHAPE;
-  if (lda < K / 2 || ldo < N) return MXFP4_ERR_SHAPE;
+  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (ldo < N) return MXFP4_ERR_SHAPE;
   if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
-      gemm_scale_bytes(M, K) > kMaxBuf || 256 * lda > kMaxBuf || 64 * lda > kMaxBuf)
+      gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
     return MXFP4_ERR_SHAPE;
   if (workspace_bytes < mxfp4_gemm_workspace_bytes(M, N, K)) return MXFP4_ERR_WORKSPACE;
   if (M == 0) return MXFP4_OK;
   if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out) return MXFP4_ERR_NULL;
-  if (!aligned(a_fp4, 16) || lda % 16 || !aligned(a_scales, 4) || !aligned(w_pre, 16) ||
+  if (!aligned(a_fp4, 16) || !aligned(a_scales, 4) || !aligned(w_pre, 16) ||
       !aligned(ws_pre, 4) || !aligned(out, 4) || (bias && !aligned(bias, 2)))
     return MXFP4_ERR_ALIGN;
   int st = check_device();
   if (st) return st;
   GemmArgs p;
   p.a = (const uint8_t*)a_fp4;
-  p.lda = lda;
   p.as = (const uint8_t*)a_scales;
   p.w = (const uint8_t*)w_pre;
   p.ws = (const uint8_t*)ws_pre;

@@ -7,103 +7,131 @@
 // weights from HBM, so the kernel is organised around that stream:
 //
 //  * a workgroup owns NS 16-row weight strips over the whole K; its KW waves
-//    split K into contiguous runs of 128-wide K-steps (intra-workgroup
-//    split-K), so no partial sums leave the chip;
-//  * per K-step a wave issues one 16-byte load per lane for each strip (a
-//    whole 1 KiB preshuffled unit, fully coalesced) and one per 16-row
-//    activation tile (row-major packed FP4, masked to zero past M and past
-//    K), plus the matching scale dwords, for UNROLL steps before it issues
-//    the MFMAs, to keep several KiB in flight per wave;
+//    split the K-step groups (4 K-steps of 128 = one scale dword) evenly
+//    (intra-workgroup split-K), so no partial sums leave the chip;
+//  * a wave issues every load of a round of GPR groups at once -- per K-step
+//    one 16-byte load per lane for each strip (a whole preshuffled 1 KiB
+//    unit, non-temporal: it is read exactly once) and for each 16-row
+//    activation tile (a 1 KiB unit of the GEMM activation layout, shared by
+//    all workgroups through L2), plus one scale dword per tile and group --
+//    and only then waits, so typically the whole K-run of a wave costs one
+//    memory round trip;
 //  * block scales are applied by the MFMA itself (v_mfma_scale 16x16x128,
-//    both operands E2M1), accumulation in fp32;
-//  * the KW partial tiles are summed through LDS in a fixed order (run to
-//    run identical results), the bias is added in fp32 and the result is
+//    both operands E2M1, op_sel picking the K-step's byte), fp32 accumulate;
+//  * the KW partial tiles are summed through LDS in a fixed order (results
+//    identical run to run), the bias is added in fp32 and the result is
 //    rounded once to bf16 (or stored as fp32).
 #include "mxfp4_device.h"
 #include "mxfp4_launch.h"
 
 namespace mxfp4 {
 
-template <int MT, int NS, int KW, int UNROLL>
-__global__ __launch_bounds__(64 * KW) void gemm_decode_kernel(GemmArgs p) {
-  __shared__ v4f red[KW][MT * NS][64];
+namespace {
+
+constexpr int kAuxNT = 2;  // cache policy bits of a buffer load: non-temporal
+
+template <int SEL>
+__device__ __forceinline__ v4f mfma_sel(const int4& a, const int4& b, uint32_t sa, uint32_t sb, v4f acc) {
+  return mfma_fp4<SEL, SEL>(a, b, sa, sb, acc);
+}
+
+}  // namespace
+
+template <int MT, int NS, int GPR, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int gpw) {
+  extern __shared__ v4f red[];  // [KW][MT * NS][64]
+  constexpr int STEPS = 4 * GPR;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
+  const int KW = blockDim.x >> 6;
   const int s0 = blockIdx.x * NS;
-  const int nblocks = p.K >> 5;
 
-  // Contiguous run of K-steps for this wave.
-  const int per = p.Kt / KW, rem = p.Kt % KW;
-  const int t0 = wv * per + min(wv, rem);
-  const int t1 = t0 + per + (wv < rem ? 1 : 0);
-
-  const uint32_t a_bytes = (uint32_t)min<int64_t>((int64_t)p.M * p.lda, 0x7FFFFFFF);
-  const auto ra = make_rsrc(p.a, a_bytes);
+  const auto ra = make_rsrc(p.a, (uint32_t)MT * p.Kt * 1024u);
   const auto rw = make_rsrc(p.w, (uint32_t)p.Ns * p.Kt * 1024u);
-  const auto ras = make_rsrc(p.as, (uint32_t)((p.M + 15) / 16) * p.G * 256u);
+  const auto ras = make_rsrc(p.as, (uint32_t)MT * p.G * 256u);
   const auto rws = make_rsrc(p.ws, (uint32_t)p.Ns * p.G * 256u);
 
-  const int kb = lane >> 4, rl = lane & 15;
   v4f acc[MT][NS];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  for (int tb = t0; tb < t1; tb += UNROLL) {
-    int4 af[UNROLL][MT], bf[UNROLL][NS];
-    uint32_t sa[UNROLL][MT], sb[UNROLL][NS];
+  const int g_begin = wv * gpw;
+  const int g_end = min(g_begin + gpw, p.G);
+  for (int gr = g_begin; gr < g_end; gr += GPR) {
+    int4 bf[STEPS][NS], af[STEPS][MT];
+    uint32_t sa[GPR][MT], sb[GPR][NS];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int t = tb + u;
-      const bool tv = t < t1;
-      const int c = t * 4 + kb;
-      const int g = t >> 2;
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int row = i * 16 + rl;
-        const uint32_t off = (tv && row < p.M && c < nblocks)
-                                 ? (uint32_t)(row * p.lda + t * 64 + kb * 16)
-                                 : kOOB;
-        af[u][i] = buf_load16(ra, off);
-        sa[u][i] = buf_load4(ras, tv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
-      }
+    for (int u = 0; u < STEPS; ++u) {
+      const int t = gr * 4 + u;
+      const bool tv = (gr + u / 4) < g_end && t < p.Kt;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int s = s0 + j;
-        const bool ok = tv && s < p.Ns;
-        bf[u][j] = buf_load16(rw, ok ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB);
-        sb[u][j] = buf_load4(rws, ok ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
+        const uint32_t off = (tv && s < p.Ns) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
+        bf[u][j] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
       }
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int sh = ((tb + u) & 3) * 8;
+    for (int q = 0; q < GPR; ++q) {
+      const int g = gr + q;
+      const bool gv = g < g_end;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int s = s0 + j;
+        sb[q][j] = buf_load4(rws, (gv && s < p.Ns) ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) sa[q][i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+    }
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const int t = gr * 4 + u;
+      const bool tv = (gr + u / 4) < g_end && t < p.Kt;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        // rows past M are zero padding: skip their bytes
+        const bool rv = i * 16 + (lane & 15) < p.M;
+        af[u][i] = buf_load16(ra, (tv && rv) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+      }
+    }
+    // Keep every load of the round ahead of the first wait: without this the
+    // scheduler interleaves loads and MFMAs to save registers, which turns one
+    // memory round trip into several.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NS; ++j)
-          acc[i][j] = mfma_fp4<0, 0>(af[u][i], bf[u][j], sa[u][i] >> sh, sb[u][j] >> sh, acc[i][j]);
-    }
+        for (int j = 0; j < NS; ++j) {
+          const uint32_t a_s = sa[u / 4][i], b_s = sb[u / 4][j];
+          switch (u & 3) {
+            case 0: acc[i][j] = mfma_sel<0>(af[u][i], bf[u][j], a_s, b_s, acc[i][j]); break;
+            case 1: acc[i][j] = mfma_sel<1>(af[u][i], bf[u][j], a_s, b_s, acc[i][j]); break;
+            case 2: acc[i][j] = mfma_sel<2>(af[u][i], bf[u][j], a_s, b_s, acc[i][j]); break;
+            default: acc[i][j] = mfma_sel<3>(af[u][i], bf[u][j], a_s, b_s, acc[i][j]); break;
+          }
+        }
   }
 
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NS; ++j) red[wv][i * NS + j][lane] = acc[i][j];
+    for (int j = 0; j < NS; ++j) red[(wv * MT * NS + i * NS + j) * 64 + lane] = acc[i][j];
   __syncthreads();
 
-  // Ordered sum over the KW waves; thread -> (tile, lane, register) with the
+  // Ordered sum over the KW waves; thread -> (tile, register, lane) with the
   // lane fastest so 16 consecutive threads write 16 consecutive columns.
   constexpr int TOTAL = MT * NS * 64 * 4;
-  for (int idx = threadIdx.x; idx < TOTAL; idx += 64 * KW) {
+  for (int idx = threadIdx.x; idx < TOTAL; idx += blockDim.x) {
     const int l = idx & 63;
     const int reg = (idx >> 6) & 3;
     const int tile = idx >> 8;
     const int i = tile / NS, j = tile % NS;
     float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < KW; ++w) v += red[w][tile][l][reg];
+    for (int w = 0; w < KW; ++w) v += red[(w * MT * NS + tile) * 64 + l][reg];
     const int m = i * 16 + 4 * (l >> 4) + reg;
     const int n = (s0 + j) * 16 + (l & 15);
     if (m < p.M && n < p.N) {
@@ -116,28 +144,37 @@ __global__ __launch_bounds__(64 * KW) void gemm_decode_kernel(GemmArgs p) {
   }
 }
 
-template <int MT, int NS, int KW>
-static hipError_t launch_decode_t(const GemmArgs& p, hipStream_t stream) {
+template <int MT, int NS, int GPR, int MAXW>
+static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_t stream) {
   const dim3 grid((unsigned)((p.Ns + NS - 1) / NS));
-  gemm_decode_kernel<MT, NS, KW, 4><<<grid, 64 * KW, 0, stream>>>(p);
+  const size_t lds = (size_t)kw * MT * NS * 64 * sizeof(v4f);
+  gemm_decode_kernel<MT, NS, GPR, MAXW><<<grid, 64 * kw, lds, stream>>>(p, gpw);
   return hipGetLastError();
 }
 
+// Launch shape, from a sweep on MI355X: every wave owns whole scale groups
+// (4 K-steps), at most 16 waves per workgroup (8 with more than two row
+// tiles, for registers), the groups split evenly and loaded in rounds of
+// two groups (one group beyond a single row tile, for registers); two
+// strips per workgroup reuse each activation tile unless the strips are
+// plentiful and M tiny.
 template <int MT>
 static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
-  // Enough waves per strip that each runs ~5 K-steps; two strips per
-  // workgroup once there are plenty of strips.
-  const int kw_want = (p.Kt + 4) / 5;
-  const bool two = p.Ns >= 2048;
-  if (kw_want >= 12) return two ? launch_decode_t<MT, 2, 16>(p, stream) : launch_decode_t<MT, 1, 16>(p, stream);
-  if (kw_want >= 6) return two ? launch_decode_t<MT, 2, 8>(p, stream) : launch_decode_t<MT, 1, 8>(p, stream);
-  if (kw_want >= 3) return two ? launch_decode_t<MT, 2, 4>(p, stream) : launch_decode_t<MT, 1, 4>(p, stream);
-  return two ? launch_decode_t<MT, 2, 1>(p, stream) : launch_decode_t<MT, 1, 1>(p, stream);
+  constexpr int MAXW = MT <= 2 ? 16 : 8;
+  const int gpw = (p.G + MAXW - 1) / MAXW;
+  const int kw = (p.G + gpw - 1) / gpw;
+  const bool one_strip = p.Ns >= 1024 && p.M <= 8;
+  if constexpr (MT == 1) {
+    if (gpw >= 2)
+      return one_strip ? launch_decode_t<MT, 1, 2, MAXW>(p, kw, gpw, stream)
+                       : launch_decode_t<MT, 2, 2, MAXW>(p, kw, gpw, stream);
+  }
+  return one_strip ? launch_decode_t<MT, 1, 1, MAXW>(p, kw, gpw, stream)
+                   : launch_decode_t<MT, 2, 1, MAXW>(p, kw, gpw, stream);
 }
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream) {
-  const int mt = (p.M + 15) / 16;
-  switch (mt) {
+  switch ((p.M + 15) / 16) {
     case 1: return launch_decode_mt<1>(p, stream);
     case 2: return launch_decode_mt<2>(p, stream);
     case 3: return launch_decode_mt<3>(p, stream);

@@ -12,10 +12,9 @@
 //    fetched by one buffer_load_dwordx4 ... lds per wave (global -> LDS with
 //    no register staging), so LDS holds fragments in exactly the lane order
 //    the MFMA consumes and every ds_read_b128 is conflict free;
-//  * activation fragments come from the row-major packed FP4 matrix (16
-//    rows x 64 bytes each), masked past M and past K by out-of-range buffer
-//    offsets (buffer loads return zeros there); weight fragments are whole
-//    preshuffled units;
+//  * activation and weight fragments are whole 1 KiB units of the GEMM
+//    layouts (padding already zero); tiles past the last 16-row strip read
+//    zeros through out-of-range buffer offsets;
 //  * block scales: one dword per lane per 16-row tile per 4 K-steps, read
 //    straight into registers; the op_sel byte selector of the scaled MFMA
 //    walks the 4 K-steps, so the K loop is unrolled by 4 (two stages);
@@ -36,12 +35,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct TileCtx {
   __amdgpu_buffer_rsrc_t ra, rw, ras, rws;
-  int lda, Kt, G, nblocks, rows, strips;  // rows of A / weight strips inside this tile
+  int Kt, G, mstrips, strips;  // 16-row activation tiles / weight strips inside this tile
 };
 
 // Issue the global->LDS loads of one stage (K-steps 2*st, 2*st+1).
 __device__ __forceinline__ void issue_stage(const TileCtx& c, int4 (*buf)[64], int st, int wv, int lane) {
-  const int kb = lane >> 4, rl = lane & 15;
 #pragma unroll
   for (int q = 0; q < kFrags / 8; ++q) {
     const int f = wv * (kFrags / 8) + q;
@@ -50,9 +48,7 @@ __device__ __forceinline__ void issue_stage(const TileCtx& c, int4 (*buf)[64], i
     if (f < kFragsA) {
       const int u = f >> 4, i = f & 15;
       const int t = st * 2 + u;
-      const int row = i * 16 + rl;
-      const int cblk = t * 4 + kb;
-      off = (cblk < c.nblocks && row < c.rows) ? (uint32_t)(row * c.lda + t * 64 + kb * 16) : kOOB;
+      off = (t < c.Kt && i < c.mstrips) ? (uint32_t)((i * c.Kt + t) * 1024 + lane * 16) : kOOB;
       r = c.ra;
     } else {
       const int u = (f - kFragsA) >> 4, j = (f - kFragsA) & 15;
@@ -102,16 +98,13 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int ti
   const int s0 = tn * (kBN / 16);
 
   TileCtx c;
-  c.lda = (int)p.lda;
   c.Kt = p.Kt;
   c.G = p.G;
-  c.nblocks = p.K >> 5;
-  c.rows = min(kBM, p.M - m0);
   const int strips = min(kBN / 16, p.Ns - s0);
   c.strips = strips;
-  const int mstrips_total = (p.M + 15) >> 4;
-  const int mstrips = min(kBM / 16, mstrips_total - m0 / 16);
-  c.ra = make_rsrc(p.a + (int64_t)m0 * p.lda, (uint32_t)(c.rows * p.lda));
+  const int mstrips = min(kBM / 16, ((p.M + 15) >> 4) - m0 / 16);
+  c.mstrips = mstrips;
+  c.ra = make_rsrc(p.a + (int64_t)(m0 / 16) * p.Kt * 1024, (uint32_t)mstrips * p.Kt * 1024u);
   c.rw = make_rsrc(p.w + (int64_t)s0 * p.Kt * 1024, (uint32_t)strips * p.Kt * 1024u);
   c.ras = make_rsrc(p.as + (int64_t)(m0 / 16) * p.G * 256, (uint32_t)mstrips * p.G * 256u);
   c.rws = make_rsrc(p.ws + (int64_t)s0 * p.G * 256, (uint32_t)strips * p.G * 256u);

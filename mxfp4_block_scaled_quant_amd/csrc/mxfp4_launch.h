@@ -10,8 +10,7 @@ namespace mxfp4 {
 
 // Validated, device-side view of one W4A4 GEMM call.
 struct GemmArgs {
-  const uint8_t* a;    // packed FP4 activations [M, K/2], row stride lda bytes
-  int64_t lda;
+  const uint8_t* a;    // packed FP4 activations, GEMM data layout
   const uint8_t* as;   // activation scales, GEMM scale layout
   const uint8_t* w;    // preshuffled weights
   const uint8_t* ws;   // weight scales, GEMM scale layout

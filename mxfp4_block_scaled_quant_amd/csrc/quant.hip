@@ -12,13 +12,17 @@
 // against the rounding midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 (strict '>'
 // where the midpoint rounds down to the even code, '>=' where it rounds up).
 //
-// Work split: one wave per 512-element row segment (16 blocks); lane l owns
-// 8 consecutive elements (one 16-byte load, one 4-byte store), lanes
-// 4j..4j+3 share block j and combine their amax with two xor shuffles.
-// In the GEMM scale layout the grid also covers the padding rows (up to a
-// multiple of 16) and padding blocks (up to a multiple of 16 per row), where
-// it writes 0x7F: P2 §2 pads activation scales with E8M0 1.0 because whole
-// tiles are read and 0xFF would be NaN.
+// Two output forms:
+//  * ROWMAJOR (weights before a preshuffle, interop): one wave per
+//    512-element row segment (16 blocks); lane l owns 8 consecutive elements
+//    (one 16-byte load, one 4-byte store), lanes 4j..4j+3 share block j and
+//    combine their amax with two xor shuffles.
+//  * GEMM (what the FP4 GEMM reads): one workgroup per 1 KiB unit of the
+//    GEMM data layout (16 rows x one 128-wide K-step), same 8 elements per
+//    lane.  The grid covers the padding rows (to 16) and K-steps (to the
+//    4-step scale group) and writes 0x00 data and 0x7F scales there: P2 §2
+//    pads scale tiles with E8M0 1.0 because whole tiles are read and 0xFF
+//    would be NaN.
 #include "mxfp4_device.h"
 #include "mxfp4_launch.h"
 
@@ -41,14 +45,12 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t h, uint32_t b) {
   return c | ((h >> 12) & 8u);
 }
 
-template <int LAYOUT>
-__global__ __launch_bounds__(256) void quant_1x32_kernel(
+__global__ __launch_bounds__(256) void quant_1x32_rowmajor_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K,
-    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales,
-    int rows_cover, int segs, int G) {
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int segs) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= (int64_t)rows_cover * segs) return;
+  if (wave >= (int64_t)M * segs) return;
   const int r = (int)(wave / segs), seg = (int)(wave % segs);
   const int nblocks = K >> 5;
   const int c = seg * 16 + (lane >> 2);
@@ -80,32 +82,72 @@ __global__ __launch_bounds__(256) void quant_1x32_kernel(
     for (int i = 0; i < 8; ++i) packed |= e2m1_code(h[i], b) << (4 * i);
     *reinterpret_cast<uint32_t*>(q + (int64_t)r * ldq + (k0 >> 1)) = packed;
   }
-  if ((lane & 3) == 0) {
-    if (LAYOUT == 0) {
-      if (valid) scales[(int64_t)r * nblocks + c] = (uint8_t)b;
-    } else {
-      scales[gemm_scale_offset(r, c, G)] = valid ? (uint8_t)b : (uint8_t)kE8M0One;
+  if ((lane & 3) == 0 && valid) scales[(int64_t)r * nblocks + c] = (uint8_t)b;
+}
+
+// GEMM layout: one 256-thread workgroup per 1 KiB unit (16-row strip s,
+// K-step t).  Lane L takes row r = L/16 and the 8 elements [8q, 8q+8) of block
+// kb of that K-step, (kb, q) = ((L%16)/4, L%4): 16 consecutive lanes read one
+// row's 256 contiguous bytes; the 4 lanes of a block combine their amax with
+// two xor shuffles and store their 4 packed bytes into the block's 16-byte
+// slot kb*16 + r.  Units past the last K-step only fill scale padding.
+__global__ __launch_bounds__(256) void quant_1x32_gemm_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, int M, int K, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ scales, int Kt, int G) {
+  const int L = threadIdx.x;
+  const int tq = blockIdx.x % (4 * G);          // K-step, including scale-only padding steps
+  const int s = blockIdx.x / (4 * G);
+  const int r = L >> 4, kb = (L >> 2) & 3, sub = L & 3;
+  const int row = s * 16 + r;
+  const int c = tq * 4 + kb;
+  const bool valid = row < M && c < (K >> 5);
+
+  uint32_t h[8];
+  uint32_t amax = 0;
+  if (valid) {
+    const int4 v = *reinterpret_cast<const int4*>(x + (int64_t)row * ldx + (int64_t)c * 32 + sub * 8);
+    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = w[i] & 0xFFFFu;
+      h[2 * i + 1] = w[i] >> 16;
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = max(amax, h[i] & 0x7FFFu);
   }
+  // The 4 lanes of a block are aligned and all valid or all invalid.
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  const uint32_t e = amax >> 7;
+  const uint32_t b = valid ? (e > 2 ? e - 2 : 0) : kE8M0One;
+
+  if (tq < Kt) {
+    uint32_t packed = 0;
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) packed |= e2m1_code(h[i], b) << (4 * i);
+    }
+    *reinterpret_cast<uint32_t*>(q + (int64_t)(s * Kt + tq) * 1024 + (kb * 16 + r) * 16 + sub * 4) = packed;
+  }
+  if (sub == 0) scales[(int64_t)(s * G + (tq >> 2)) * 256 + (kb * 16 + r) * 4 + (tq & 3)] = (uint8_t)b;
 }
 
 hipError_t launch_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q,
                              int64_t ldq, void* scales, int layout, hipStream_t stream) {
   const int Kt = (int)((K + 127) / 128);
   const int G = (Kt + 3) / 4;
-  const int segs = (int)((K + 511) / 512);
-  const int rows_cover = layout == 0 ? (int)M : (int)((M + 15) / 16 * 16);
-  const int64_t waves = (int64_t)rows_cover * segs;
-  if (waves == 0) return hipSuccess;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (layout == 0)
-    quant_1x32_kernel<0><<<grid, 256, 0, stream>>>((const uint16_t*)x, ldx, (int)M, (int)K,
-                                                    (uint8_t*)q, ldq, (uint8_t*)scales,
-                                                    rows_cover, segs, G);
-  else
-    quant_1x32_kernel<1><<<grid, 256, 0, stream>>>((const uint16_t*)x, ldx, (int)M, (int)K,
-                                                    (uint8_t*)q, ldq, (uint8_t*)scales,
-                                                    rows_cover, segs, G);
+  if (layout == 0) {
+    const int segs = (int)((K + 511) / 512);
+    const int64_t waves = M * segs;
+    if (waves == 0) return hipSuccess;
+    quant_1x32_rowmajor_kernel<<<dim3((unsigned)((waves + 3) / 4)), 256, 0, stream>>>(
+        (const uint16_t*)x, ldx, (int)M, (int)K, (uint8_t*)q, ldq, (uint8_t*)scales, segs);
+  } else {
+    const int64_t units = (M + 15) / 16 * (int64_t)(4 * G);
+    if (units == 0) return hipSuccess;
+    quant_1x32_gemm_kernel<<<dim3((unsigned)units), 256, 0, stream>>>(
+        (const uint16_t*)x, ldx, (int)M, (int)K, (uint8_t*)q, (uint8_t*)scales, Kt, G);
+  }
   return hipGetLastError();
 }
 

@@ -31,6 +31,14 @@ Preshuffled weight layout (W4A4 GEMM and A16WFP4 BMM weights)
     Weight scales for it use the GEMM scale layout per batch entry, with the
     batch entries concatenated.
 
+GEMM activation layout
+    Quantised activations for the GEMM use the preshuffled weight layout
+    with the M rows in place of N (batch 1): 1 KiB units of 16 rows x 128 K,
+    slot kb*16 + r = row r's block kb, rows padded to 16 and K to 128 with
+    zero bytes; their scales use the GEMM scale layout.  So a weight prepared
+    by quantising straight into the GEMM layout is bytewise the preshuffled
+    weight.
+
 Pins (tests/test_oracle_layout.py): forward/inverse bijection over all
 in-range indices; every non-image byte is the documented fill; hand-placed
 positions worked from the formulas above; an independent reshape/transpose
@@ -155,6 +163,13 @@ def unshuffle_weight(data, scales, B: int, N: int, K: int):
     scales = np.asarray(scales, dtype=np.uint8).reshape(B, sbytes)
     sc = np.stack([scales_from_gemm_layout(scales[i], N, K) for i in range(B)])
     return packed, sc
+
+
+def to_gemm_layout(packed, scales_rm):
+    """Row-major packed FP4 [R, K/2] + scales [R, K/32] -> GEMM-layout (data, scales).
+
+    The activation form of the preshuffled layout (batch 1)."""
+    return preshuffle_weight(np.asarray(packed)[None], np.asarray(scales_rm)[None])
 
 
 # --------------------------------------------------------------------------

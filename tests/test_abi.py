@@ -52,6 +52,8 @@ def test_status_strings_and_version(lib):
 def test_scale_bytes_match_oracle_geometry(lib, rows, K):
     assert lib.mxfp4_scale_bytes(rows, K, 0) == rows * K // 32
     assert lib.mxfp4_scale_bytes(rows, K, 1) == L.gemm_scale_geometry(rows, K)[3]
+    assert lib.mxfp4_data_bytes(rows, K, 0) == rows * K // 2
+    assert lib.mxfp4_data_bytes(rows, K, 1) == L.weight_geometry(rows, K)[2]
 
 
 @pytest.mark.parametrize("B,N,K", [(1, 96, 4128), (1, 34816, 5120), (16, 512, 192), (16, 256, 512)])
@@ -83,6 +85,7 @@ def test_quant_validation(lib):
     assert f(None, 4, 64, 64, P, 32, P, 1, None) == 1          # NULL x
     assert f(P_ODD, 4, 64, 64, P, 32, P, 1, None) == 3         # x misaligned
     assert f(P, 4, 64, 68, P, 32, P, 1, None) == 3             # ldx % 8
+    assert f(P, 4, 64, 64, P_ODD, 32, P, 1, None) == 3         # GEMM-layout q not 16-aligned
     assert f(None, 0, 64, 64, None, 32, None, 1, None) == 0    # M == 0: nothing to do
 
 
@@ -96,21 +99,20 @@ def test_preshuffle_validation(lib):
 
 def test_gemm_validation(lib):
     f = lib.mxfp4_gemm_a4w4
-    ok = dict(a=P, lda=32, as_=P, w=P, ws=P, bias=None, out=P, ldo=16, dt=0, M=4, N=16, K=64)
+    ok = dict(a=P, as_=P, w=P, ws=P, bias=None, out=P, ldo=16, dt=0, M=4, N=16, K=64)
 
     def call(**kw):
         d = dict(ok)
         d.update(kw)
-        return f(d["a"], d["lda"], d["as_"], d["w"], d["ws"], d["bias"], d["out"], d["ldo"],
+        return f(d["a"], d["as_"], d["w"], d["ws"], d["bias"], d["out"], d["ldo"],
                  d["dt"], d["M"], d["N"], d["K"], None, 0, None)
 
     assert call(dt=3) == 7
-    assert call(K=48, lda=32) == 2
+    assert call(K=48) == 2
     assert call(N=0) == 2
-    assert call(lda=16) == 2        # lda < K/2
+    assert call(M=-1) == 2
     assert call(ldo=8) == 2         # ldo < N
     assert call(w=None) == 1
-    assert call(lda=40) == 3        # lda % 16
     assert call(a=P_ODD) == 3
     assert call(M=0, a=None) == 0   # nothing to do
 
@@ -136,7 +138,8 @@ def test_valid_call_without_gpu_reports_device(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: fake pointers must not reach a kernel")
     assert lib.mxfp4_quant_1x32(P, 4, 64, 64, P, 32, P, 1, None) == 5
-    assert lib.mxfp4_gemm_a4w4(P, 32, P, P, P, None, P, 16, 0, 4, 16, 64, None, 0, None) == 5
+    assert lib.mxfp4_quant_1x32(P, 4, 64, 64, P, 0, P, 1, None) == 5   # ldq ignored (GEMM layout)
+    assert lib.mxfp4_gemm_a4w4(P, P, P, P, None, P, 16, 0, 4, 16, 64, None, 0, None) == 5
 
 
 def test_debug_path_hook(lib):

@@ -84,7 +84,7 @@ def test_bmm_exact_mxfp4_activations_match_gemm():
     for b in range(B):
         W = mx.quantize_weight(dev_bf16(prob["w"][b]))
         q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"][b]))
-        g = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, N, K, None, torch.float32).cpu().numpy()
+        g = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, None, torch.float32).cpu().numpy()
         ref, S = G.gemm_a4w4_from_quant(qx[b], sx[b], *Q.quant_1x32(prob["w"][b]))
         check_f32_tolerance(g, ref, S)
         check_f32_tolerance(y32[b], ref, S)

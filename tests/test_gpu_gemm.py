@@ -31,9 +31,9 @@ def _run(prob, path, weight=None):
     b = dev_bf16(prob["bias"]) if prob["bias"] is not None else None
     mx.set_gemm_path(path)
     try:
-        q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_SCALES_GEMM)
-        y32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, N, K, b, torch.float32)
-        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, N, K, b, torch.bfloat16)
+        q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
+        y32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
+        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16)
     finally:
         mx.set_gemm_path(0)
     torch.cuda.synchronize()

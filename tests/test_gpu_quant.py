@@ -36,16 +36,20 @@ def _gpu_quant(x_bits, layout, ldx_pad=0, ldq_pad=0):
     q = None
     if ldq_pad:
         q = torch.full((M, K // 2 + ldq_pad), 0xAB, dtype=torch.uint8, device="cuda")[:, :K // 2]
-    q, s = mx.mxfp4_quant_1x32(x, layout, q=q)
+    elif layout == mx.MXFP4_LAYOUT_GEMM:
+        # poison the output so every padding byte must be written
+        q = torch.full((mx.data_bytes(M, K, layout),), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((mx.scale_bytes(M, K, layout),), 0xFF, dtype=torch.uint8, device="cuda")
+    q, s = mx.mxfp4_quant_1x32(x, layout, q=q, scales=s)
     torch.cuda.synchronize()
     return host_u8(q), host_u8(s)
 
 
 def _expect(x_bits, layout):
     q_ref, s_ref = Q.quant_1x32(x_bits)
-    if layout == mx.MXFP4_SCALES_ROWMAJOR:
+    if layout == mx.MXFP4_LAYOUT_ROWMAJOR:
         return q_ref, s_ref.ravel()
-    return q_ref, L.scales_to_gemm_layout(s_ref)
+    return L.to_gemm_layout(q_ref, s_ref)
 
 
 @pytest.mark.parametrize("layout", [0, 1], ids=["rowmajor", "gemm"])
@@ -114,7 +118,10 @@ def test_quant_scale_exponent_sweep_with_ties():
 def test_quant_strided_input_and_output():
     need_gpu()
     x = inputs.activations(37, 4128, 5, edge=True)
-    q, s = _gpu_quant(x, 1, ldx_pad=24, ldq_pad=12)
+    q, s = _gpu_quant(x, 0, ldx_pad=24, ldq_pad=12)
+    q_ref, s_ref = _expect(x, 0)
+    assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
+    q, s = _gpu_quant(x, 1, ldx_pad=24)
     q_ref, s_ref = _expect(x, 1)
     assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
 
@@ -128,7 +135,8 @@ def test_quant_full_prefill_size_sampled_rows():
     q, s = _gpu_quant(x, 1)
     rows = np.unique(np.concatenate([[0, 1, M - 1], np.random.default_rng(0).choice(M, 45, replace=False)]))
     q_ref, s_ref = Q.quant_1x32(x[rows])
-    assert np.array_equal(q[rows], q_ref)
+    rr, kk = np.meshgrid(rows, np.arange(0, K, 2), indexing="ij")
+    assert np.array_equal(q[L.weight_byte_offset(0, rr, kk, M, K)], q_ref)
     G = L.gemm_scale_geometry(M, K)[2]
     rr, cc = np.meshgrid(rows, np.arange(K // 32), indexing="ij")
     assert np.array_equal(s[L.gemm_scale_offset(rr, cc, G)], s_ref)
@@ -143,29 +151,37 @@ PRESHUFFLE_CASES = [
 ]
 
 
-def _gpu_weight(w_bits_3d):
+def _gpu_preshuffle(w_bits_3d):
+    """Row-major GPU quant, then the GPU preshuffle (the checkpoint path)."""
     B, N, K = w_bits_3d.shape
-    W = mx.quantize_weight(dev_bf16(w_bits_3d.reshape(B * N, K)).reshape(B, N, K))
+    q, s = mx.mxfp4_quant_1x32(dev_bf16(w_bits_3d.reshape(B * N, K)), mx.MXFP4_LAYOUT_ROWMAJOR)
+    d, sc = mx.mxfp4_preshuffle_weight(q, s, N, K, batch=B)
     torch.cuda.synchronize()
-    return host_u8(W.w_pre), host_u8(W.ws_pre)
+    return host_u8(d), host_u8(sc)
 
 
 @pytest.mark.parametrize("name,B,N,K", PRESHUFFLE_CASES, ids=[c[0] for c in PRESHUFFLE_CASES])
 def test_preshuffle_bit_exact(name, B, N, K):
     need_gpu()
     w = np.stack([inputs.weights(N, K, 4, tag=(b,)) for b in range(B)])
-    d, s = _gpu_weight(w)
     q_ref, s_ref = Q.quant_1x32(w)
     d_ref, sc_ref = L.preshuffle_weight(q_ref, s_ref)
+    d, s = _gpu_preshuffle(w)
     assert np.array_equal(d, d_ref)
     assert np.array_equal(s, sc_ref)
+    # the load-time helper (direct GEMM-layout quantisation when the batch
+    # entries align to 16 rows) produces the same bytes
+    W = mx.quantize_weight(dev_bf16(w.reshape(B * N, K)).reshape(B, N, K))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(W.w_pre), d_ref)
+    assert np.array_equal(host_u8(W.ws_pre), sc_ref)
 
 
 def test_preshuffle_full_size_sampled_strips():
     need_gpu()
     N, K = 34816, 5120
     w = inputs.weights(N, K, 2)
-    d, s = _gpu_weight(w[None])
+    d, s = _gpu_preshuffle(w[None])
     _, kt, _ = L.weight_geometry(N, K)
     G = L.gemm_scale_geometry(N, K)[2]
     for st in (0, 1, 777, N // 16 - 1):
