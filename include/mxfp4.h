@@ -144,7 +144,7 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
  *   w_pre, ws_pre    weights in the same layouts (one batch entry)
  *   bias      bf16 [N] or NULL
  *   out       [M, N], row stride ldo ELEMENTS, bf16 or fp32 per out_dtype
- *             (ldo >= N; 4-byte aligned)
+ *             (N <= ldo < 2^22 for bf16, < 2^21 for fp32; 4-byte aligned)
  *   workspace may be NULL when mxfp4_gemm_workspace_bytes() returns 0.
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
  * Results are identical run to run (no atomics; fixed reduction order).

@@ -32,19 +32,26 @@ int64_t gemm_scale_bytes(int64_t rows, int64_t K) {
 int64_t gemm_data_bytes(int64_t rows, int64_t K) { return cdiv(rows, 16) * cdiv(K, 128) * 1024; }
 int64_t weight_bytes_one(int64_t N, int64_t K) { return gemm_data_bytes(N, K); }
 
-// 0 = unknown, 1 = gfx950, 2 = other; per device ordinal.
-int g_dev_kind[64];
+// Per device ordinal: 0 = unknown, 1 = gfx950, 2 = other; and its compute
+// unit count (written before the kind is published).
+std::atomic<int> g_dev_kind[64];
+std::atomic<int> g_dev_cus[64];
 
-int check_device() {
+// Checks that the current device is a gfx950; on success *cus (if given)
+// receives its compute-unit count.
+int check_device(int* cus = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MXFP4_ERR_DEVICE;
   if (dev < 0 || dev >= 64) return MXFP4_ERR_DEVICE;
-  if (g_dev_kind[dev] == 0) {
+  if (g_dev_kind[dev].load(std::memory_order_acquire) == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXFP4_ERR_DEVICE;
-    g_dev_kind[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1, std::memory_order_relaxed);
+    g_dev_kind[dev].store(strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2, std::memory_order_release);
   }
-  return g_dev_kind[dev] == 1 ? MXFP4_OK : MXFP4_ERR_DEVICE;
+  if (g_dev_kind[dev].load(std::memory_order_acquire) != 1) return MXFP4_ERR_DEVICE;
+  if (cus) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return MXFP4_OK;
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_LAUNCH; }
@@ -141,6 +148,8 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
     return MXFP4_ERR_SHAPE;
   if (ldo < N) return MXFP4_ERR_SHAPE;
+  // 256 output rows (one prefill tile) must stay addressable by 32-bit offsets
+  if (ldo > kMaxBuf / 256 / (out_dtype == MXFP4_OUT_F32 ? 4 : 2)) return MXFP4_ERR_SHAPE;
   if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
       gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
     return MXFP4_ERR_SHAPE;
@@ -150,9 +159,11 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   if (!aligned(a_fp4, 16) || !aligned(a_scales, 4) || !aligned(w_pre, 16) ||
       !aligned(ws_pre, 4) || !aligned(out, 4) || (bias && !aligned(bias, 2)))
     return MXFP4_ERR_ALIGN;
-  int st = check_device();
+  int cus = 0;
+  int st = check_device(&cus);
   if (st) return st;
   GemmArgs p;
+  p.cus = cus;
   p.a = (const uint8_t*)a_fp4;
   p.as = (const uint8_t*)a_scales;
   p.w = (const uint8_t*)w_pre;

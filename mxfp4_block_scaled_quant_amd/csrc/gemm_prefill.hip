@@ -4,29 +4,33 @@
 // the preshuffled [N, K] weight, NT form, bias after; P1 §Accuracy Tests:
 // equal to the dequantised reference), organised for the MFMA roofline:
 //
-//  * a 512-thread workgroup computes a 256 x 256 output tile; its 8 waves
-//    (two per SIMD, so one can issue while the other waits) form a 2 x 4
-//    grid of 128 x 64 wave tiles, 8 x 4 MFMA tiles of 16 x 16 each (128
-//    fp32 accumulators per lane).  One K-step (128) is 32 MFMAs per wave
-//    against 12 KiB of operand reads from LDS;
-//  * operands stream through four single-K-step LDS buffers (32 KiB each):
+//  * persistent: one 512-thread workgroup per compute unit walks a list of
+//    256 x 256 output tiles.  Its 8 waves (two per SIMD, so one can issue
+//    while the other waits) form a 2 x 4 grid of 128 x 64 wave tiles, 8 x 4
+//    MFMA tiles of 16 x 16 each (128 fp32 accumulators per lane);
+//  * operands stream through four single-K-step LDS stages (32 KiB each):
 //    every 1 KiB operand unit of the GEMM layouts (activations and weights
-//    alike) is fetched by one buffer_load_dwordx4 ... lds per wave, so LDS
-//    holds fragments in the lane order the MFMA consumes (conflict-free
-//    ds_read_b128).  Loads run three K-steps ahead; each step needs one
-//    wait (hand-counted vmcnt) and one barrier;
-//  * the next step's fragments are read while this step's MFMAs run: each
-//    activation fragment is re-read right after its row of 8 MFMAs, weight
-//    fragments alternate between two register sets;
-//  * block scales: one dword per lane per 16-row tile per 4 K-steps, loaded
-//    a group ahead; op_sel walks the 4 K-steps of a dword;
+//    alike) is fetched by one buffer_load_dwordx4 ... lds, so LDS holds
+//    fragments in the lane order the MFMA consumes (conflict-free
+//    ds_read_b128).  Loads run three K-steps ahead, across tile boundaries:
+//    the last steps of a tile already fetch the first steps of the next;
+//  * one barrier per K-step, in its middle: before it, hand-counted waits for
+//    this wave's loads of the next step; after it, the freed stage is
+//    refilled and the next step's fragments are read while the rest of this
+//    step's MFMAs run;
+//  * block scales: one dword per lane per 16-row tile per 4 K-steps.  The
+//    next group's scales go to LDS by the same kind of load and are read into
+//    registers at the group boundary; op_sel walks the 4 K-steps of a dword;
 //  * the MFMA takes the weight as its A operand and the activations as B, so
 //    a lane ends with 4 consecutive output columns of one row; the epilogue
-//    adds the bias in fp32, rounds once to bf16 and transposes through LDS to
-//    write whole 16-byte chunks of output rows (fp32 output, used for the
-//    pre-cast checks, is stored directly);
-//  * tiles are ordered in groups of 8 row-tiles and dealt to the 8 XCDs in
-//    contiguous runs, so the workgroups sharing an XCD's L2 share operands.
+//    adds the bias in fp32, rounds once and stores straight from registers
+//    (buffer stores, out-of-range lanes masked by offset) while the next
+//    tile's operands are already in flight;
+//  * tiles are ordered in groups of 8 row-tiles; each XCD's workgroups take
+//    consecutive tiles, so the tiles in flight on an XCD share its L2.
+//
+// Every register counts: at two waves per SIMD a wave has 256 registers, 128
+// of them accumulators and 64 operand fragments.
 #include "mxfp4_device.h"
 #include "mxfp4_launch.h"
 
@@ -38,34 +42,42 @@ constexpr int kBM = 256, kBN = 256;
 constexpr int kTilesA = kBM / 16;            // 16 activation units per K-step
 constexpr int kTilesB = kBN / 16;            // 16 weight units per K-step
 constexpr int kUnits = kTilesA + kTilesB;    // 32 units of 1 KiB per K-step
-constexpr int kBufs = 4;                     // LDS buffers (K-steps in flight)
+constexpr int kBufs = 4;                     // LDS stages (K-steps in flight)
 constexpr int kWaves = 8;
 constexpr int kLoadsPerWave = kUnits / kWaves;  // 4 buffer->LDS loads per wave per step
 constexpr int kWM = 8, kWN = 4;                 // wave tile: 8 x 4 MFMA tiles (128 x 64)
-constexpr int kScaleLoads = kWM + kWN;          // scale dwords per wave per group
 constexpr int kGroupM = 8;                   // row-tiles per ordering group
-constexpr int kRowB = 144;                   // epilogue staging row stride (bytes)
-constexpr int kStageBytes = kBufs * kUnits * 64 * 16;
-constexpr int kEpiBytes = kWaves * 128 * kRowB;
-constexpr int kLdsBytes = kStageBytes > kEpiBytes ? kStageBytes : kEpiBytes;
+// LDS: unit u of stage b at u * 4 KiB + b * 1 KiB (so a wave reaches its
+// fragments in all four stages from one base register), then the scales of
+// one group: 16 activation tiles, then 16 weight strips, 256 bytes each; then
+// each wave's 64 bias values of the tile (256 bytes per wave); then each
+// wave's 16-row bf16 staging area of the epilogue.
+constexpr int kStageBytes = kUnits * kBufs * 1024;  // 128 KiB
+constexpr int kScaleLds = kStageBytes;
+constexpr int kBiasLds = kScaleLds + kUnits * 256;  // + 8 KiB
+constexpr int kEpiRowB = 144;                        // epilogue staging row stride (bytes)
+constexpr int kEpiLds = kBiasLds + kWaves * 256;     // + 2 KiB
+constexpr int kLdsBytes = kEpiLds + kWaves * 16 * kEpiRowB;  // + 18 KiB: 156 KiB in all
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
+#ifndef MXFP4_STORE_AUX
+#define MXFP4_STORE_AUX 0
+#endif
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Base pointers and byte sizes of this tile's operand windows.  Buffer
-// descriptors are built after any selection between them: a select between
-// descriptors becomes a vector select, which then costs a waterfall loop per
-// buffer instruction.
-struct Ctx {
-  const uint8_t *pa, *pw, *pas, *pws;
-  uint32_t na, nw, nas, nws;
-  int Kt, G;
-};
-
-typedef int4 StageBuf[kUnits][64];
 // Fragment registers: a native 4 x 32-bit vector, so inline assembly can take
 // it as a register operand.
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ lds_ptr_t lds_at(uint32_t addr) { return (lds_ptr_t)(uintptr_t)addr; }
+
+// Lane id, recomputed where it is used (two instructions): a volatile
+// statement the compiler cannot hoist into a register that would stay live
+// through the K loop, where every register counts.
+__device__ __forceinline__ uint32_t lane_here() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 template <int SEL>
 __device__ __forceinline__ v4f mfma_fp4v(v4i a, v4i b, uint32_t sa, uint32_t sb, v4f acc) {
@@ -74,53 +86,151 @@ __device__ __forceinline__ v4f mfma_fp4v(v4i a, v4i b, uint32_t sa, uint32_t sb,
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, SEL, (int)sa, SEL, (int)sb);
 }
 
-// Issue this wave's 4 buffer->LDS loads of K-step t into stage buffer `buf`.
-// Waves 0-3 fetch the 16 activation units, waves 4-7 the 16 weight units.
-// The unit's position goes in the vector offset, so units past the tile's
-// last strip fall outside the window (zeros); steps past K use an empty
-// window; the step's position goes in the scalar offset.
-__device__ __forceinline__ void issue_step(const Ctx& c, StageBuf& buf, int t, int wv, const uint32_t (&voff)[4]) {
+// One output tile: its first 16-row activation strip and strip count, its
+// first 16-column weight strip and strip count (counts are 0 for an empty
+// tile past the end).  Buffer descriptors are derived from it where a load is
+// issued, after any selection between tiles: a select between descriptors
+// becomes a vector select, which then costs a waterfall loop per load.
+struct Tile {
+  int ms, mstrips, s0, strips;
+};
+
+// Linear tile L: tiles run down groups of kGroupM row-tiles, then across
+// columns.
+__device__ __forceinline__ Tile tile_at(const GemmArgs& p, int L, int tiles_m, int tiles_n) {
+  Tile t = {0, 0, 0, 0};
+  if (L >= tiles_m * tiles_n) return t;
+  const int group = L / (kGroupM * tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int r = L % (kGroupM * tiles_n);
+  t.ms = (first_m + r % gm) * kTilesA;
+  t.mstrips = min(kTilesA, ((p.M + 15) >> 4) - t.ms);
+  t.s0 = (r / gm) * kTilesB;
+  t.strips = min(kTilesB, p.Ns - t.s0);
+  return t;
+}
+
+// This wave's buffer->LDS load of unit q (of its 4) of K-step t of tile
+// `tl` into stage J.  Waves 0-3 fetch the 16 activation units, waves 4-7 the
+// 16 weight units.  Each unit has its own descriptor (the unit's row of
+// K-steps); units past the tile's last strip and steps past K get an empty
+// one and load zeros.  The vector offset is the lane's 16 bytes, the step
+// goes in the scalar offset (in range whenever the descriptor is not empty).
+__device__ __forceinline__ void issue_unit(const GemmArgs& p, const Tile& tl, int J, int t, int q, int wv,
+                                           uint32_t lane16) {
   const bool is_a = wv < 4;
-  const uint8_t* base = is_a ? c.pa : c.pw;
-  const uint32_t size = t < c.Kt ? (is_a ? c.na : c.nw) : 0u;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, size);
-  const int u0 = (is_a ? 0 : kTilesA) + (wv & 3) * kLoadsPerWave;
-#pragma unroll
-  for (int q = 0; q < kLoadsPerWave; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)&buf[u0 + q][0], 16, voff[q], t << 10, 0, 0);
+  const int first = is_a ? tl.ms : tl.s0;
+  const int count = t < p.Kt ? (is_a ? tl.mstrips : tl.strips) : 0;
+  const uint8_t* base = is_a ? p.a : p.w;
+  const int u = (wv & 3) * kLoadsPerWave + q;
+  const int fb = is_a ? 0 : kTilesA;
+  const uint32_t row_bytes = (uint32_t)p.Kt * 1024u;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)(first + u) * row_bytes, u < count ? row_bytes : 0u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(((fb + u) * kBufs + J) * 1024), 16, lane16, t << 10, 0, 0);
 }
 
-// Scale dwords of group g for this wave's 8 row tiles and 4 column strips.
-__device__ __forceinline__ void issue_scales(const Ctx& c, uint32_t (&sa)[kWM], uint32_t (&sb)[kWN], int g,
-                                             const uint32_t (&soff_a)[kWM], const uint32_t (&soff_b)[kWN]) {
-  const __amdgpu_buffer_rsrc_t ras = make_rsrc(c.pas, g < c.G ? c.nas : 0u);
-  const __amdgpu_buffer_rsrc_t rws = make_rsrc(c.pws, g < c.G ? c.nws : 0u);
+__device__ __forceinline__ void issue_step(const GemmArgs& p, const Tile& tl, int J, int t, int wv,
+                                           uint32_t lane16) {
 #pragma unroll
-  for (int i = 0; i < kWM; ++i) sa[i] = __builtin_amdgcn_raw_buffer_load_b32(ras, soff_a[i], g << 8, 0);
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) sb[j] = __builtin_amdgcn_raw_buffer_load_b32(rws, soff_b[j], g << 8, 0);
+  for (int q = 0; q < kLoadsPerWave; ++q) issue_unit(p, tl, J, t, q, wv, lane16);
 }
 
-// Fragment reads from LDS are written as inline assembly with hand-counted
-// lgkmcnt waits.  The compiler cannot tell the LDS written by buffer->LDS
-// loads from the LDS these reads use, so for its own LDS reads it would
-// wait for every buffer->LDS load in flight (draining the prefetch) and sink
-// each read to just before its first use.
+// This wave's one buffer->LDS load of the scales of group g of tile `tl`:
+// waves 0-3 fetch 4 activation tiles each, waves 4-7 4 weight strips each
+// (lane l: tile l/16, bytes (l%16)*16 of its 256).  Tiles past the last
+// strip fall outside the descriptor through the vector offset (zeros), and
+// an empty descriptor covers groups past K; the group goes in the scalar
+// offset.
+__device__ __forceinline__ void issue_scales(const GemmArgs& p, const Tile& tl, int g, int wv) {
+  const bool is_a = wv < 4;
+  const int first = is_a ? tl.ms : tl.s0;
+  const int count = is_a ? tl.mstrips : tl.strips;
+  const int rt0 = (wv & 3) * 4;
+  const int G = p.G;
+  const int left = __builtin_amdgcn_readfirstlane(max(0, count - rt0));
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc((is_a ? p.as : p.ws) + (int64_t)(first + rt0) * G * 256, g < G ? (uint32_t)(left * G * 256) : 0u);
+  const uint32_t lds = kScaleLds + ((is_a ? 0 : kTilesA) + rt0) * 256;
+  const uint32_t l = lane_here();
+  const uint32_t svoff = (l >> 4) * (uint32_t)(G * 256) + (l & 15) * 16;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(lds), 16, svoff, g << 8, 0, 0);
+}
+
+// This wave's buffer->LDS load of the bias of its 64 output columns of tile
+// `tl` (lanes 0-31 one bf16 pair each; N is a multiple of 4 here, so the
+// window ends on a whole pair; no bias: an empty window, zeros).
+__device__ __forceinline__ void issue_bias(const GemmArgs& p, const Tile& tl, int wv, int wn) {
+  const uint32_t lane = lane_here();
+  const int col0 = (tl.s0 + wn * kWN) * 16;
+  const int cols = __builtin_amdgcn_readfirstlane(p.bias ? max(0, min(64, p.N - col0)) : 0);
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(p.bias ? (const void*)(p.bias + col0) : (const void*)p.a, (uint32_t)(cols * 2));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(kBiasLds + wv * 256), 4, lane < 32 ? lane * 4 : kOOB, 0, 0,
+                                           0);
+}
+
+// LDS reads are written as inline assembly with hand-counted lgkmcnt
+// waits.  The compiler cannot tell the LDS written by buffer->LDS loads from
+// the LDS these reads use, so for its own LDS reads it would wait for every
+// buffer->LDS load in flight (draining the prefetch) and sink each read to
+// just before its first use.
 template <int OFF>
 __device__ __forceinline__ void ds_read16(v4i& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
+template <int OFF>
+__device__ __forceinline__ void ds_read4(uint32_t& v, uint32_t addr) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+typedef int v2i __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ void ds_read8(v2i& v, uint32_t addr) {
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_write8(uint32_t addr, v2i v) {
+  asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF));
+}
 
-// lgkmcnt(N) wait that the given fragments depend on, so no MFMA reading
+// lgkmcnt(N) waits that the given registers depend on, so no MFMA reading
 // them is scheduled above it.
 template <int N>
 __device__ __forceinline__ void wait_lgkm(v4i& a, v4i& b, v4i& c, v4i& d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "i"(N));
 }
+template <int N>
+__device__ __forceinline__ void wait_lgkm_scales(uint32_t (&sa)[kWM], uint32_t (&sb)[kWN]) {
+  asm volatile("s_waitcnt lgkmcnt(%12)"
+               : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sa[4]), "+v"(sa[5]), "+v"(sa[6]),
+                 "+v"(sa[7]), "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]), "+v"(sb[3])
+               : "i"(N));
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// vmcnt(N_SET) if `flag` (a uniform value) is non-zero, else vmcnt(N).  The
+// branch stays inside one assembly statement: as control flow the compiler
+// would see, it costs register copies around the whole K loop.
+template <int N, int N_SET>
+__device__ __forceinline__ void wait_vm_sel(int flag) {
+  if (N == N_SET) {
+    wait_vm<N>();
+  } else {
+    asm volatile(
+        "s_cmp_eq_u32 %0, 0\n\t"
+        "s_cbranch_scc1 1f\n\t"
+        "s_waitcnt vmcnt(%2)\n\t"
+        "s_branch 2f\n"
+        "1:\n\t"
+        "s_waitcnt vmcnt(%1)\n"
+        "2:" ::"s"(flag),
+        "i"(N), "i"(N_SET)
+        : "memory", "scc");
+  }
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (the fence
@@ -133,40 +243,49 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
-// LDS addresses of this lane's fragments: stage buffers 0-1 are reached
-// from the first base, 2-3 from the second (the read offset field is 16 bits).
-struct FragAddr {
-  uint32_t a01, a23, b01, b23;
+// LDS base addresses of this lane's fragment reads: activation fragments
+// (unit wm*8) and weight fragments (unit 16 + wn*4).
+struct ReadAddr {
+  uint32_t a, b;
 };
 
-template <int BUF, int I>
-__device__ __forceinline__ void read_a(v4i& v, const FragAddr& fa) {
-  ds_read16<(BUF & 1) * (int)sizeof(StageBuf) + I * 1024>(v, BUF < 2 ? fa.a01 : fa.a23);
-}
-template <int BUF, int J>
-__device__ __forceinline__ void read_b(v4i& v, const FragAddr& fa) {
-  ds_read16<(BUF & 1) * (int)sizeof(StageBuf) + J * 1024>(v, BUF < 2 ? fa.b01 : fa.b23);
-}
-
-// First half of the next step's fragments (weights 0-3, activations 0-3),
-// then the second half (activations 4-7): 8 + 4 LDS reads in this order.
+// First half of stage BUF's fragments (weights 0-3, activations 0-3), then
+// the second half (activations 4-7): 8 + 4 LDS reads in this order.
 template <int BUF>
-__device__ __forceinline__ void read_first_half(v4i (&af)[kWM], v4i (&bf)[kWN], const FragAddr& fa) {
-  read_b<BUF, 0>(bf[0], fa);
-  read_b<BUF, 1>(bf[1], fa);
-  read_b<BUF, 2>(bf[2], fa);
-  read_b<BUF, 3>(bf[3], fa);
-  read_a<BUF, 0>(af[0], fa);
-  read_a<BUF, 1>(af[1], fa);
-  read_a<BUF, 2>(af[2], fa);
-  read_a<BUF, 3>(af[3], fa);
+__device__ __forceinline__ void read_first_half(v4i (&af)[kWM], v4i (&bf)[kWN], const ReadAddr& ra) {
+  ds_read16<0 * 4096 + BUF * 1024>(bf[0], ra.b);
+  ds_read16<1 * 4096 + BUF * 1024>(bf[1], ra.b);
+  ds_read16<2 * 4096 + BUF * 1024>(bf[2], ra.b);
+  ds_read16<3 * 4096 + BUF * 1024>(bf[3], ra.b);
+  ds_read16<0 * 4096 + BUF * 1024>(af[0], ra.a);
+  ds_read16<1 * 4096 + BUF * 1024>(af[1], ra.a);
+  ds_read16<2 * 4096 + BUF * 1024>(af[2], ra.a);
+  ds_read16<3 * 4096 + BUF * 1024>(af[3], ra.a);
 }
 template <int BUF>
-__device__ __forceinline__ void read_second_half(v4i (&af)[kWM], const FragAddr& fa) {
-  read_a<BUF, 4>(af[4], fa);
-  read_a<BUF, 5>(af[5], fa);
-  read_a<BUF, 6>(af[6], fa);
-  read_a<BUF, 7>(af[7], fa);
+__device__ __forceinline__ void read_second_half(v4i (&af)[kWM], const ReadAddr& ra) {
+  ds_read16<4 * 4096 + BUF * 1024>(af[4], ra.a);
+  ds_read16<5 * 4096 + BUF * 1024>(af[5], ra.a);
+  ds_read16<6 * 4096 + BUF * 1024>(af[6], ra.a);
+  ds_read16<7 * 4096 + BUF * 1024>(af[7], ra.a);
+}
+// The 12 scale dwords of the group in LDS.
+__device__ __forceinline__ void read_scales(uint32_t (&sa)[kWM], uint32_t (&sb)[kWN], int wm, int wn) {
+  const uint32_t l4 = lane_here() * 4;
+  const uint32_t a = l4 + (uint32_t)(kScaleLds + wm * kWM * 256);
+  const uint32_t b = l4 + (uint32_t)(kScaleLds + (kTilesA + wn * kWN) * 256);
+  ds_read4<0 * 256>(sa[0], a);
+  ds_read4<1 * 256>(sa[1], a);
+  ds_read4<2 * 256>(sa[2], a);
+  ds_read4<3 * 256>(sa[3], a);
+  ds_read4<4 * 256>(sa[4], a);
+  ds_read4<5 * 256>(sa[5], a);
+  ds_read4<6 * 256>(sa[6], a);
+  ds_read4<7 * 256>(sa[7], a);
+  ds_read4<0 * 256>(sb[0], b);
+  ds_read4<1 * 256>(sb[1], b);
+  ds_read4<2 * 256>(sb[2], b);
+  ds_read4<3 * 256>(sb[3], b);
 }
 
 // MFMAs of activation rows I0..I0+3 of one K-step: acc[i][j] (+)= W-strip j
@@ -180,220 +299,354 @@ __device__ __forceinline__ void mfma_rows(v4f (&acc)[kWM][kWN], const v4i (&af)[
     for (int j = 0; j < kWN; ++j) acc[i][j] = mfma_fp4v<SEL>(bf[j], af[i], sb[j], sa[i], acc[i][j]);
 }
 
-// One K-step t = 4*g + J, its operands in stage buffer J:
-//  * rows 0-3 (their fragments, and the weight fragments, were read in the
-//    second half of the previous step: wait for all but the last 4 reads);
-//  * then the step's one barrier.  Before it this wave's reads of buffer J
-//    are done and its buffer->LDS loads of step t+1 have landed; after it
-//    buffer J is refilled with step t+4 (at J == 0 after the scale loads of
-//    group g+1), and the first half of step t+1's fragments is read from
-//    buffer J+1 (weights into the other weight set);
-//  * rows 4-7, then the second half of step t+1's fragments.
-// Loads in flight after the ones step t+1 needs: steps t+2 and t+3 plus,
-// for J = 1 and 2, the 12 scale loads issued at J = 0.
-template <int J>
-__device__ __forceinline__ void main_step(const Ctx& c, StageBuf& cur, v4f (&acc)[kWM][kWN], v4i (&af)[kWM],
-                                          v4i (&bf_cur)[kWN], v4i (&bf_nxt)[kWN], const uint32_t (&sa)[kWM],
-                                          const uint32_t (&sb)[kWN], uint32_t (&sa_nxt)[kWM],
-                                          uint32_t (&sb_nxt)[kWN], int g, int wv, const FragAddr& fa,
-                                          const uint32_t (&voff)[4], const uint32_t (&soff_a)[kWM],
-                                          const uint32_t (&soff_b)[kWN]) {
-  const int t = 4 * g + J;
+template <int SEL, int I>
+__device__ __forceinline__ void mfma_row(v4f (&acc)[kWM][kWN], const v4i (&af)[kWM], const v4i (&bf)[kWN],
+                                         const uint32_t (&sa)[kWM], const uint32_t (&sb)[kWN]) {
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) acc[I][j] = mfma_fp4v<SEL>(bf[j], af[I], sb[j], sa[I], acc[I][j]);
+}
+
+// Zero accumulators, each from its own opaque statement: from one shared
+// zero the compiler would keep a single zero register live through the loop
+// (or specialise the first K-step), both of which cost registers.
+__device__ __forceinline__ void zero_acc(v4f (&acc)[kWM][kWN]) {
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+#pragma unroll
+    for (int j = 0; j < kWN; ++j) {
+      float z0, z1, z2, z3;
+      asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
+                   : "=v"(z0), "=v"(z1), "=v"(z2), "=v"(z3));
+      acc[i][j] = (v4f){z0, z1, z2, z3};
+    }
+}
+
+// Per-wave state of the K loop.
+struct Pipe {
+  v4f acc[kWM][kWN];
+  v4i af[kWM], b0[kWN], b1[kWN];
+  uint32_t sa[kWM], sb[kWN];
+};
+
+// One K-step (step J of a group of 4), its operands in stage J:
+//  * rows 0-3 (their fragments, the weight fragments and at J == 0 the
+//    group's scales were read before the previous step's last 4 reads: wait
+//    for all but those);
+//  * then the step's one barrier.  Before it this wave's reads of stage J
+//    are done and its buffer->LDS loads of the next step have landed; after
+//    it the first half of the next step's fragments is read from stage J+1
+//    (weights into the other weight set), and stage J is refilled with step
+//    `td` of tile `dt` (four steps on in the stream of steps, possibly in
+//    the next tile; at J == 0 after the scales of group td/4 and the bias of
+//    the current tile `ct`), one unit after each of rows 4-7;
+//  * at J == 3 the next group's scales are read (they landed with the loads
+//    the barrier waited for); then the second half of the next step's
+//    fragments.
+// Loads in flight issued after the ones the next step needs: two steps of 4
+// loads plus, for J = 1 and 2, the scale and bias loads issued at J = 0,
+// plus, in a tile's first group (`first`), the kStores output stores of the
+// previous tile's epilogue (or the prologue's dropped stores).
+template <int J, int kStores, bool kBias>
+__device__ __forceinline__ void main_step(const GemmArgs& p, Pipe& P, v4i (&bf_cur)[kWN], v4i (&bf_nxt)[kWN],
+                                          const Tile& dt, const Tile& ct, int td, int first, int wv, int wm,
+                                          int wn, const ReadAddr& ra, uint32_t lane16) {
   constexpr int kNext = (J + 1) & 3;
-  wait_lgkm<4>(af[0], af[1], af[2], af[3]);
+  constexpr int kAfter = 2 * kLoadsPerWave + ((J == 1 || J == 2) ? 1 + (kBias ? 1 : 0) : 0);
+  wait_lgkm<4>(P.af[0], P.af[1], P.af[2], P.af[3]);
   wait_lgkm<4>(bf_cur[0], bf_cur[1], bf_cur[2], bf_cur[3]);
-  mfma_rows<J, 0>(acc, af, bf_cur, sa, sb);
+  if (J == 0) wait_lgkm_scales<4>(P.sa, P.sb);
+  mfma_rows<J, 0>(P.acc, P.af, bf_cur, P.sa, P.sb);
   __builtin_amdgcn_sched_barrier(0);
-  wait_lgkm<0>(af[4], af[5], af[6], af[7]);
-  if (J == 1 || J == 2)
-    wait_vm<2 * kLoadsPerWave + kScaleLoads>();
-  else
-    wait_vm<2 * kLoadsPerWave>();
+  wait_lgkm<0>(P.af[4], P.af[5], P.af[6], P.af[7]);
+  wait_vm_sel<kAfter, kAfter + (J < 3 ? kStores : 0)>(first);
   barrier_nofence();
-  if (J == 0) issue_scales(c, sa_nxt, sb_nxt, g + 1, soff_a, soff_b);
-  issue_step(c, cur, t + 4, wv, voff);
-  read_first_half<kNext>(af, bf_nxt, fa);
+  read_first_half<kNext>(P.af, bf_nxt, ra);
+  // Rows 4-7 with this wave's buffer->LDS loads spread between them: issued
+  // back to back by all waves right after the barrier, they would queue up
+  // in the address unit and stall instruction issue (and the MFMAs behind).
+  if (J == 0) issue_scales(p, dt, td >> 2, wv);
+  if (J == 0 && kBias) issue_bias(p, ct, wv, wn);
   __builtin_amdgcn_sched_barrier(0);
-  mfma_rows<J, 4>(acc, af, bf_cur, sa, sb);
+  mfma_row<J, 4>(P.acc, P.af, bf_cur, P.sa, P.sb);
+  issue_unit(p, dt, J, td, 0, wv, lane16);
   __builtin_amdgcn_sched_barrier(0);
-  read_second_half<kNext>(af, fa);
+  mfma_row<J, 5>(P.acc, P.af, bf_cur, P.sa, P.sb);
+  issue_unit(p, dt, J, td, 1, wv, lane16);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_row<J, 6>(P.acc, P.af, bf_cur, P.sa, P.sb);
+  issue_unit(p, dt, J, td, 2, wv, lane16);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_row<J, 7>(P.acc, P.af, bf_cur, P.sa, P.sb);
+  issue_unit(p, dt, J, td, 3, wv, lane16);
+  __builtin_amdgcn_sched_barrier(0);
+  if (J == 3) read_scales(P.sa, P.sb, wm, wn);
+  read_second_half<kNext>(P.af, ra);
+}
+
+// Output store modes:
+//  0  bf16, staged: each 16-row block goes through LDS and leaves as whole
+//     16-byte pieces of output rows (N and ldo multiples of 8, 16-byte
+//     aligned output): 16 stores per wave per tile;
+//  1  bf16, single elements: 128 stores;
+//  2  fp32, 4-column groups (16-byte stores; N and ldo multiples of 4,
+//     16-byte aligned output): 32 stores;
+//  3  fp32, single elements: 128 stores.
+// The stores of modes 0 and 2 stay in flight into the next tile and are
+// counted by its waits (vmcnt retires loads and stores in issue order); the
+// 128 of an element mode would exceed the counter's range (63), so that
+// epilogue waits for them instead.
+template <int MODE>
+struct OutMode {
+  static constexpr bool kF32 = MODE >= 2;
+  static constexpr bool kStaged = MODE == 0;
+  static constexpr bool kVec = MODE == 2;
+  static constexpr int kStores = kStaged ? 2 * kWM : kVec ? kWM * kWN : 4 * kWM * kWN;
+  static constexpr bool kDrain = !kStaged && !kVec;
+  static constexpr int kInFlight = kDrain ? 0 : kStores;  // stores the next tile's waits count
+  static constexpr bool kBiasLds = !kDrain;  // bias staged in LDS (whole pairs: N % 4 == 0)
+};
+
+// This lane's 4 bias columns of each 16-column strip j of the wave (columns
+// 16j + 4*(lane/16) ...), from the bias this wave staged in LDS.
+__device__ __forceinline__ void read_bias(v2i (&bl)[kWN], int wv, int lane) {
+  const uint32_t ba = kBiasLds + (uint32_t)(lane >> 4) * 8 + (uint32_t)wv * 256;
+  ds_read8<0>(bl[0], ba);
+  ds_read8<32>(bl[1], ba);
+  ds_read8<64>(bl[2], ba);
+  ds_read8<96>(bl[3], ba);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bl[0]), "+v"(bl[1]), "+v"(bl[2]), "+v"(bl[3]));
+}
+
+// Staged bf16 epilogue (mode 0).  Per 16-row block i: each lane writes its
+// 4 x 4 results (bias added in fp32, one rounding) to the wave's staging
+// rows, then reads back two 16-byte pieces of whole rows (8 lanes per
+// 128-byte row) and stores them.  The wave's own LDS operations run in
+// order, so no barrier is needed.
+__device__ __forceinline__ void epilogue_staged(const GemmArgs& p, const Tile& tl, v4f (&acc)[kWM][kWN], int wv,
+                                                int wm, int wn) {
+  const int lane = (int)lane_here();
+  const int row0 = tl.ms * 16 + wm * 128;
+  const int n = (tl.s0 + wn * kWN) * 16 + (lane & 7) * 8;  // this lane's 8 stored columns
+  v2i bl[kWN];
+  read_bias(bl, wv, lane);
+  const uint32_t wst = kEpiLds + (uint32_t)wv * 16 * kEpiRowB;
+  const uint32_t waddr = wst + (uint32_t)(lane & 15) * kEpiRowB + (uint32_t)(lane >> 4) * 8;
+  const uint32_t raddr = wst + (uint32_t)(lane >> 3) * kEpiRowB + (uint32_t)(lane & 7) * 16;
+  const uint32_t voff0 = n < p.N ? (uint32_t)((lane >> 3) * p.ldo + n) * 2 : kOOB;
+  const uint32_t voff1 = n < p.N ? voff0 + (uint32_t)(8 * p.ldo) * 2 : kOOB;
+  uint8_t* const out = reinterpret_cast<uint8_t*>(p.out);
+#pragma unroll
+  for (int i = 0; i < kWM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kWN; ++j) {
+      const float b0 = __uint_as_float((uint32_t)bl[j].x << 16), b1 = __uint_as_float((uint32_t)bl[j].x & 0xFFFF0000u);
+      const float b2 = __uint_as_float((uint32_t)bl[j].y << 16), b3 = __uint_as_float((uint32_t)bl[j].y & 0xFFFF0000u);
+      const uint32_t lo = f32_to_bf16_rne(acc[i][j][0] + b0) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1] + b1) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc[i][j][2] + b2) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3] + b3) << 16);
+      const v2i d = {(int)lo, (int)hi};
+      if (j == 0) ds_write8<0>(waddr, d);
+      if (j == 1) ds_write8<32>(waddr, d);
+      if (j == 2) ds_write8<64>(waddr, d);
+      if (j == 3) ds_write8<96>(waddr, d);
+    }
+    v4i r0, r1;
+    ds_read16<0>(r0, raddr);
+    ds_read16<8 * kEpiRowB>(r1, raddr);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1));
+    const int rb = row0 + i * 16;
+    // (uniform, but max/min would be computed in a vector register, which
+    // would turn every store into a waterfall loop over the descriptor)
+    const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, p.M - rb)));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (int64_t)rb * p.ldo * 2, (uint32_t)(nrows * p.ldo * 2));
+    __builtin_amdgcn_raw_buffer_store_b128(r0, ro, voff0, 0, MXFP4_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(r1, ro, voff1, 0, MXFP4_STORE_AUX);
+  }
+}
+
+// Tile epilogue of modes 1-3: bias (fp32), one rounding, stores of every
+// accumulator.  Rows are addressed through one buffer descriptor per 16-row block whose
+// size ends at the last valid row; columns past N get an out-of-range
+// offset.  Each store instruction is issued unconditionally, so the count of
+// memory operations the K loop's waits rely on is exact.
+template <int MODE>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& tl, v4f (&acc)[kWM][kWN], int wv, int wm,
+                                         int wn) {
+  using OM = OutMode<MODE>;
+  const int lane = (int)lane_here();
+  constexpr int esz = OM::kF32 ? 4 : 2;
+  const int row0 = tl.ms * 16 + wm * 128;  // wave's first output row
+  const int ncol0 = (tl.s0 + wn * kWN) * 16 + 4 * (lane >> 4);
+  const uint32_t lrow = (uint32_t)((lane & 15) * p.ldo) * esz;
+  uint8_t* const out = reinterpret_cast<uint8_t*>(p.out);
+  // Bias staged in LDS by this wave (mode 2): 4 columns per j.
+  v2i bl[kWN];
+  if (OM::kBiasLds) read_bias(bl, wv, lane);
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    const int n = ncol0 + j * 16;
+    float bias[4];
+    if (OM::kBiasLds) {
+      bias[0] = __uint_as_float((uint32_t)bl[j].x << 16);
+      bias[1] = __uint_as_float((uint32_t)bl[j].x & 0xFFFF0000u);
+      bias[2] = __uint_as_float((uint32_t)bl[j].y << 16);
+      bias[3] = __uint_as_float((uint32_t)bl[j].y & 0xFFFF0000u);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bias[r] = (p.bias && n + r < p.N) ? bf16_to_f32(p.bias[n + r]) : 0.f;
+    }
+    const uint32_t voff = lrow + (uint32_t)n * esz;
+#pragma unroll
+    for (int i = 0; i < kWM; ++i) {
+      const int rb = row0 + i * 16;
+      // (uniform, but max/min would be computed in a vector register, which
+      // would turn every store into a waterfall loop over the descriptor)
+      const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, p.M - rb)));
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (int64_t)rb * p.ldo * esz, (uint32_t)(nrows * p.ldo * esz));
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] + bias[r];
+      if (OM::kVec) {
+        const uint32_t off = n < p.N ? voff : kOOB;
+        if (OM::kF32) {
+          __builtin_amdgcn_raw_buffer_store_b128(
+              (v4i){(int)__float_as_uint(v[0]), (int)__float_as_uint(v[1]), (int)__float_as_uint(v[2]),
+                    (int)__float_as_uint(v[3])},
+              ro, off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t off = n + r < p.N ? voff + r * esz : kOOB;
+          if (OM::kF32)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), ro, off, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v[r]), ro, off, 0, 0);
+        }
+      }
+    }
+  }
+  if (OM::kDrain) wait_vm<0>();
+}
+
+// The four K-steps of group g of tile c, loading four steps on (from tile
+// cn when g is the tile's last group).
+template <int kStores, bool kBias>
+__device__ __forceinline__ void group_body(const GemmArgs& p, Pipe& P, const Tile& c, const Tile& cn, int g,
+                                           int wv, int wm, int wn, const ReadAddr& ra, uint32_t lane16) {
+  const bool last = g + 1 == p.G;
+  Tile dt;
+  dt.ms = last ? cn.ms : c.ms;
+  dt.mstrips = last ? cn.mstrips : c.mstrips;
+  dt.s0 = last ? cn.s0 : c.s0;
+  dt.strips = last ? cn.strips : c.strips;
+  const int t4 = last ? 0 : 4 * (g + 1);
+  // 1 in the tile's first group, from a scalar instruction the compiler
+  // cannot see through (it would peel the first group to fold the test,
+  // which costs register copies around the loop).
+  int first;
+  asm volatile("s_cmp_eq_u32 %1, 0\n\ts_cselect_b32 %0, 1, 0" : "=s"(first) : "s"(g) : "scc");
+  main_step<0, kStores, kBias>(p, P, P.b0, P.b1, dt, c, t4 + 0, first, wv, wm, wn, ra, lane16);
+  main_step<1, kStores, kBias>(p, P, P.b1, P.b0, dt, c, t4 + 1, first, wv, wm, wn, ra, lane16);
+  main_step<2, kStores, kBias>(p, P, P.b0, P.b1, dt, c, t4 + 2, first, wv, wm, wn, ra, lane16);
+  main_step<3, kStores, kBias>(p, P, P.b1, P.b0, dt, c, t4 + 3, first, wv, wm, wn, ra, lane16);
 }
 
 }  // namespace
 
+template <int MODE>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-  // The four stage buffers (128 KiB); the bf16 epilogue reuses the space
-  // (144 KiB) for its transpose.
+  constexpr int kStores = OutMode<MODE>::kInFlight;
+  constexpr bool kBiasLds = OutMode<MODE>::kBiasLds;
+  // The stage and scale addresses above are absolute LDS addresses: this is
+  // the kernel's only LDS allocation, so it starts at address 0.
   __shared__ int4 lds_raw[kLdsBytes / 16];
-  StageBuf* smem = reinterpret_cast<StageBuf*>(lds_raw);
   const int lane = threadIdx.x & 63;
   // The wave index is uniform across the wave; saying so keeps the buffer
   // resource and LDS address of every buffer->LDS load in scalar registers.
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wv >> 2, wn = wv & 3;
+  const int G = p.G;
 
-  // Tile order: consecutive ids run down a group of kGroupM row-tiles, then
-  // across columns; ids are dealt to the XCDs (round-robin by workgroup id)
-  // in contiguous runs.
+  // Tile list of this workgroup: tiles L = k * grid + slot, k = 0, 1, ...
+  // Workgroups are dealt to the 8 XCDs round-robin; with a grid that is a
+  // multiple of 8, slot numbers are remapped so each XCD's workgroups hold
+  // consecutive slots (and so consecutive tiles at every k).
   const int ntiles = tiles_m * tiles_n;
-  int id = blockIdx.x;
+  const int grid = gridDim.x;
+  const int slot = (grid & 7) == 0 ? (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int ntile_wg = (ntiles - slot + grid - 1) / grid;
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)&lds_raw[0];
+  const uint32_t lane16 = lane * 16;
+  ReadAddr ra;
+  ra.a = lds0 + wm * kWM * 4096 + lane16;
+  ra.b = lds0 + (kTilesA + wn * kWN) * 4096 + lane16;
+
+  Pipe P;
+  zero_acc(P.acc);
+
+  Tile c = tile_at(p, slot, tiles_m, tiles_n);
+  Tile cn = tile_at(p, slot + grid, tiles_m, tiles_n);
+
+  // Prologue: scales of group 0 and steps 0..3 of the first tile in flight;
+  // then as many dropped stores (out-of-range offset) as an epilogue leaves
+  // in flight, so every tile's first group counts the same operations.
+  // Once the scales and step 0 have landed everywhere, read them in the
+  // order the loop expects.
+  issue_scales(p, c, 0, wv);
+  issue_step(p, c, 0, 0, wv, lane16);
+  issue_step(p, c, 1, 1, wv, lane16);
+  issue_step(p, c, 2, 2, wv, lane16);
+  issue_step(p, c, 3, 3, wv, lane16);
   {
-    const int per_xcd = (ntiles + 7) / 8;
-    const int xcd = id % 8, k = id / 8;
-    const int full = ntiles - (per_xcd - 1) * 8;  // XCDs that get per_xcd ids
-    id = xcd < full ? xcd * per_xcd + k : full * per_xcd + (xcd - full) * (per_xcd - 1) + k;
+    // Inline assembly, so identical stores are not merged into one; the
+    // descriptor has no records (base 0, size 0), so every store is dropped
+    // without touching memory.
+    const v4i none = {0, 0, 0, 0x00020000};
+    const uint32_t zero = 0;
+#pragma unroll
+    for (int q = 0; q < kStores; ++q)
+      asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(zero), "v"(kOOB), "s"(none) : "memory");
   }
-  const int group = id / (kGroupM * tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (id % (kGroupM * tiles_n)) % gm;
-  const int tn = (id % (kGroupM * tiles_n)) / gm;
-
-  const int m0 = tm * kBM;
-  const int s0 = tn * kTilesB;
-  Ctx c;
-  c.Kt = p.Kt;
-  c.G = p.G;
-  const int strips = min(kTilesB, p.Ns - s0);
-  const int mstrips = min(kTilesA, ((p.M + 15) >> 4) - m0 / 16);
-  c.pa = p.a + (int64_t)(m0 / 16) * p.Kt * 1024;
-  c.na = (uint32_t)mstrips * p.Kt * 1024u;
-  c.pw = p.w + (int64_t)s0 * p.Kt * 1024;
-  c.nw = (uint32_t)strips * p.Kt * 1024u;
-  c.pas = p.as + (int64_t)(m0 / 16) * p.G * 256;
-  c.nas = (uint32_t)mstrips * p.G * 256u;
-  c.pws = p.ws + (int64_t)s0 * p.G * 256;
-  c.nws = (uint32_t)strips * p.G * 256u;
-
-  uint32_t voff[kLoadsPerWave];
-#pragma unroll
-  for (int q = 0; q < kLoadsPerWave; ++q)
-    voff[q] = (uint32_t)((((wv & 3) * kLoadsPerWave + q) * p.Kt) << 10) + lane * 16;
-  uint32_t soff_a[kWM], soff_b[kWN];
-#pragma unroll
-  for (int i = 0; i < kWM; ++i) soff_a[i] = (uint32_t)(((wm * kWM + i) * p.G) << 8) + lane * 4;
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) soff_b[j] = (uint32_t)(((wn * kWN + j) * p.G) << 8) + lane * 4;
-  FragAddr fa;
-  {
-    const uint32_t base = (uint32_t)(uintptr_t)(lds_ptr_t)&smem[0][0][0] + lane * 16;
-    fa.a01 = base + wm * kWM * 1024;
-    fa.b01 = base + (kTilesA + wn * kWN) * 1024;
-    fa.a23 = fa.a01 + 2 * (uint32_t)sizeof(StageBuf);
-    fa.b23 = fa.b01 + 2 * (uint32_t)sizeof(StageBuf);
-  }
-
-  // Zero accumulators the compiler cannot see through, so it does not peel
-  // the first K-group to specialise it (which costs accumulator copies).
-  float zero;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  v4f acc[kWM][kWN];
-#pragma unroll
-  for (int i = 0; i < kWM; ++i)
-#pragma unroll
-    for (int j = 0; j < kWN; ++j) acc[i][j] = (v4f){zero, zero, zero, zero};
-
-  uint32_t sa[kWM], sb[kWN], sa_n[kWM], sb_n[kWN];
-  v4i af[kWM], b0[kWN], b1[kWN];
-
-  // Prologue: scales of group 0 and steps 0..3 in flight; once step 0 has
-  // landed everywhere, read its fragments in the order the loop expects.
-  issue_scales(c, sa, sb, 0, soff_a, soff_b);
-  issue_step(c, smem[0], 0, wv, voff);
-  issue_step(c, smem[1], 1, wv, voff);
-  issue_step(c, smem[2], 2, wv, voff);
-  issue_step(c, smem[3], 3, wv, voff);
-  wait_vm<3 * kLoadsPerWave>();
+  wait_vm<3 * kLoadsPerWave + kStores>();
   barrier_nofence();
-  read_first_half<0>(af, b0, fa);
-  read_second_half<0>(af, fa);
+  read_scales(P.sa, P.sb, wm, wn);
+  read_first_half<0>(P.af, P.b0, ra);
+  read_second_half<0>(P.af, ra);
 
-  for (int g = 0; g < p.G; ++g) {
-    main_step<0>(c, smem[0], acc, af, b0, b1, sa, sb, sa_n, sb_n, g, wv, fa, voff, soff_a, soff_b);
-    main_step<1>(c, smem[1], acc, af, b1, b0, sa, sb, sa_n, sb_n, g, wv, fa, voff, soff_a, soff_b);
-    main_step<2>(c, smem[2], acc, af, b0, b1, sa, sb, sa_n, sb_n, g, wv, fa, voff, soff_a, soff_b);
-    main_step<3>(c, smem[3], acc, af, b1, b0, sa, sb, sa_n, sb_n, g, wv, fa, voff, soff_a, soff_b);
-#pragma unroll
-    for (int i = 0; i < kWM; ++i) sa[i] = sa_n[i];
-#pragma unroll
-    for (int j = 0; j < kWN; ++j) sb[j] = sb_n[j];
+  for (int k = 0;;) {
+    for (int g = 0; g < G; ++g) group_body<kStores, kBiasLds>(p, P, c, cn, g, wv, wm, wn, ra, lane16);
+    if (OutMode<MODE>::kStaged)
+      epilogue_staged(p, c, P.acc, wv, wm, wn);
+    else
+      epilogue<MODE>(p, c, P.acc, wv, wm, wn);
+    if (++k == ntile_wg) break;
+    zero_acc(P.acc);
+    c = cn;
+    cn = tile_at(p, slot + (k + 1) * grid, tiles_m, tiles_n);
   }
-  // Drain the reads and loads of steps past the end before the stage
-  // buffers are reused for the output.
-  wait_lgkm<0>(af[4], af[5], af[6], af[7]);
+  // The loads issued past the last tile (empty descriptors) still write
+  // zeros to LDS: let them and the LDS reads finish before the workgroup
+  // ends.
+  wait_lgkm<0>(P.af[4], P.af[5], P.af[6], P.af[7]);
   wait_vm<0>();
-  __syncthreads();
-
-  // Epilogue.  Lane l, register r of tile (i, j): output row
-  // m0 + wm*128 + 16i + l%16, column (s0 + wn*4 + j)*16 + 4*(l/16) + r.
-  const int ncol0 = (s0 + wn * kWN) * 16;
-  const int mrow0 = m0 + wm * 128;
-  if (p.out_f32) {
-#pragma unroll
-    for (int i = 0; i < kWM; ++i)
-#pragma unroll
-      for (int j = 0; j < kWN; ++j) {
-        const int m = mrow0 + i * 16 + (lane & 15);
-        const int n = ncol0 + j * 16 + 4 * (lane >> 4);
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < p.N)
-            reinterpret_cast<float*>(p.out)[(int64_t)m * p.ldo + n + r] =
-                acc[i][j][r] + (p.bias ? bf16_to_f32(p.bias[n + r]) : 0.f);
-      }
-    return;
-  }
-  // bf16: stage this wave's 128 x 64 tile in LDS (row stride 144 bytes to
-  // spread banks), then write 16-byte chunks of whole rows.
-  uint8_t* stage = reinterpret_cast<uint8_t*>(lds_raw) + wv * 128 * kRowB;
-  float bias4[kWN][4];
-#pragma unroll
-  for (int j = 0; j < kWN; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = ncol0 + j * 16 + 4 * (lane >> 4) + r;
-      bias4[j][r] = (p.bias && n < p.N) ? bf16_to_f32(p.bias[n]) : 0.f;
-    }
-#pragma unroll
-  for (int i = 0; i < kWM; ++i)
-#pragma unroll
-    for (int j = 0; j < kWN; ++j) {
-      const uint32_t lo = f32_to_bf16_rne(acc[i][j][0] + bias4[j][0]) |
-                          ((uint32_t)f32_to_bf16_rne(acc[i][j][1] + bias4[j][1]) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc[i][j][2] + bias4[j][2]) |
-                          ((uint32_t)f32_to_bf16_rne(acc[i][j][3] + bias4[j][3]) << 16);
-      const int row = i * 16 + (lane & 15);
-      const int col = j * 16 + 4 * (lane >> 4);
-      *reinterpret_cast<uint2*>(stage + row * kRowB + col * 2) = make_uint2(lo, hi);
-    }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-  __builtin_amdgcn_wave_barrier();
-  // 8 lanes cover a 128-byte row; 8 rows per pass, 16 passes.
-#pragma unroll 4
-  for (int pass = 0; pass < 16; ++pass) {
-    const int row = pass * 8 + (lane >> 3);
-    const int col = (lane & 7) * 8;
-    const int m = mrow0 + row;
-    const int n = ncol0 + col;
-    if (m >= p.M) continue;
-    const int4 v = *reinterpret_cast<const int4*>(stage + row * kRowB + col * 2);
-    uint16_t* dst = reinterpret_cast<uint16_t*>(p.out) + (int64_t)m * p.ldo + n;
-    if (n + 8 <= p.N && (((uintptr_t)dst & 15) == 0)) {
-      *reinterpret_cast<int4*>(dst) = v;
-    } else {
-      const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n + e < p.N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-  }
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = (p.Ns * 16 + kBN - 1) / kBN;
-  gemm_prefill_kernel<<<dim3((unsigned)(tiles_m * tiles_n)), 64 * kWaves, 0, stream>>>(p, tiles_m, tiles_n);
+  const int ntiles = tiles_m * tiles_n;
+  const int grid = ntiles < p.cus ? ntiles : p.cus;
+  const bool a16 = ((uintptr_t)p.out & 15) == 0;
+  const int mode = p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
+                             : ((p.N % 8 == 0 && p.ldo % 8 == 0 && a16) ? 0 : 1);
+  const dim3 g((unsigned)grid), b(64 * kWaves);
+  switch (mode) {
+    case 0: gemm_prefill_kernel<0><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
+    case 1: gemm_prefill_kernel<1><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
+    case 2: gemm_prefill_kernel<2><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
+    default: gemm_prefill_kernel<3><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
+  }
   return hipGetLastError();
 }
 

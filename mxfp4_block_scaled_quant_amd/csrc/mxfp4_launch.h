@@ -19,6 +19,7 @@ struct GemmArgs {
   int64_t ldo;
   int out_f32;
   int M, N, K, Kt, G, Ns;  // Kt = ceil(K/128), G = ceil(Kt/4), Ns = ceil(N/16)
+  int cus;                 // compute units of the device (persistent grids)
 };
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);

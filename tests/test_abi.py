@@ -112,6 +112,8 @@ def test_gemm_validation(lib):
     assert call(N=0) == 2
     assert call(M=-1) == 2
     assert call(ldo=8) == 2         # ldo < N
+    assert call(ldo=1 << 22) == 2   # 256 bf16 rows past 32-bit offsets
+    assert call(ldo=1 << 21, dt=1) == 2
     assert call(w=None) == 1
     assert call(a=P_ODD) == 3
     assert call(M=0, a=None) == 0   # nothing to do
