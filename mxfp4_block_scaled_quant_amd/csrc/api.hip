@@ -201,10 +201,11 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, cons
   if (!aligned(x, 16) || sxb % 8 || sxm % 8 || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
       !aligned(out, 4) || sob % 2 || som % 2)
     return MXFP4_ERR_ALIGN;
-  int st = check_device();
+  int cus = 0;
+  int st = check_device(&cus);
   if (st) return st;
   return launched(launch_bmm_a16w4(x, sxb, sxm, w_pre, ws_pre, out, sob, som,
-                                   out_dtype == MXFP4_OUT_F32, B, M, N, K, (hipStream_t)stream));
+                                   out_dtype == MXFP4_OUT_F32, B, M, N, K, (hipStream_t)stream, cus));
 }
 
 // Test hook: force the decode (1) or prefill (2) GEMM kernel, 0 = by M.

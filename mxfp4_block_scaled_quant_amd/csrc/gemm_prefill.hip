@@ -441,8 +441,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& p, const Tile& t
     for (int j = 0; j < kWN; ++j) {
       const float b0 = __uint_as_float((uint32_t)bl[j].x << 16), b1 = __uint_as_float((uint32_t)bl[j].x & 0xFFFF0000u);
       const float b2 = __uint_as_float((uint32_t)bl[j].y << 16), b3 = __uint_as_float((uint32_t)bl[j].y & 0xFFFF0000u);
-      const uint32_t lo = f32_to_bf16_rne(acc[i][j][0] + b0) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1] + b1) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc[i][j][2] + b2) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3] + b3) << 16);
+      const uint32_t lo = pack_bf16x2(acc[i][j][0] + b0, acc[i][j][1] + b1);
+      const uint32_t hi = pack_bf16x2(acc[i][j][2] + b2, acc[i][j][3] + b3);
       const v2i d = {(int)lo, (int)hi};
       if (j == 0) ds_write8<0>(waddr, d);
       if (j == 1) ds_write8<32>(waddr, d);

@@ -49,12 +49,17 @@ __device__ __forceinline__ v4f mfma_fp4(const int4& a, const int4& b, uint32_t s
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, SEL_A, (int)sa, SEL_B, (int)sb);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16 bits, round to nearest even, by gfx950's conversion
+// instruction: identical to integer RNE rounding (add 0x7FFF plus the kept
+// LSB, truncate) for every non-NaN fp32 pattern, and NaN stays NaN (checked
+// exhaustively over all 2^32 inputs on MI355X).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two fp32 values -> packed bf16 pair (lo in bits 0-15), one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  const v2bf h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }

@@ -33,7 +33,7 @@ hipError_t launch_preshuffle(const void* w_fp4, const void* w_scales, int64_t ba
 
 hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void* w,
                             const void* ws, void* out, int64_t sob, int64_t som, int out_f32,
-                            int64_t B, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            int64_t B, int64_t M, int64_t N, int64_t K, hipStream_t stream, int cus);
 
 // Kernel-selection overrides used only by the tests and the benchmark to
 // exercise each GEMM path on every shape: 0 = automatic by M, 1 = decode
