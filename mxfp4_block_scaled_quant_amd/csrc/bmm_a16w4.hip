@@ -6,7 +6,7 @@
 //   out[b, m, n] = round(sum_k x[b, m, k] * dq(W)[b, n, k])
 // with the activations used exactly (no activation quantisation), the
 // weights dequantised exactly to bf16 in registers (an E2M1 value times a
-// power of two always fits bf16), the bf16 16x16x32 MFMA with fp32
+// power of two fits bf16 for every scale byte quantisation produces), the bf16 16x16x32 MFMA with fp32
 // accumulation, and one RNE rounding to bf16 (or fp32 out).  The weight
 // dequantisation uses gfx950's scaled FP4 -> bf16 conversion instruction.  Output
 // strides (sob, som) cover both [B, M, N] and batch-major [M, B, N].
@@ -49,9 +49,11 @@ struct BmmArgs {
 
 // Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) times
 // 2^(sc-127) as bf16 pairs: gfx950's scaled FP4 -> bf16 conversion, one
-// instruction per byte.  Exact: an E2M1 value times a power of two always
-// fits bf16; measured bit-identical to the exact product for every byte and
-// every scale byte 0..254 (sc = 0 passes the fp32 subnormal 2^-127).
+// instruction per byte.  Exact whenever the product fits bf16, which holds
+// for every scale byte up to 252 (all that quantising bf16 data produces;
+// bytes 253-254 with the largest codes overflow to +-inf); measured
+// bit-identical to the exact product for every byte and every scale byte
+// 0..254 (sc = 0 passes the fp32 subnormal 2^-127).
 __device__ __forceinline__ v8bf dequant8(uint32_t word, uint32_t sc) {
   const float scale = __uint_as_float(sc == 0 ? 0x00400000u : (sc << 23));
   typedef __bf16 v2bf __attribute__((ext_vector_type(2)));

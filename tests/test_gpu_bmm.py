@@ -88,3 +88,33 @@ def test_bmm_exact_mxfp4_activations_match_gemm():
         ref, S = G.gemm_a4w4_from_quant(qx[b], sx[b], *Q.quant_1x32(prob["w"][b]))
         check_f32_tolerance(g, ref, S)
         check_f32_tolerance(y32[b], ref, S)
+
+
+def test_bmm_dequant_exact_every_scale():
+    # Weight dequantisation, pinned element by element: one head (K-up shape,
+    # the streaming kernel) whose blocks carry every scale byte 0..252 (every
+    # scale quantisation of bf16 data can produce: amax < 2^128) and every
+    # E2M1 code, times identity activations, so out[m, n] is the single
+    # nonzero product 1 * dq(W)[n, m]: exact in fp32 and in bf16 (each such
+    # dequantised value is a bf16 number).  Zeros compare without their sign
+    # (the sum over the other, zero, products decides it).
+    need_gpu()
+    B, N, K = 1, 512, 192
+    nb = K // 32
+    n_idx = np.arange(N)[:, None]
+    scales = ((n_idx * nb + np.arange(nb)[None, :]) % 253).astype(np.uint8)          # [N, K/32]
+    codes = ((np.arange(K)[None, :] + n_idx) % 16).astype(np.uint8)                 # [N, K]
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)              # [N, K/2]
+    w_pre, ws_pre = mx.mxfp4_preshuffle_weight(torch.from_numpy(packed).cuda(),
+                                               torch.from_numpy(scales).cuda(), N, K, batch=B)
+    eye = np.zeros((B, K, K), dtype=np.uint16)
+    eye[0, np.arange(K), np.arange(K)] = 0x3F80                                        # bf16 1.0
+    x = dev_bf16(eye)
+    y32 = mx.a16wfp4_bmm(x, w_pre, ws_pre, N, out_dtype=torch.float32)
+    y16 = mx.a16wfp4_bmm(x, w_pre, ws_pre, N)
+    torch.cuda.synchronize()
+    dq = Q.dequant(packed, scales)                                                  # fp64 [N, K]
+    assert np.array_equal(y32.cpu().numpy()[0], dq.T.astype(np.float32))          # -0.0 == 0.0
+    from oracle import formats as F
+    unsigned_zero = lambda b: np.where((b & 0x7FFF) == 0, 0, b)
+    assert np.array_equal(unsigned_zero(host_bf16_bits(y16)[0]), unsigned_zero(F.f64_to_bf16(dq.T)))

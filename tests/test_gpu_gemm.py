@@ -145,3 +145,38 @@ def test_prefill_sweep_full_size(N, K):
         y32, y16 = _run(prob, 0, weight=W)
         rows = _sample(M, 64, M)
         _check(prob, y32, y16, rows=rows, cols=cols)
+
+
+@pytest.mark.parametrize("path,K", [(1, 64), (2, 192)], ids=["smallM", "tiled"])
+def test_gemm_weight_scales_exact(path, K):
+    # Every weight scale byte 0..254 with every E2M1 code, times identity
+    # activations (each row one 1.0: quantised exactly, code 6 at scale 125),
+    # so out[m, n] is the single nonzero product dq(W)[n, m]: exact in fp32
+    # (values past the fp32 range are infinite on both sides) and in bf16.
+    # Zeros compare without their sign (the sum of the other, zero, products
+    # decides it).
+    need_gpu()
+    N = 512
+    nb = K // 32
+    n_idx = np.arange(N)[:, None]
+    scales = ((n_idx * nb + np.arange(nb)[None, :]) % 255).astype(np.uint8)
+    codes = ((np.arange(K)[None, :] + n_idx) % 16).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    w_pre, ws_pre = mx.mxfp4_preshuffle_weight(torch.from_numpy(packed).cuda(),
+                                               torch.from_numpy(scales).cuda(), N, K)
+    eye = np.zeros((K, K), dtype=np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80
+    mx.set_gemm_path(path)
+    try:
+        q, s = mx.mxfp4_quant_1x32(dev_bf16(eye), mx.MXFP4_LAYOUT_GEMM)
+        y32 = mx.mxfp4_gemm_a4w4(q, s, w_pre, ws_pre, K, N, K, None, torch.float32)
+        y16 = mx.mxfp4_gemm_a4w4(q, s, w_pre, ws_pre, K, N, K, None, torch.bfloat16)
+    finally:
+        mx.set_gemm_path(0)
+    torch.cuda.synchronize()
+    from oracle import quant as Q
+    dq = Q.dequant(packed, scales)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(y32.cpu().numpy(), dq.T.astype(np.float32))      # -0.0 == 0.0, inf == inf
+    unsigned_zero = lambda b: np.where((b & 0x7FFF) == 0, 0, b)
+    assert np.array_equal(unsigned_zero(host_bf16_bits(y16)), unsigned_zero(F.f64_to_bf16(dq.T)))
