@@ -6,18 +6,22 @@
 
 Headline (the metric's M <= 16 decode regime): one step is one pass over the
 decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
-(5120, 14336), (34816, 5120)} -- for each shape, per-1x32 quantisation of the
-bf16 activations (GEMM scale layout, 0x7F padding) and the block-scaled FP4
-GEMM with a bf16 bias and bf16 output, against weights quantised and
-preshuffled once at load time.  value = sum of the pipeline's algorithmic
+(5120, 14336), (34816, 5120)} -- for each shape, mxfp4_linear: per-1x32
+quantisation of the bf16 activations and the block-scaled FP4 GEMM with a
+bf16 bias and bf16 output (M <= 4: one launch, the quantisation fused into
+the GEMM kernel; M = 16: quantisation into a workspace, then the GEMM),
+against weights quantised and preshuffled once at load time.  value = sum of the pipeline's algorithmic
 bytes over the step / step time (GB/s).  Inputs are resident in HBM before the
 timed region.  Each launch reads a different copy of its weights (>= 1 GiB of
 copies per shape) so the 256 MB Infinity Cache and the L2s cannot serve them.
 Steps are replayed from HIP graphs (one graph per step position in the copy
 rotation), bracketed by HIP events on the capture/replay stream.
 
-Also reported (same JSON line): the dominant kernel's roofline (decode GEMM,
-timed in its own graph-replayed loop), the full decode sweep (M up to 64), the
+Also reported (same JSON line): the dominant kernel's roofline (the decode
+GEMM on pre-quantised activations at the headline shapes, timed in its own
+graph-replayed loop),
+the full decode sweep (M up to 64: the whole call, and the GEMM alone with
+quant apart), the
 prefill sweep (M in {512, 2048, 8192}: TFLOP/s and fraction of the 10.1
 PFLOP/s dense FP4 peak), the A16WFP4 BMM sweep (MLA K-up / V-up on 16 heads),
 and the CPU oracle timed on a bounded sample of the headline workload.
@@ -157,15 +161,14 @@ def main():
         b = dev_bf16(inputs.bias(N, 2))
         for M in HEADLINE_M:
             x = dev_bf16(inputs.activations(M, K, 2))
-            q = torch.empty(mx.data_bytes(M, K, mx.MXFP4_LAYOUT_GEMM), dtype=torch.uint8, device=dev)
-            s = torch.empty(mx.scale_bytes(M, K, mx.MXFP4_LAYOUT_GEMM), dtype=torch.uint8, device=dev)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            cases.append(dict(M=M, N=N, K=K, x=x, q=q, s=s, out=out, bias=b))
+            need = mx.linear_workspace_bytes(M, N, K)
+            work = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+            cases.append(dict(M=M, N=N, K=K, x=x, out=out, bias=b, work=work))
 
     def launch_case(c, copy):
-        mx.mxfp4_quant_1x32(c["x"], mx.MXFP4_LAYOUT_GEMM, q=c["q"], scales=c["s"])
-        mx.mxfp4_gemm_a4w4(c["q"], c["s"], copy.w_pre, copy.ws_pre, c["M"], c["N"], c["K"],
-                           c["bias"], torch.bfloat16, out=c["out"])
+        mx.mxfp4_linear(c["x"], copy.w_pre, copy.ws_pre, c["N"], c["bias"], torch.bfloat16,
+                        out=c["out"], workspace=c["work"])
 
     # One graph per step position of the rotation cycle: launch i of shape (N,K)
     # uses copy (i mod R); the cycle repeats after lcm over shapes of R/3 steps.
@@ -223,6 +226,15 @@ def main():
             mx.mxfp4_gemm_a4w4(x_q, x_s, cp.w_pre, cp.ws_pre, M, N, K, bias, torch.bfloat16, out=out)
         return per_launch_time(launch, len(copies), reps_target)
 
+    def linear_time(M, N, K, x, bias, out, copies, reps_target=400):
+        need = mx.linear_workspace_bytes(M, N, K)
+        work = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+
+        def launch(i):
+            cp = copies[i]
+            mx.mxfp4_linear(x, cp.w_pre, cp.ws_pre, N, bias, torch.bfloat16, out=out, workspace=work)
+        return per_launch_time(launch, len(copies), reps_target)
+
     def quant_time(x, q, s, reps_target=400):
         return per_launch_time(lambda i: mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM, q=q, scales=s),
                                1, reps_target)
@@ -237,11 +249,17 @@ def main():
             t = gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
             gb = gemm_bytes(M, N, K, True)
             tq = quant_time(x, q, s)
-            decode_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 3),
+            tl = linear_time(M, N, K, x, b, out, weights[(N, K)])
+            pb = pipeline_bytes(M, N, K, True)
+            decode_rows.append(dict(M=M, N=N, K=K,
+                                    linear_us=round(tl * 1e6, 3),
+                                    linear_GBps=round(pb / tl / 1e9, 1),
+                                    linear_hbm_frac=round(pb / tl / PEAK_HBM, 4),
+                                    gemm_us=round(t * 1e6, 3),
                                     gemm_GBps=round(gb / t / 1e9, 1),
                                     hbm_frac=round(gb / t / PEAK_HBM, 4),
                                     quant_us=round(tq * 1e6, 3),
-                                    tflops=round(2 * M * N * K / t / 1e12, 2)))
+                                    tflops=round(2 * M * N * K / tl / 1e12, 2)))
     head_rows = [r for r in decode_rows if r["M"] in HEADLINE_M]
     dom_bytes = sum(gemm_bytes(r["M"], r["N"], r["K"], True) for r in head_rows)
     dom_time = sum(r["gemm_us"] for r in head_rows) * 1e-6
@@ -323,7 +341,8 @@ def main():
             "workload": "decode-sweep W4A4 MXFP4 linear at M<=16: per-1x32 quant of bf16 "
                         "activations + block-scaled FP4 GEMM + bf16 bias, bf16 out",
             "M": HEADLINE_M, "NK": DECODE_NK,
-            "step": "9 shapes x (quant + GEMM), weights preshuffled at load, rotated copies",
+            "step": "9 shapes x mxfp4_linear (M<=4: quant fused into the GEMM; M=16: "
+                    "quant then GEMM), weights preshuffled at load, rotated copies",
             "hbm_frac": round(value_gbs * 1e9 / PEAK_HBM, 4),
         },
         "roofline": {

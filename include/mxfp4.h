@@ -156,6 +156,31 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The whole W4A4 linear from bf16 activations (P2 §2, apply_weights: the
+ * activations are quantised per 1x32 and fed with the preshuffled weight to
+ * the FP4 GEMM, bias added after).  Same result as mxfp4_quant_1x32 (GEMM
+ * layout) followed by mxfp4_gemm_a4w4:
+ *   out[m, n] = round(sum_k dq(Q(x))[m,k] dq(W)[n,k] + bias[n]).
+ * Where it is faster (M = 1; M <= 4 for N < 16384 and K <= 8192) the
+ * quantisation runs inside the GEMM kernel: one launch, no quantised copy of
+ * x, bitwise the same output as the two-call form.  Otherwise x is quantised
+ * into `workspace` and the GEMM kernel for that M then reads it.
+ *
+ *   x       bf16 [M, K], row stride ldx ELEMENTS (ldx >= K, ldx % 8 == 0,
+ *           16-byte aligned); for M <= 4, ((M-1)*ldx + K)*2 < 2^31
+ *   w_pre, ws_pre, bias, out, ldo, out_dtype: as for mxfp4_gemm_a4w4
+ *   workspace  mxfp4_linear_workspace_bytes(M, N, K) bytes (0 when the
+ *           quantisation is fused: then it may be NULL), 16-byte aligned;
+ *           overwritten, caller-owned
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
+ */
+size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre,
+                 const void* bias, void* out, int64_t ldo, int out_dtype,
+                 int64_t M, int64_t N, int64_t K,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * A16WFP4 batched GEMM (P3 §Motivation and §Modifications: the MLA absorbed
  * K/V projection weights stay in packed MXFP4, the batched products take
  * bf16 activations, and the V-up result is written batch-major).  For each

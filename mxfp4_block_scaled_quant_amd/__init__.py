@@ -11,10 +11,12 @@ Entry points (same names as the C ABI):
 * :func:`mxfp4_quant_1x32` -- bf16 [M, K] -> packed FP4 [M, K/2] + E8M0 scales
 * :func:`mxfp4_preshuffle_weight` -- quantised weights -> preshuffled layout
 * :func:`mxfp4_gemm_a4w4` -- W4A4 GEMM with optional bias, bf16/fp32 out
+* :func:`mxfp4_linear` -- bf16 activations -> quant + GEMM (+ bias) in one call,
+  the quantisation fused into the GEMM kernel for M <= 16
 * :func:`a16wfp4_bmm` -- bf16 [B, M, K] x MXFP4 [B, N, K] batched GEMM
 
 Convenience: :func:`quantize_weight` (quant + preshuffle, once at load) and
-:func:`linear` (quant of the activations + GEMM).
+:func:`linear` (:func:`mxfp4_linear` over any leading dimensions).
 """
 
 from __future__ import annotations
@@ -51,6 +53,9 @@ _SIGNATURES = {
     "mxfp4_preshuffle_weight": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "mxfp4_gemm_a4w4": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
                                  _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
+    "mxfp4_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_linear": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
+                              _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
     "a16wfp4_bmm": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int,
                              _c_i64, _c_i64, _c_i64, _c_i64, _c_vp]),
     "mxfp4_debug_set_gemm_path": (_c_int, [_c_int]),
@@ -183,6 +188,37 @@ def mxfp4_gemm_a4w4(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre: torch.Te
     return out
 
 
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mxfp4_linear_workspace_bytes(M, N, K))
+
+
+def mxfp4_linear(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: int,
+                 bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """out[M, N] = round(dq(Q(x)) dq(W)^T (+ bias)) from bf16 x [M, K] (unit stride along K).
+
+    ``workspace`` (uint8, >= :func:`linear_workspace_bytes` bytes) is
+    allocated here when needed and not given; M <= 16 needs none.
+    """
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit stride along K")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
+        raise ValueError("bias must be bf16 [N]")
+    M, K = x.shape
+    code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    need = linear_workspace_bytes(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check("mxfp4_linear", lib().mxfp4_linear(
+        _ptr(x), x.stride(0), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0),
+        code, M, N, K, _ptr(workspace), ws_bytes, _stream(x.device)))
+    return out
+
+
 def a16wfp4_bmm(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: int,
                 out: Optional[torch.Tensor] = None, batch_major: bool = False,
                 out_dtype: torch.dtype = torch.bfloat16):
@@ -244,10 +280,10 @@ def quantize_weight(w: torch.Tensor) -> MXFP4Weight:
 
 def linear(x: torch.Tensor, weight: MXFP4Weight, bias: Optional[torch.Tensor] = None,
            out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
-    """W4A4 linear: quantise bf16 activations [..., K] per 1x32, then the FP4 GEMM."""
+    """W4A4 linear: bf16 activations [..., K] quantised per 1x32, then the FP4 GEMM."""
     lead = x.shape[:-1]
     x2 = x.reshape(-1, x.shape[-1])
-    q, s = mxfp4_quant_1x32(x2, MXFP4_LAYOUT_GEMM)
-    y = mxfp4_gemm_a4w4(q, s, weight.w_pre, weight.ws_pre, x2.shape[0], weight.N, weight.K,
-                        bias, out_dtype)
+    if x2.stride(1) != 1:
+        x2 = x2.contiguous()
+    y = mxfp4_linear(x2, weight.w_pre, weight.ws_pre, weight.N, bias, out_dtype)
     return y.reshape(*lead, weight.N)

@@ -21,6 +21,7 @@ namespace {
 
 constexpr int64_t kMaxBuf = 0x7FFFFFFFll;  // buffer-resource offsets stay below 2^31
 constexpr int64_t kMaxK = 1 << 20;         // keeps per-tile 32-bit offsets far from wrapping
+constexpr int64_t kFusedMaxM = 4;          // mxfp4_linear quantises inside the GEMM up to 4 rows
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -56,6 +57,11 @@ int check_device(int* cus = nullptr) {
 
 int launched(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_LAUNCH; }
 
+// Whether mxfp4_linear quantises inside the GEMM kernel for this shape.
+bool linear_fused(int64_t M, int64_t N, int64_t K) {
+  return M <= kFusedMaxM && N <= kMaxBuf && K <= kMaxK && linear_fused_pays((int)M, (int)N, (int)K);
+}
+
 }  // namespace
 }  // namespace mxfp4
 
@@ -77,7 +83,7 @@ const char* mxfp4_status_str(int status) {
   }
 }
 
-int mxfp4_abi_version(void) { return 100; }
+int mxfp4_abi_version(void) { return 101; }
 
 size_t mxfp4_data_bytes(int64_t rows, int64_t K, int layout) {
   if (rows < 0 || K <= 0 || K % 32) return 0;
@@ -178,11 +184,81 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   p.Kt = (int)cdiv(K, 128);
   p.G = (int)cdiv(p.Kt, 4);
   p.Ns = (int)cdiv(N, 16);
+  p.x = nullptr;
+  p.ldx = 0;
+  p.x_bytes = 0;
   int path = get_gemm_path_override();
   if (path == 0) path = M <= 64 ? 1 : 2;
   if (path == 1 && M > 64) path = 2;  // the decode kernel covers at most 64 rows
   hipStream_t s = (hipStream_t)stream;
   return launched(path == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+}
+
+size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
+  if (M == 0 || linear_fused(M, N, K)) return 0;
+  return (size_t)(cdiv(gemm_data_bytes(M, K), 256) * 256 + gemm_scale_bytes(M, K)) +
+         mxfp4_gemm_workspace_bytes(M, N, K);
+}
+
+int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre,
+                 const void* bias, void* out, int64_t ldo, int out_dtype, int64_t M, int64_t N,
+                 int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
+  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (ldo < N || ldx < K) return MXFP4_ERR_SHAPE;
+  if (ldo > kMaxBuf / 256 / (out_dtype == MXFP4_OUT_F32 ? 4 : 2)) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
+      gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  const bool fused = M > 0 && linear_fused(M, N, K);
+  // the fused kernel addresses x through one 32-bit buffer range
+  if (fused && M > 0 && ((M - 1) * ldx + K) * 2 > kMaxBuf) return MXFP4_ERR_SHAPE;
+  const size_t need = mxfp4_linear_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return MXFP4_ERR_WORKSPACE;
+  if (M == 0) return MXFP4_OK;
+  if (!x || !w_pre || !ws_pre || !out || (need && !workspace)) return MXFP4_ERR_NULL;
+  if (!aligned(x, 16) || ldx % 8 || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
+      !aligned(out, 4) || (bias && !aligned(bias, 2)) || (need && !aligned(workspace, 16)))
+    return MXFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = check_device(&cus);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs p;
+  p.cus = cus;
+  p.w = (const uint8_t*)w_pre;
+  p.ws = (const uint8_t*)ws_pre;
+  p.bias = (const uint16_t*)bias;
+  p.out = out;
+  p.ldo = ldo;
+  p.out_f32 = out_dtype == MXFP4_OUT_F32;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.Kt = (int)cdiv(K, 128);
+  p.G = (int)cdiv(p.Kt, 4);
+  p.Ns = (int)cdiv(N, 16);
+  if (fused) {
+    p.a = nullptr;
+    p.as = nullptr;
+    p.x = (const uint16_t*)x;
+    p.ldx = (int)ldx;
+    p.x_bytes = (uint32_t)(((M - 1) * ldx + K) * 2);
+    return launched(launch_linear_decode(p, s));
+  }
+  // Larger M: quantise into the workspace, then the GEMM kernel for that M.
+  uint8_t* q = (uint8_t*)workspace;
+  uint8_t* sc = q + cdiv(gemm_data_bytes(M, K), 256) * 256;
+  st = launched(launch_quant_1x32(x, M, K, ldx, q, 0, sc, MXFP4_LAYOUT_GEMM, s));
+  if (st) return st;
+  p.a = q;
+  p.as = sc;
+  p.x = nullptr;
+  p.ldx = 0;
+  p.x_bytes = 0;
+  return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
 }
 
 int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, const void* ws_pre,

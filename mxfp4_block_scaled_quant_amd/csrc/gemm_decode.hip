@@ -37,13 +37,48 @@ __device__ __forceinline__ v4f mfma_sel(const int4& a, const int4& b, uint32_t s
 
 }  // namespace
 
+// Sums the KW waves' partial tiles through LDS in a fixed order (results
+// identical run to run), adds the bias in fp32 and stores the tile rows
+// below M: bf16 rounded once to nearest even, or fp32.
+template <int MT, int NS>
+__device__ __forceinline__ void reduce_store(v4f* red, const v4f (&acc)[MT][NS], const GemmArgs& p, int s0) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int KW = blockDim.x >> 6;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) red[(wv * MT * NS + i * NS + j) * 64 + lane] = acc[i][j];
+  __syncthreads();
+
+  // Thread -> (tile, register, lane) with the lane fastest so 16 consecutive
+  // threads write 16 consecutive columns.
+  constexpr int TOTAL = MT * NS * 64 * 4;
+  for (int idx = threadIdx.x; idx < TOTAL; idx += blockDim.x) {
+    const int l = idx & 63;
+    const int reg = (idx >> 6) & 3;
+    const int tile = idx >> 8;
+    const int i = tile / NS, j = tile % NS;
+    float v = 0.f;
+    for (int w = 0; w < KW; ++w) v += red[(w * MT * NS + tile) * 64 + l][reg];
+    const int m = i * 16 + 4 * (l >> 4) + reg;
+    const int n = (s0 + j) * 16 + (l & 15);
+    if (m < p.M && n < p.N) {
+      if (p.bias) v += bf16_to_f32(p.bias[n]);
+      if (p.out_f32)
+        reinterpret_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = v;
+      else
+        reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ldo + n] = f32_to_bf16_rne(v);
+    }
+  }
+}
+
 template <int MT, int NS, int GPR, int MAXW>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int gpw) {
   extern __shared__ v4f red[];  // [KW][MT * NS][64]
   constexpr int STEPS = 4 * GPR;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int KW = blockDim.x >> 6;
   const int s0 = blockIdx.x * NS;
 
   const auto ra = make_rsrc(p.a, (uint32_t)MT * p.Kt * 1024u);
@@ -116,32 +151,127 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         }
   }
 
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NS; ++j) red[(wv * MT * NS + i * NS + j) * 64 + lane] = acc[i][j];
-  __syncthreads();
+  reduce_store<MT, NS>(red, acc, p, s0);
+}
 
-  // Ordered sum over the KW waves; thread -> (tile, register, lane) with the
-  // lane fastest so 16 consecutive threads write 16 consecutive columns.
-  constexpr int TOTAL = MT * NS * 64 * 4;
-  for (int idx = threadIdx.x; idx < TOTAL; idx += blockDim.x) {
-    const int l = idx & 63;
-    const int reg = (idx >> 6) & 3;
-    const int tile = idx >> 8;
-    const int i = tile / NS, j = tile % NS;
-    float v = 0.f;
-    for (int w = 0; w < KW; ++w) v += red[(w * MT * NS + tile) * 64 + l][reg];
-    const int m = i * 16 + 4 * (l >> 4) + reg;
-    const int n = (s0 + j) * 16 + (l & 15);
-    if (m < p.M && n < p.N) {
-      if (p.bias) v += bf16_to_f32(p.bias[n]);
-      if (p.out_f32)
-        reinterpret_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = v;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * p.ldo + n] = f32_to_bf16_rne(v);
+// The same product with the activation quantisation fused in, for M <= 4:
+// the A operand is encoded from bf16 x in registers instead of being read
+// from a quantised copy.  Per scale group (4 K-steps x 4 blocks = 16 blocks
+// per row) a wave encodes all M x 16 blocks in one pass, one whole 1x32
+// block per lane (lane l: row l/16, block l%16 of the group; 64 bytes
+// loaded, amax, scale byte and 16 code bytes on its own, no cross-lane
+// step), then moves each block to its MFMA lane (row r, K-step u, block kb
+// -> lane kb*16 + r of step u) with one LDS-crossbar permute per dword;
+// rows r >= M take zero codes.  The x loads are issued ahead of the weight
+// stream and encoded while the weights are in flight.  Every workgroup
+// encodes the x rows it needs; the K split, the per-wave MFMA order and the
+// reduction are those of gemm_decode_kernel for one row tile, so the two
+// paths give identical bits.
+constexpr int kFusedRows = 4;
+
+__device__ __forceinline__ uint32_t lane_permute(uint32_t src_lane, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src_lane * 4u), (int)v);
+}
+
+template <int NS, int GPR, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void linear_decode_kernel(GemmArgs p, int gpw) {
+  extern __shared__ v4f red[];  // [KW][NS][64]
+  constexpr int STEPS = 4 * GPR;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int s0 = blockIdx.x * NS;
+
+  const auto rx = make_rsrc(p.x, p.x_bytes);
+  const auto rw = make_rsrc(p.w, (uint32_t)p.Ns * p.Kt * 1024u);
+  const auto rws = make_rsrc(p.ws, (uint32_t)p.Ns * p.G * 256u);
+
+  // Encoding pass: lane -> (row er, block ec of the group).  Rows past M and
+  // blocks past K load nothing (zero data: scale byte 0, codes 0).
+  const int er = lane >> 4, ec = lane & 15;
+  const bool erv = er < p.M;
+  const uint32_t xlane = (uint32_t)er * (uint32_t)p.ldx * 2u + (uint32_t)ec * 64u;
+  const int nblk = p.K >> 5;
+  // MFMA lane -> its row (lane % 16) and block kb (lane / 16); the encoding
+  // lane of step u is row*16 + u*4 + kb.
+  const int mr = lane & 15;
+  const bool mrv = mr < p.M;
+  const uint32_t src0 = (uint32_t)((mr & 3) * 16 + (lane >> 4));
+
+  v4f acc[1][NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  const int g_begin = wv * gpw;
+  const int g_end = min(g_begin + gpw, p.G);
+  for (int gr = g_begin; gr < g_end; gr += GPR) {
+    int4 xv[GPR][4];
+#pragma unroll
+    for (int q = 0; q < GPR; ++q) {
+      const int g = gr + q;
+      const bool ok = erv && g < g_end && g * 16 + ec < nblk;
+      const uint32_t off = xlane + (uint32_t)g * 1024u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[q][c] = buf_load16(rx, ok ? off + c * 16 : kOOB);
     }
+    int4 bf[STEPS][NS];
+    uint32_t sb[GPR][NS];
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const int t = gr * 4 + u;
+      const bool tv = (gr + u / 4) < g_end && t < p.Kt;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int s = s0 + j;
+        const uint32_t off = (tv && s < p.Ns) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
+        bf[u][j] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < GPR; ++q) {
+      const int g = gr + q;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const int s = s0 + j;
+        sb[q][j] = buf_load4(rws, (g < g_end && s < p.Ns) ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
+      }
+    }
+    // Loads stay ahead of the encoding, and the encoding ahead of the MFMAs
+    // (which wait for the weights).
+    __builtin_amdgcn_sched_barrier(0);
+    int4 af[STEPS];
+    uint32_t sa[STEPS];
+#pragma unroll
+    for (int q = 0; q < GPR; ++q) {
+      uint32_t b;
+      const int4 c = quant_block32(xv[q], b);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t src = src0 + (uint32_t)u * 4u;
+        int4 a;
+        a.x = (int)lane_permute(src, (uint32_t)c.x);
+        a.y = (int)lane_permute(src, (uint32_t)c.y);
+        a.z = (int)lane_permute(src, (uint32_t)c.z);
+        a.w = (int)lane_permute(src, (uint32_t)c.w);
+        const uint32_t sc = lane_permute(src, b);
+        af[q * 4 + u] = mrv ? a : (int4){0, 0, 0, 0};
+        sa[q * 4 + u] = sc;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u)
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        switch (u & 3) {
+          case 0: acc[0][j] = mfma_fp4<0, 0>(af[u], bf[u][j], sa[u], sb[u / 4][j], acc[0][j]); break;
+          case 1: acc[0][j] = mfma_fp4<0, 1>(af[u], bf[u][j], sa[u], sb[u / 4][j], acc[0][j]); break;
+          case 2: acc[0][j] = mfma_fp4<0, 2>(af[u], bf[u][j], sa[u], sb[u / 4][j], acc[0][j]); break;
+          default: acc[0][j] = mfma_fp4<0, 3>(af[u], bf[u][j], sa[u], sb[u / 4][j], acc[0][j]); break;
+        }
+      }
   }
+
+  reduce_store<1, NS>(red, acc, p, s0);
 }
 
 template <int MT, int NS, int GPR, int MAXW>
@@ -182,4 +312,37 @@ hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream) {
   }
 }
 
+// Fused form (M <= 4): the K split of the one-row-tile decode kernel.
+template <int NS, int GPR>
+static hipError_t launch_linear_t(const GemmArgs& p, int kw, int gpw, hipStream_t stream) {
+  const dim3 grid((unsigned)((p.Ns + NS - 1) / NS));
+  const size_t lds = (size_t)kw * NS * 64 * sizeof(v4f);
+  linear_decode_kernel<NS, GPR, 16><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  return hipGetLastError();
+}
+
+bool linear_fused_pays(int M, int N, int K) {
+  // Every workgroup re-reads and re-encodes the bf16 rows, so the fused
+  // call beats quantisation + GEMM (about 2 us for the extra launch) only
+  // while that traffic is small: measured on MI355X, at M = 1 for every
+  // decode shape, and up to M = 4 when there are few workgroups (N < 16384)
+  // and one round of groups per wave (K <= 8192).
+  if (M < 1 || M > kFusedRows) return false;
+  return M == 1 || (N < 16384 && K <= 8192);
+}
+
+hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
+  if (p.M > kFusedRows) return hipErrorInvalidValue;
+  // Up to 8192-wide K: at most 16 waves of one group each, one strip per
+  // workgroup when strips are plentiful.  Wider K: at most 8 waves of two
+  // groups per round and one strip (fewer waves re-encoding the rows, and
+  // two strips would not fit the registers).
+  if (p.G <= 16) {
+    const int kw = p.G;
+    return p.Ns >= 1024 ? launch_linear_t<1, 1>(p, kw, 1, stream) : launch_linear_t<2, 1>(p, kw, 1, stream);
+  }
+  const int gpw = (p.G + 7) / 8;
+  const int kw = (p.G + gpw - 1) / gpw;
+  return launch_linear_t<1, 2>(p, kw, gpw, stream);
+}
 }  // namespace mxfp4

@@ -64,6 +64,66 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// ---- Encoding one MX block (OCP MX v1.0, conversion of a vector of 32
+// values into one block with E2M1 elements and an E8M0 scale).
+//
+// Scale byte from the largest |bf16| bit pattern of the block: the biased
+// exponent E of amax, less emax(E2M1) = 2, clamped at 0 (zero and subnormal
+// amax give 0).  |bf16| bit patterns order like their values.
+__device__ __forceinline__ uint32_t e8m0_of_amax_bits(uint32_t amax_bits) {
+  const uint32_t e = amax_bits >> 7;
+  return e > 2 ? e - 2 : 0;
+}
+
+// Packed per-half max of |bf16| over dwords holding two bf16 each.
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t absmax_pairs(uint32_t m, uint32_t w) {
+  const v2u16 a = __builtin_bit_cast(v2u16, m), b = __builtin_bit_cast(v2u16, w & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+// The fp32 value 2^(b-127) of a scale byte (b = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t b) { return __uint_as_float(b ? (b << 23) : 0x00400000u); }
+
+// Eight bf16 values (four dwords, element 2j in the low half of dword j) ->
+// eight E2M1 codes in one dword (element i in bits 4i..4i+3), each |v| /
+// 2^(b-127) rounded to the nearest E2M1 magnitude, ties to the even code,
+// saturating at 6, sign copied.  gfx950's scaled FP4 conversion divides by
+// its scale operand and rounds exactly this way for every finite bf16 input
+// and every scale byte (checked over all 65536 patterns on MI355X; the
+// quantisation kernels' parity tests pin it against the oracle bytewise).
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e2m1_pack8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, float scale) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w0), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w1), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w2), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf16, w3), scale, 3);
+  return r;
+}
+
+// A whole 1x32 block held by one lane (four 16-byte pieces in element order)
+// -> its 16 code bytes (the lane's operand of the block-scaled FP4 MFMA) and
+// its scale byte.
+__device__ __forceinline__ int4 quant_block32(const int4 (&v)[4], uint32_t& b) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = absmax_pairs(m, (uint32_t)v[i].x);
+    m = absmax_pairs(m, (uint32_t)v[i].y);
+    m = absmax_pairs(m, (uint32_t)v[i].z);
+    m = absmax_pairs(m, (uint32_t)v[i].w);
+  }
+  b = e8m0_of_amax_bits(max(m & 0xFFFFu, m >> 16));
+  const float sc = e8m0_value(b);
+  int4 c;
+  c.x = (int)e2m1_pack8((uint32_t)v[0].x, (uint32_t)v[0].y, (uint32_t)v[0].z, (uint32_t)v[0].w, sc);
+  c.y = (int)e2m1_pack8((uint32_t)v[1].x, (uint32_t)v[1].y, (uint32_t)v[1].z, (uint32_t)v[1].w, sc);
+  c.z = (int)e2m1_pack8((uint32_t)v[2].x, (uint32_t)v[2].y, (uint32_t)v[2].z, (uint32_t)v[2].w, sc);
+  c.w = (int)e2m1_pack8((uint32_t)v[3].x, (uint32_t)v[3].y, (uint32_t)v[3].z, (uint32_t)v[3].w, sc);
+  return c;
+}
+
 // Byte offset of scale (row r, block c) in the GEMM scale layout with G groups.
 __device__ __forceinline__ uint32_t gemm_scale_offset(uint32_t r, uint32_t c, uint32_t G) {
   uint32_t t = c >> 2, kb = c & 3, g = t >> 2, j = t & 3;

@@ -20,10 +20,19 @@ struct GemmArgs {
   int out_f32;
   int M, N, K, Kt, G, Ns;  // Kt = ceil(K/128), G = ceil(Kt/4), Ns = ceil(N/16)
   int cus;                 // compute units of the device (persistent grids)
+  // bf16 activations [M, K] of the fused-quantisation path (else unused):
+  // row stride ldx elements, x_bytes = ((M-1)*ldx + K)*2 readable bytes.
+  const uint16_t* x;
+  int ldx;
+  uint32_t x_bytes;
 };
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream);
+// Activation quantisation fused into the small-M GEMM (M <= 4), and whether
+// that beats quantisation + GEMM for a shape.
+hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream);
+bool linear_fused_pays(int M, int N, int K);
 
 hipError_t launch_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q,
                              int64_t ldq, void* scales, int layout, hipStream_t stream);

@@ -7,10 +7,10 @@
 //   b = max(E(amax) - 2, 0)           E = biased exponent field of amax
 //   code = nearest E2M1 magnitude of |v| / 2^(b-127), ties to even, <= 6
 //   sign bit copied from v; element 2j -> low nibble of byte j.
-// The scaled magnitude is formed exactly by rewriting the exponent field (no
-// rounding), and the nearest-even choice is a sum of seven threshold tests
-// against the rounding midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5 (strict '>'
-// where the midpoint rounds down to the even code, '>=' where it rounds up).
+// The scale byte comes from integer compares on the |bf16| bit patterns; the
+// elements are encoded by gfx950's scaled bf16 -> FP4 conversion, which
+// divides by 2^(b-127) and rounds to nearest-even with saturation exactly
+// as above.
 //
 // Two output forms:
 //  * ROWMAJOR (weights before a preshuffle, interop): one wave per
@@ -28,23 +28,6 @@
 
 namespace mxfp4 {
 
-__device__ __forceinline__ uint32_t e2m1_code(uint32_t h, uint32_t b) {
-  const uint32_t mag = h & 0x7FFFu;
-  const uint32_t ev = mag >> 7, m7 = mag & 0x7Fu;
-  float y;
-  if (ev == 0) {
-    // bf16 subnormal (or zero): |v| = m7 * 2^-133, so y = m7 * 2^(-6-b).
-    y = __builtin_ldexpf((float)m7, -6 - (int)b);
-  } else {
-    // |v| = 2^(ev-127) (1 + m7/128); y = |v| 2^(127-b): exponent ev + 127 - b.
-    const int ye = (int)ev + 127 - (int)b;
-    y = ye <= 0 ? 0.0f : __uint_as_float(((uint32_t)ye << 23) | (m7 << 16));
-  }
-  uint32_t c = (y > 0.25f) + (y >= 0.75f) + (y > 1.25f) + (y >= 1.75f) +
-               (y > 2.5f) + (y >= 3.5f) + (y > 5.0f);
-  return c | ((h >> 12) & 8u);
-}
-
 __global__ __launch_bounds__(256) void quant_1x32_rowmajor_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, int K,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ scales, int segs) {
@@ -57,29 +40,22 @@ __global__ __launch_bounds__(256) void quant_1x32_rowmajor_kernel(
   const bool valid = (r < M) && (c < nblocks);
   const int k0 = seg * 512 + lane * 8;
 
-  uint32_t h[8];
-  uint32_t amax = 0;
+  uint32_t w[4] = {0, 0, 0, 0};
   if (valid) {
     const int4 v = *reinterpret_cast<const int4*>(x + (int64_t)r * ldx + k0);
-    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[2 * i] = w[i] & 0xFFFFu;
-      h[2 * i + 1] = w[i] >> 16;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = max(amax, h[i] & 0x7FFFu);
+    w[0] = (uint32_t)v.x, w[1] = (uint32_t)v.y, w[2] = (uint32_t)v.z, w[3] = (uint32_t)v.w;
   }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = absmax_pairs(m, w[i]);
+  uint32_t amax = max(m & 0xFFFFu, m >> 16);
   // Lanes of one block are 4 aligned lanes, all valid or all invalid.
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  const uint32_t e = amax >> 7;
-  const uint32_t b = e > 2 ? e - 2 : 0;
+  const uint32_t b = e8m0_of_amax_bits(amax);
 
   if (valid) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_code(h[i], b) << (4 * i);
+    const uint32_t packed = e2m1_pack8(w[0], w[1], w[2], w[3], e8m0_value(b));
     *reinterpret_cast<uint32_t*>(q + (int64_t)r * ldq + (k0 >> 1)) = packed;
   }
   if ((lane & 3) == 0 && valid) scales[(int64_t)r * nblocks + c] = (uint8_t)b;
@@ -102,31 +78,22 @@ __global__ __launch_bounds__(256) void quant_1x32_gemm_kernel(
   const int c = tq * 4 + kb;
   const bool valid = row < M && c < (K >> 5);
 
-  uint32_t h[8];
-  uint32_t amax = 0;
+  uint32_t w[4] = {0, 0, 0, 0};
   if (valid) {
     const int4 v = *reinterpret_cast<const int4*>(x + (int64_t)row * ldx + (int64_t)c * 32 + sub * 8);
-    const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[2 * i] = w[i] & 0xFFFFu;
-      h[2 * i + 1] = w[i] >> 16;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = max(amax, h[i] & 0x7FFFu);
+    w[0] = (uint32_t)v.x, w[1] = (uint32_t)v.y, w[2] = (uint32_t)v.z, w[3] = (uint32_t)v.w;
   }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = absmax_pairs(m, w[i]);
+  uint32_t amax = max(m & 0xFFFFu, m >> 16);
   // The 4 lanes of a block are aligned and all valid or all invalid.
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  const uint32_t e = amax >> 7;
-  const uint32_t b = valid ? (e > 2 ? e - 2 : 0) : kE8M0One;
+  const uint32_t b = valid ? e8m0_of_amax_bits(amax) : kE8M0One;
 
   if (tq < Kt) {
-    uint32_t packed = 0;
-    if (valid) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) packed |= e2m1_code(h[i], b) << (4 * i);
-    }
+    const uint32_t packed = valid ? e2m1_pack8(w[0], w[1], w[2], w[3], e8m0_value(b)) : 0u;
     *reinterpret_cast<uint32_t*>(q + (int64_t)(s * Kt + tq) * 1024 + (kb * 16 + r) * 16 + sub * 4) = packed;
   }
   if (sub == 0) scales[(int64_t)(s * G + (tq >> 2)) * 256 + (kb * 16 + r) * 4 + (tq & 3)] = (uint8_t)b;

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.mxfp4_abi_version() == 100
+    assert lib.mxfp4_abi_version() == 101
     for s in range(8):
         assert lib.mxfp4_status_str(s)
     assert lib.mxfp4_status_str(99) == b"unknown status"
@@ -119,6 +119,33 @@ def test_gemm_validation(lib):
     assert call(M=0, a=None) == 0   # nothing to do
 
 
+def test_linear_validation(lib):
+    f = lib.mxfp4_linear
+    assert lib.mxfp4_linear_workspace_bytes(4, 1024, 5120) == 0         # fused: none
+    need = lib.mxfp4_linear_workspace_bytes(17, 1024, 5120)
+    assert need >= L.weight_geometry(17, 5120)[2] + L.gemm_scale_geometry(17, 5120)[3]
+    assert lib.mxfp4_linear_workspace_bytes(5, 1024, 5120) > 0
+    assert lib.mxfp4_linear_workspace_bytes(17, 1024, 48) == 0          # K % 32
+
+    def call(x=P, ldx=64, w=P, ws=P, bias=None, out=P, ldo=16, dt=0, M=4, N=16, K=64,
+             work=None, work_bytes=0):
+        return f(x, ldx, w, ws, bias, out, ldo, dt, M, N, K, work, work_bytes, None)
+
+    assert call(dt=2) == 7
+    assert call(K=48) == 2
+    assert call(ldx=32) == 2          # ldx < K
+    assert call(ldo=8) == 2           # ldo < N
+    assert call(M=4, ldx=1 << 29) == 2    # x beyond one 32-bit buffer range
+    assert call(M=17) == 4            # workspace missing
+    assert call(M=17, work=P, work_bytes=need - 1, K=5120, ldx=5120) == 4
+    assert call(x=None) == 1
+    assert call(M=17, work=None, work_bytes=1 << 30) == 1
+    assert call(x=P_ODD) == 3
+    assert call(ldx=68) == 3
+    assert call(M=17, work=P_ODD, work_bytes=1 << 30) == 3
+    assert call(M=0, x=None) == 0
+
+
 def test_bmm_validation(lib):
     f = lib.a16wfp4_bmm
 
@@ -142,6 +169,7 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.mxfp4_quant_1x32(P, 4, 64, 64, P, 32, P, 1, None) == 5
     assert lib.mxfp4_quant_1x32(P, 4, 64, 64, P, 0, P, 1, None) == 5   # ldq ignored (GEMM layout)
     assert lib.mxfp4_gemm_a4w4(P, P, P, P, None, P, 16, 0, 4, 16, 64, None, 0, None) == 5
+    assert lib.mxfp4_linear(P, 64, P, P, None, P, 16, 0, 4, 16, 64, None, 0, None) == 5
 
 
 def test_debug_path_hook(lib):
