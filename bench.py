@@ -3,6 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-prefill] [--no-bmm]
+    python bench.py --traffic-pass          (workload of the counter runs)
+    python bench.py --traffic-summary FETCH.csv WRITE.csv CMD...   (CPU only)
 
 Headline (the metric's M <= 16 decode regime): one step is one pass over the
 decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
@@ -107,7 +109,145 @@ class Timer:
         return a.elapsed_time(b) / reps * 1e-3      # seconds per replay
 
 
+TRAFFIC_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                          "gemm_decode_kernel__headline_traffic.md")
+CALIB_BYTES = 256 << 20     # the calibration copy reads and writes this many bytes
+
+
+def decode_source_digest():
+    """sha256 over the sources the decode GEMM kernel is built from."""
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "mxfp4_block_scaled_quant_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm_decode.hip", "mxfp4_device.h", "mxfp4_launch.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """Measured HBM bytes per decode-GEMM launch (mean over the headline
+    shapes) from the committed counter summary, or None when it is missing or
+    was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_MD).read()
+    except OSError:
+        return None
+    import re
+    m = re.search(r"```json\n(.*?)\n```", text, flags=re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha256") != decode_source_digest():
+        return None
+    return d
+
+
+def traffic_pass():
+    """The workload of the FETCH_SIZE / WRITE_SIZE counter runs (run under
+    rocprofv3 --pmc): a calibration copy of CALIB_BYTES (an elementwise
+    int32 kernel reading and writing that many bytes), then the decode GEMM
+    of every headline shape once on each of its rotated weight copies."""
+    import mxfp4_block_scaled_quant_amd as mx
+    from mxfp4_block_scaled_quant_amd import inputs
+    mx.lib()
+    dev = torch.device("cuda:0")
+    src = torch.arange(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    plan = []
+    for (N, K) in DECODE_NK:
+        W = mx.quantize_weight(inputs.bits_to_torch_bf16(inputs.weights(N, K, 2)).to(dev))
+        R = copies_for(W.w_pre.numel() + W.ws_pre.numel())
+        copies = [W] + [mx.MXFP4Weight(W.w_pre.clone(), W.ws_pre.clone(), N, K) for _ in range(R - 1)]
+        b = inputs.bits_to_torch_bf16(inputs.bias(N, 2)).to(dev)
+        for M in HEADLINE_M:
+            x = inputs.bits_to_torch_bf16(inputs.activations(M, K, 2)).to(dev)
+            q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            for cp in copies:
+                mx.mxfp4_gemm_a4w4(q, s, cp.w_pre, cp.ws_pre, M, N, K, b, torch.bfloat16, out=out)
+            torch.cuda.synchronize()
+            plan.append((M, N, K, R))
+        del copies, W
+        torch.cuda.empty_cache()
+    print(json.dumps({"traffic_pass": plan}), flush=True)
+
+
+def _counter_rows(csv_path):
+    import csv
+    rows = []
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                         float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def traffic_summary(fetch_csv, write_csv, command):
+    """Turn the two counter runs into the committed summary (TRAFFIC_MD)."""
+    per = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r[2] == name]
+        calib = [v for _, k, _, v in rows if "bitwise_not" in k]
+        gemm = [v for _, k, _, v in rows if "gemm_decode_kernel" in k]
+        per[name] = (calib, gemm)
+    f_cal, f_gemm = per["FETCH_SIZE"]
+    w_cal, w_gemm = per["WRITE_SIZE"]
+    ff = CALIB_BYTES / (np.mean(f_cal) * 1024)
+    wf = CALIB_BYTES / (np.mean(w_cal) * 1024)
+    shapes = []
+    i = 0
+    for (N, K) in DECODE_NK:
+        for M in HEADLINE_M:
+            R = copies_for(N * K * 17 // 32)   # traffic_pass's copies (data + scale bytes, unpadded here)
+            fk = float(np.mean(f_gemm[i:i + R]))
+            wk = float(np.mean(w_gemm[i:i + R]))
+            i += R
+            alg = gemm_bytes(M, N, K, True)
+            tr = fk * 1024 * ff + wk * 1024 * wf
+            shapes.append(dict(M=M, N=N, K=K, launches=R, fetch_kib=round(fk, 1), write_kib=round(wk, 1),
+                               hbm_bytes=round(tr), algorithmic_bytes=round(alg),
+                               ratio=round(tr / alg, 4)))
+    assert i == len(f_gemm) == len(w_gemm), (i, len(f_gemm), len(w_gemm))
+    traffic = float(np.mean([r["hbm_bytes"] for r in shapes]))
+    summary = dict(kernel="gemm_decode_kernel", traffic_bytes_per_launch=round(traffic),
+                   algorithmic_bytes_per_launch=round(float(np.mean([r["algorithmic_bytes"] for r in shapes]))),
+                   fetch_scale=round(ff, 4), write_scale=round(wf, 4),
+                   calibration=f"int32 bitwise_not (torch elementwise kernel) over {CALIB_BYTES} bytes: FETCH_SIZE "
+                               f"{np.mean(f_cal):.0f} KiB, WRITE_SIZE {np.mean(w_cal):.0f} KiB per dispatch",
+                   source_sha256=decode_source_digest(), shapes=shapes)
+    lines = ["# gemm_decode_kernel — HBM traffic at the headline decode shapes", "",
+             "Two counter runs of the same workload (`python bench.py --traffic-pass`: the",
+             "decode GEMM of each headline shape once per rotated weight copy, after a",
+             f"calibration copy of {CALIB_BYTES >> 20} MiB):", "", "```", *command, "```", "",
+             "Each counter is scaled by what it reads for the calibration copy (known",
+             "bytes read and written), then averaged per shape over its launches;",
+             "`traffic_bytes_per_launch` is the mean over the 9 shapes, as `achieved`",
+             "in the benchmark's roofline.  bench.py reports it only while",
+             "`source_sha256` matches the decode kernel's sources.", "",
+             "| M | N | K | launches | FETCH KiB | WRITE KiB | HBM bytes | algorithmic | ratio |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in shapes:
+        lines.append(f"| {r['M']} | {r['N']} | {r['K']} | {r['launches']} | {r['fetch_kib']} | "
+                     f"{r['write_kib']} | {r['hbm_bytes']} | {r['algorithmic_bytes']} | {r['ratio']} |")
+    lines += ["", "```json", json.dumps(summary), "```", ""]
+    with open(TRAFFIC_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {TRAFFIC_MD}: traffic {traffic:.0f} B/launch")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-pass":
+        return traffic_pass()
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-summary":
+        return traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -324,6 +464,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inputs)
 
+    traffic = read_traffic()
     line = {
         "metric": METRIC,
         "value": round(value_gbs, 1),
@@ -352,7 +493,7 @@ def main():
             "peak": PEAK_HBM / 1e9,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM, 4),
-            "traffic": None,
+            "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
             "launch_us": round(dom_time / len(head_rows) * 1e6, 3),
             "bytes_per_launch": round(dom_bytes / len(head_rows)),
         },
