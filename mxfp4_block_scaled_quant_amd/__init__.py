@@ -16,7 +16,10 @@ Entry points (same names as the C ABI):
 * :func:`a16wfp4_bmm` -- bf16 [B, M, K] x MXFP4 [B, N, K] batched GEMM
 
 Convenience: :func:`quantize_weight` (quant + preshuffle, once at load) and
-:func:`linear` (:func:`mxfp4_linear` over any leading dimensions).
+:func:`linear` (:func:`mxfp4_linear` over any leading dimensions).  The same
+entry points as torch custom operators (``torch.ops.mxfp4.*``, with fake
+implementations for tracing and torch.compile) are registered by importing
+:mod:`mxfp4_block_scaled_quant_amd.ops`.
 """
 
 from __future__ import annotations
