@@ -22,8 +22,8 @@ rotation), bracketed by HIP events on the capture/replay stream.
 Also reported (same JSON line): the dominant kernel's roofline (the decode
 GEMM on pre-quantised activations at the headline shapes, timed in its own
 graph-replayed loop),
-the full decode sweep (M up to 64: the whole call, and the GEMM alone with
-quant apart), the
+the full decode sweep (M up to 64: the whole call, the GEMM alone with quant
+apart, and the call on row-major prequantised activations), the
 prefill sweep (M in {512, 2048, 8192}: TFLOP/s and fraction of the 10.1
 PFLOP/s dense FP4 peak), the A16WFP4 BMM sweep (MLA K-up / V-up on 16 heads),
 and the CPU oracle timed on a bounded sample of the headline workload.
@@ -390,6 +390,11 @@ def main():
             gb = gemm_bytes(M, N, K, True)
             tq = quant_time(x, q, s)
             tl = linear_time(M, N, K, x, b, out, weights[(N, K)])
+            qr, sr = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_ROWMAJOR)
+            sr = sr.reshape(M, K // 32)
+            cps = weights[(N, K)]
+            tp = per_launch_time(lambda i: mx.mxfp4_linear_prequantized(
+                qr, sr, cps[i].w_pre, cps[i].ws_pre, N, b, torch.bfloat16, out=out), len(cps), 400)
             pb = pipeline_bytes(M, N, K, True)
             decode_rows.append(dict(M=M, N=N, K=K,
                                     linear_us=round(tl * 1e6, 3),
@@ -399,6 +404,7 @@ def main():
                                     gemm_GBps=round(gb / t / 1e9, 1),
                                     hbm_frac=round(gb / t / PEAK_HBM, 4),
                                     quant_us=round(tq * 1e6, 3),
+                                    prequantized_us=round(tp * 1e6, 3),
                                     tflops=round(2 * M * N * K / tl / 1e12, 2)))
     head_rows = [r for r in decode_rows if r["M"] in HEADLINE_M]
     dom_bytes = sum(gemm_bytes(r["M"], r["N"], r["K"], True) for r in head_rows)

@@ -181,6 +181,44 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Scale re-layout for activations quantised elsewhere (P2 §2: a fused
+ * producer hands over (packed FP4, row-major E8M0 scales); the scales are
+ * swizzled into the GEMM's order and padded with E8M0 1.0 before the GEMM).
+ *
+ *   scales  ROWMAJOR [rows, K/32], row stride lds BYTES (lds >= K/32)
+ *   out     mxfp4_scale_bytes(rows, K, MXFP4_LAYOUT_GEMM) bytes, 4-byte
+ *           aligned: the GEMM scale layout, every padding byte 0x7F
+ *   rows >= 0 (0 enqueues nothing), K > 0, K % 32 == 0.
+ */
+int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t K,
+                         void* out, void* stream);
+
+/*
+ * The W4A4 linear from activations quantised elsewhere (P2 §2, the
+ * prequantised-input form of apply_weights): packed FP4 and E8M0 scales in
+ * the ROWMAJOR form mxfp4_quant_1x32 also writes, as a fused producer
+ * (normalisation + quantisation) would hand them over.
+ *   out[m, n] = round(sum_k dq(x)[m,k] dq(W)[n,k] + bias[n])
+ * For M <= 64 the GEMM kernel reads the row-major operands directly (one
+ * launch; bitwise the result of mxfp4_gemm_a4w4 on the same values in the
+ * GEMM layouts); for larger M they are permuted into `workspace` first.
+ *
+ *   x_fp4     packed FP4 [M, K/2], row stride ldq BYTES (ldq >= K/2,
+ *             ldq % 16 == 0, 16-byte aligned)
+ *   x_scales  E8M0 [M, K/32], row stride lds BYTES (lds >= K/32)
+ *   w_pre, ws_pre, bias, out, ldo, out_dtype: as for mxfp4_gemm_a4w4
+ *   workspace mxfp4_linear_prequantized_workspace_bytes(M, N, K) bytes (0
+ *             for M <= 64: may be NULL), 16-byte aligned, caller-owned
+ *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
+ */
+size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scales,
+                              int64_t lds, const void* w_pre, const void* ws_pre,
+                              const void* bias, void* out, int64_t ldo, int out_dtype,
+                              int64_t M, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * A16WFP4 batched GEMM (P3 §Motivation and §Modifications: the MLA absorbed
  * K/V projection weights stay in packed MXFP4, the batched products take
  * bf16 activations, and the V-up result is written batch-major).  For each

@@ -13,6 +13,9 @@ Entry points (same names as the C ABI):
 * :func:`mxfp4_gemm_a4w4` -- W4A4 GEMM with optional bias, bf16/fp32 out
 * :func:`mxfp4_linear` -- bf16 activations -> quant + GEMM (+ bias) in one call,
   the quantisation fused into the GEMM kernel for M <= 16
+* :func:`mxfp4_shuffle_scales` -- row-major E8M0 scales -> the GEMM scale layout
+* :func:`mxfp4_linear_prequantized` -- the linear from row-major packed FP4 +
+  scales handed over by a producer
 * :func:`a16wfp4_bmm` -- bf16 [B, M, K] x MXFP4 [B, N, K] batched GEMM
 
 Convenience: :func:`quantize_weight` (quant + preshuffle, once at load) and
@@ -59,6 +62,11 @@ _SIGNATURES = {
     "mxfp4_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_linear": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
                               _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
+    "mxfp4_shuffle_scales": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "mxfp4_linear_prequantized_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "mxfp4_linear_prequantized": (_c_int, [_c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp,
+                                           _c_vp, _c_i64, _c_int, _c_i64, _c_i64, _c_i64,
+                                           _c_vp, _c_size, _c_vp]),
     "a16wfp4_bmm": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int,
                              _c_i64, _c_i64, _c_i64, _c_i64, _c_vp]),
     "mxfp4_debug_set_gemm_path": (_c_int, [_c_int]),
@@ -219,6 +227,56 @@ def mxfp4_linear(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: 
     _check("mxfp4_linear", lib().mxfp4_linear(
         _ptr(x), x.stride(0), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0),
         code, M, N, K, _ptr(workspace), ws_bytes, _stream(x.device)))
+    return out
+
+
+def mxfp4_shuffle_scales(scales: torch.Tensor, rows: int, K: int,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row-major E8M0 scales [rows, K/32] (any row stride, unit stride along
+    the blocks) -> 1-D uint8 in the GEMM scale layout, padding 0x7F."""
+    _require_cuda(scales, "scales")
+    s2 = scales.reshape(rows, K // 32) if scales.dim() == 1 else scales
+    if s2.dtype != torch.uint8 or s2.shape != (rows, K // 32) or s2.stride(1) != 1:
+        raise ValueError("scales must be uint8 [rows, K/32] with unit stride along the blocks")
+    if out is None:
+        out = torch.empty(scale_bytes(rows, K, MXFP4_LAYOUT_GEMM), dtype=torch.uint8,
+                          device=scales.device)
+    _check("mxfp4_shuffle_scales", lib().mxfp4_shuffle_scales(
+        _ptr(s2), s2.stride(0), rows, K, _ptr(out), _stream(scales.device)))
+    return out
+
+
+def linear_prequantized_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mxfp4_linear_prequantized_workspace_bytes(M, N, K))
+
+
+def mxfp4_linear_prequantized(x_fp4: torch.Tensor, x_scales: torch.Tensor, w_pre: torch.Tensor,
+                              ws_pre: torch.Tensor, N: int, bias: Optional[torch.Tensor] = None,
+                              out_dtype: torch.dtype = torch.bfloat16,
+                              out: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[M, N] from row-major packed FP4 x_fp4 [M, K/2] and E8M0 x_scales
+    [M, K/32] (each with unit stride along K and any row stride)."""
+    _require_cuda(x_fp4, "x_fp4")
+    if x_fp4.dtype != torch.uint8 or x_fp4.dim() != 2 or x_fp4.stride(1) != 1:
+        raise ValueError("x_fp4 must be uint8 [M, K/2] with unit stride along K")
+    M, K = x_fp4.shape[0], x_fp4.shape[1] * 2
+    if (x_scales.dtype != torch.uint8 or x_scales.dim() != 2 or x_scales.shape != (M, K // 32)
+            or x_scales.stride(1) != 1):
+        raise ValueError("x_scales must be uint8 [M, K/32] with unit stride along the blocks")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
+        raise ValueError("bias must be bf16 [N]")
+    code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x_fp4.device)
+    need = linear_prequantized_workspace_bytes(M, N, K)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_fp4.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check("mxfp4_linear_prequantized", lib().mxfp4_linear_prequantized(
+        _ptr(x_fp4), x_fp4.stride(0), _ptr(x_scales), x_scales.stride(0), _ptr(w_pre),
+        _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0), code, M, N, K, _ptr(workspace),
+        ws_bytes, _stream(x_fp4.device)))
     return out
 
 

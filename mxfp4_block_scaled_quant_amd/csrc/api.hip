@@ -187,6 +187,8 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   p.x = nullptr;
   p.ldx = 0;
   p.x_bytes = 0;
+  p.a_rowmajor = 0;
+  p.lda = p.lds = 0;
   int path = get_gemm_path_override();
   if (path == 0) path = M <= 64 ? 1 : 2;
   if (path == 1 && M > 64) path = 2;  // the decode kernel covers at most 64 rows
@@ -240,6 +242,8 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   p.Kt = (int)cdiv(K, 128);
   p.G = (int)cdiv(p.Kt, 4);
   p.Ns = (int)cdiv(N, 16);
+  p.a_rowmajor = 0;
+  p.lda = p.lds = 0;
   if (fused) {
     p.a = nullptr;
     p.as = nullptr;
@@ -259,6 +263,90 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   p.ldx = 0;
   p.x_bytes = 0;
   return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+}
+
+int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t K, void* out,
+                         void* stream) {
+  if (rows < 0 || K <= 0 || K % 32 || K > kMaxK || rows > kMaxBuf) return MXFP4_ERR_SHAPE;
+  if (lds < K / 32 || gemm_scale_bytes(rows, K) > kMaxBuf) return MXFP4_ERR_SHAPE;
+  if (rows == 0) return MXFP4_OK;
+  if (!scales || !out) return MXFP4_ERR_NULL;
+  if (!aligned(out, 4)) return MXFP4_ERR_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  return launched(launch_preshuffle_strided(nullptr, 0, scales, lds, 1, rows, K, nullptr, out,
+                                            (hipStream_t)stream));
+}
+
+size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
+  if (M <= 64) return 0;
+  return (size_t)(cdiv(gemm_data_bytes(M, K), 256) * 256 + gemm_scale_bytes(M, K)) +
+         mxfp4_gemm_workspace_bytes(M, N, K);
+}
+
+int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scales, int64_t lds,
+                              const void* w_pre, const void* ws_pre, const void* bias, void* out,
+                              int64_t ldo, int out_dtype, int64_t M, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
+  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (ldo < N || ldq < K / 2 || lds < K / 32) return MXFP4_ERR_SHAPE;
+  if (ldo > kMaxBuf / 256 / (out_dtype == MXFP4_OUT_F32 ? 4 : 2)) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
+      gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  // the small-M kernel addresses the row-major operands through 32-bit ranges
+  if (M > 0 && M <= 64 && ((M - 1) * ldq + K / 2 > kMaxBuf || (M - 1) * lds + K / 32 > kMaxBuf))
+    return MXFP4_ERR_SHAPE;
+  const size_t need = mxfp4_linear_prequantized_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return MXFP4_ERR_WORKSPACE;
+  if (M == 0) return MXFP4_OK;
+  if (!x_fp4 || !x_scales || !w_pre || !ws_pre || !out || (need && !workspace)) return MXFP4_ERR_NULL;
+  if (!aligned(x_fp4, 16) || ldq % 16 || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
+      !aligned(out, 4) || (bias && !aligned(bias, 2)) || (need && !aligned(workspace, 16)))
+    return MXFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = check_device(&cus);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs p;
+  p.cus = cus;
+  p.w = (const uint8_t*)w_pre;
+  p.ws = (const uint8_t*)ws_pre;
+  p.bias = (const uint16_t*)bias;
+  p.out = out;
+  p.ldo = ldo;
+  p.out_f32 = out_dtype == MXFP4_OUT_F32;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.Kt = (int)cdiv(K, 128);
+  p.G = (int)cdiv(p.Kt, 4);
+  p.Ns = (int)cdiv(N, 16);
+  p.x = nullptr;
+  p.ldx = 0;
+  p.x_bytes = 0;
+  if (M <= 64) {
+    // the small-M kernel gathers the row-major operands itself: one launch
+    p.a = (const uint8_t*)x_fp4;
+    p.as = (const uint8_t*)x_scales;
+    p.a_rowmajor = 1;
+    p.lda = (uint32_t)ldq;
+    p.lds = (uint32_t)lds;
+    return launched(launch_gemm_decode(p, s));
+  }
+  // larger M: permute into the GEMM layouts in the workspace, then the GEMM
+  uint8_t* q = (uint8_t*)workspace;
+  uint8_t* sc = q + cdiv(gemm_data_bytes(M, K), 256) * 256;
+  st = launched(launch_preshuffle_strided(x_fp4, ldq, x_scales, lds, 1, M, K, q, sc, s));
+  if (st) return st;
+  p.a = q;
+  p.as = sc;
+  p.a_rowmajor = 0;
+  p.lda = p.lds = 0;
+  return launched(launch_gemm_prefill(p, s));
 }
 
 int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, const void* ws_pre,

@@ -73,17 +73,25 @@ __device__ __forceinline__ void reduce_store(v4f* red, const v4f (&acc)[MT][NS],
   }
 }
 
-template <int MT, int NS, int GPR, int MAXW>
+// AROW: the activations come row-major as a producer hands them over
+// (packed FP4 [M, K/2], row stride lda bytes; scales [M, K/32], row stride
+// lds bytes) and are gathered into the same MFMA operands: lane l's 16 bytes
+// of row r, block kb are one contiguous piece of the row, and its scale
+// dword is assembled from the 4 K-steps' bytes.  Same values, same MFMAs.
+template <int MT, int NS, int GPR, int MAXW, bool AROW>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int gpw) {
   extern __shared__ v4f red[];  // [KW][MT * NS][64]
   constexpr int STEPS = 4 * GPR;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int s0 = blockIdx.x * NS;
+  const int nblk = p.K >> 5;
 
-  const auto ra = make_rsrc(p.a, (uint32_t)MT * p.Kt * 1024u);
+  const auto ra = make_rsrc(p.a, AROW ? (uint32_t)(p.M - 1) * p.lda + (uint32_t)(p.K >> 1)
+                                      : (uint32_t)MT * p.Kt * 1024u);
   const auto rw = make_rsrc(p.w, (uint32_t)p.Ns * p.Kt * 1024u);
-  const auto ras = make_rsrc(p.as, (uint32_t)MT * p.G * 256u);
+  const auto ras = make_rsrc(p.as, AROW ? (uint32_t)(p.M - 1) * p.lds + (uint32_t)nblk
+                                        : (uint32_t)MT * p.G * 256u);
   const auto rws = make_rsrc(p.ws, (uint32_t)p.Ns * p.G * 256u);
 
   v4f acc[MT][NS];
@@ -118,7 +126,22 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         sb[q][j] = buf_load4(rws, (gv && s < p.Ns) ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
       }
 #pragma unroll
-      for (int i = 0; i < MT; ++i) sa[q][i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+      for (int i = 0; i < MT; ++i) {
+        if constexpr (AROW) {
+          const int row = i * 16 + (lane & 15);
+          const bool ok = gv && row < p.M;
+          uint32_t word = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = (g * 4 + j) * 4 + (lane >> 4);
+            const uint32_t off = (ok && c < nblk) ? (uint32_t)row * p.lds + (uint32_t)c : kOOB;
+            word |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, off, 0, 0) << (8 * j);
+          }
+          sa[q][i] = word;
+        } else {
+          sa[q][i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
@@ -127,8 +150,15 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         // rows past M are zero padding: skip their bytes
-        const bool rv = i * 16 + (lane & 15) < p.M;
-        af[u][i] = buf_load16(ra, (tv && rv) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+        const int row = i * 16 + (lane & 15);
+        const bool rv = row < p.M;
+        if constexpr (AROW) {
+          const bool cv = t * 4 + (lane >> 4) < nblk;
+          af[u][i] = buf_load16(ra, (tv && rv && cv) ? (uint32_t)row * p.lda + (uint32_t)(t * 64 + (lane >> 4) * 16)
+                                                       : kOOB);
+        } else {
+          af[u][i] = buf_load16(ra, (tv && rv) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+        }
       }
     }
     // Keep every load of the round ahead of the first wait: without this the
@@ -278,7 +308,10 @@ template <int MT, int NS, int GPR, int MAXW>
 static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_t stream) {
   const dim3 grid((unsigned)((p.Ns + NS - 1) / NS));
   const size_t lds = (size_t)kw * MT * NS * 64 * sizeof(v4f);
-  gemm_decode_kernel<MT, NS, GPR, MAXW><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  if (p.a_rowmajor)
+    gemm_decode_kernel<MT, NS, GPR, MAXW, true><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  else
+    gemm_decode_kernel<MT, NS, GPR, MAXW, false><<<grid, 64 * kw, lds, stream>>>(p, gpw);
   return hipGetLastError();
 }
 

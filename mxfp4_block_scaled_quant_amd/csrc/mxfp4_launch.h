@@ -25,6 +25,10 @@ struct GemmArgs {
   const uint16_t* x;
   int ldx;
   uint32_t x_bytes;
+  // Row-major quantised activations (small-M kernel only): a is [M, K/2]
+  // with row stride lda bytes, as [M, K/32] with row stride lds bytes.
+  int a_rowmajor;
+  uint32_t lda, lds;
 };
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
@@ -39,6 +43,11 @@ hipError_t launch_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, v
 
 hipError_t launch_preshuffle(const void* w_fp4, const void* w_scales, int64_t batch, int64_t N,
                              int64_t K, void* w_out, void* ws_out, hipStream_t stream);
+// Same permutation from row-strided sources (ldw / lds bytes per row); a
+// NULL w_fp4 permutes the scales only.
+hipError_t launch_preshuffle_strided(const void* w_fp4, int64_t ldw, const void* w_scales,
+                                     int64_t lds, int64_t batch, int64_t N, int64_t K,
+                                     void* w_out, void* ws_out, hipStream_t stream);
 
 hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void* w,
                             const void* ws, void* out, int64_t sob, int64_t som, int out_f32,

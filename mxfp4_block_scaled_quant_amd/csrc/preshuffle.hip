@@ -1,4 +1,5 @@
-// Load-time weight preshuffle into the library's gfx950 layout.
+// Load-time weight preshuffle into the library's gfx950 layout (and the same
+// permutation for row-major quantised activations handed over by a producer).
 //
 // P1 §Modifications and P2 §2 (process_weights_after_loading) rearrange the
 // FP4 weights and their E8M0 scales once after loading, into the order the
@@ -15,10 +16,11 @@
 
 namespace mxfp4 {
 
-// One thread per 16-byte slot of the preshuffled data.
+// One thread per 16-byte slot of the preshuffled data; source row (b, n) at
+// byte (b*N + n)*ldw.
 __global__ __launch_bounds__(256) void preshuffle_data_kernel(
-    const uint8_t* __restrict__ w, int N, int K, uint8_t* __restrict__ out, int Ns, int Kt,
-    int64_t total_slots) {
+    const uint8_t* __restrict__ w, int64_t ldw, int N, int K, uint8_t* __restrict__ out, int Ns,
+    int Kt, int64_t total_slots) {
   const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (slot >= total_slots) return;
   const int l = (int)(slot & 63);
@@ -31,14 +33,15 @@ __global__ __launch_bounds__(256) void preshuffle_data_kernel(
   const int n = s * 16 + r, c = t * 4 + kb;
   int4 v = {0, 0, 0, 0};
   if (n < N && c < (K >> 5))
-    v = *reinterpret_cast<const int4*>(w + ((b * N + n) * (int64_t)(K >> 1) + (int64_t)c * 16));
+    v = *reinterpret_cast<const int4*>(w + ((b * N + n) * ldw + (int64_t)c * 16));
   *reinterpret_cast<int4*>(out + slot * 16) = v;
 }
 
-// One thread per 4-byte scale dword of the GEMM scale layout (per batch).
+// One thread per 4-byte scale dword of the GEMM scale layout (per batch);
+// source row (b, n) at byte (b*N + n)*lds.
 __global__ __launch_bounds__(256) void preshuffle_scale_kernel(
-    const uint8_t* __restrict__ ws, int N, int K, uint8_t* __restrict__ out, int Ns, int G,
-    int64_t total_dwords) {
+    const uint8_t* __restrict__ ws, int64_t lds, int N, int K, uint8_t* __restrict__ out, int Ns,
+    int G, int64_t total_dwords) {
   const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (d >= total_dwords) return;
   const int l = (int)(d & 63);
@@ -55,26 +58,35 @@ __global__ __launch_bounds__(256) void preshuffle_scale_kernel(
   for (int j = 0; j < 4; ++j) {
     const int c = (g * 4 + j) * 4 + kb;
     uint32_t byte = kE8M0One;
-    if (n < N && c < nblocks) byte = ws[(b * N + n) * (int64_t)nblocks + c];
+    if (n < N && c < nblocks) byte = ws[(b * N + n) * lds + c];
     word |= byte << (8 * j);
   }
   *reinterpret_cast<uint32_t*>(out + d * 4) = word;
 }
 
-hipError_t launch_preshuffle(const void* w_fp4, const void* w_scales, int64_t batch, int64_t N,
-                             int64_t K, void* w_out, void* ws_out, hipStream_t stream) {
+hipError_t launch_preshuffle_strided(const void* w_fp4, int64_t ldw, const void* w_scales,
+                                     int64_t lds, int64_t batch, int64_t N, int64_t K,
+                                     void* w_out, void* ws_out, hipStream_t stream) {
   const int Ns = (int)((N + 15) / 16);
   const int Kt = (int)((K + 127) / 128);
   const int G = (Kt + 3) / 4;
   const int64_t slots = batch * Ns * (int64_t)Kt * 64;
   const int64_t dwords = batch * Ns * (int64_t)G * 64;
-  preshuffle_data_kernel<<<dim3((unsigned)((slots + 255) / 256)), 256, 0, stream>>>(
-      (const uint8_t*)w_fp4, (int)N, (int)K, (uint8_t*)w_out, Ns, Kt, slots);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (w_fp4) {
+    preshuffle_data_kernel<<<dim3((unsigned)((slots + 255) / 256)), 256, 0, stream>>>(
+        (const uint8_t*)w_fp4, ldw, (int)N, (int)K, (uint8_t*)w_out, Ns, Kt, slots);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   preshuffle_scale_kernel<<<dim3((unsigned)((dwords + 255) / 256)), 256, 0, stream>>>(
-      (const uint8_t*)w_scales, (int)N, (int)K, (uint8_t*)ws_out, Ns, G, dwords);
+      (const uint8_t*)w_scales, lds, (int)N, (int)K, (uint8_t*)ws_out, Ns, G, dwords);
   return hipGetLastError();
+}
+
+hipError_t launch_preshuffle(const void* w_fp4, const void* w_scales, int64_t batch, int64_t N,
+                             int64_t K, void* w_out, void* ws_out, hipStream_t stream) {
+  return launch_preshuffle_strided(w_fp4, K / 2, w_scales, K / 32, batch, N, K, w_out, ws_out,
+                                   stream);
 }
 
 }  // namespace mxfp4

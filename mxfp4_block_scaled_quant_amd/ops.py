@@ -11,6 +11,9 @@ queries, and works with symbolic sizes.
     torch.ops.mxfp4.preshuffle_weight(w_fp4, w_scales, N, K, batch) -> (w_pre, ws_pre)
     torch.ops.mxfp4.gemm_a4w4(a, a_scales, w_pre, ws_pre, M, N, K, bias, out_dtype) -> [M, N]
     torch.ops.mxfp4.linear(x, w_pre, ws_pre, N, bias, out_dtype) -> [M, N]
+    torch.ops.mxfp4.shuffle_scales(scales, rows, K) -> GEMM-layout scales
+    torch.ops.mxfp4.linear_prequantized(x_fp4, x_scales, w_pre, ws_pre, N, bias,
+        out_dtype) -> [M, N]
     torch.ops.mxfp4.a16wfp4_bmm(x, w_pre, ws_pre, N, batch_major, out_dtype)
         -> [B, M, N] or [M, B, N]
 
@@ -26,7 +29,8 @@ import torch
 from torch import Tensor
 
 from . import (MXFP4_LAYOUT_GEMM, MXFP4_LAYOUT_ROWMAJOR, a16wfp4_bmm, mxfp4_gemm_a4w4,
-               mxfp4_linear, mxfp4_preshuffle_weight, mxfp4_quant_1x32)
+               mxfp4_linear, mxfp4_linear_prequantized, mxfp4_preshuffle_weight,
+               mxfp4_quant_1x32, mxfp4_shuffle_scales)
 
 __all__ = ["gemm_data_bytes", "gemm_scale_bytes"]
 
@@ -99,6 +103,28 @@ def linear(x: Tensor, w_pre: Tensor, ws_pre: Tensor, N: int, bias: Optional[Tens
 @linear.register_fake
 def _(x, w_pre, ws_pre, N, bias=None, out_dtype=torch.bfloat16):
     return x.new_empty((x.shape[0], N), dtype=out_dtype)
+
+
+@torch.library.custom_op("mxfp4::shuffle_scales", mutates_args=())
+def shuffle_scales(scales: Tensor, rows: int, K: int) -> Tensor:
+    return mxfp4_shuffle_scales(scales, rows, K)
+
+
+@shuffle_scales.register_fake
+def _(scales, rows, K):
+    return scales.new_empty((gemm_scale_bytes(rows, K),), dtype=torch.uint8)
+
+
+@torch.library.custom_op("mxfp4::linear_prequantized", mutates_args=())
+def linear_prequantized(x_fp4: Tensor, x_scales: Tensor, w_pre: Tensor, ws_pre: Tensor, N: int,
+                        bias: Optional[Tensor] = None,
+                        out_dtype: torch.dtype = torch.bfloat16) -> Tensor:
+    return mxfp4_linear_prequantized(x_fp4, x_scales, w_pre, ws_pre, N, bias, out_dtype)
+
+
+@linear_prequantized.register_fake
+def _(x_fp4, x_scales, w_pre, ws_pre, N, bias=None, out_dtype=torch.bfloat16):
+    return x_fp4.new_empty((x_fp4.shape[0], N), dtype=out_dtype)
 
 
 @torch.library.custom_op("mxfp4::a16wfp4_bmm", mutates_args=())

@@ -146,6 +146,33 @@ def test_linear_validation(lib):
     assert call(M=0, x=None) == 0
 
 
+def test_shuffle_scales_and_prequantized_validation(lib):
+    f = lib.mxfp4_shuffle_scales
+    assert f(P, 4, 8, 100, P, None) == 2        # K % 32
+    assert f(P, 2, 8, 128, P, None) == 2        # lds < K/32
+    assert f(None, 4, 8, 128, P, None) == 1
+    assert f(P, 4, 8, 128, P_ODD.value + 1, None) == 3
+    assert f(None, 4, 0, 128, None, None) == 0  # no rows
+    g = lib.mxfp4_linear_prequantized
+    assert lib.mxfp4_linear_prequantized_workspace_bytes(64, 96, 4128) == 0
+    need = lib.mxfp4_linear_prequantized_workspace_bytes(65, 96, 4128)
+    assert need >= L.weight_geometry(65, 4128)[2] + L.gemm_scale_geometry(65, 4128)[3]
+
+    def call(x=P, ldq=32, s=P, lds=2, w=P, ws=P, bias=None, out=P, ldo=16, dt=0, M=4, N=16, K=64,
+             work=None, work_bytes=0):
+        return g(x, ldq, s, lds, w, ws, bias, out, ldo, dt, M, N, K, work, work_bytes, None)
+
+    assert call(dt=5) == 7
+    assert call(K=48) == 2
+    assert call(ldq=16) == 2          # ldq < K/2
+    assert call(lds=1) == 2           # lds < K/32
+    assert call(M=65) == 4            # workspace missing
+    assert call(s=None) == 1
+    assert call(ldq=40) == 3          # ldq % 16
+    assert call(x=P_ODD) == 3
+    assert call(M=0, x=None, s=None) == 0
+
+
 def test_bmm_validation(lib):
     f = lib.a16wfp4_bmm
 

@@ -1,0 +1,79 @@
+"""GPU parity of the prequantised-input path: activations quantised by a
+producer arrive as row-major packed FP4 + row-major E8M0 scales.
+
+* mxfp4_shuffle_scales: bytewise the oracle's GEMM scale layout (0x7F
+  padding), with and without a row stride.
+* mxfp4_linear_prequantized: the oracle's GEMM tolerance, and bitwise the
+  result of mxfp4_gemm_a4w4 on the same values in the GEMM layouts through
+  the same kernel (small-M kernel reading the row-major operands directly
+  for M <= 64; permutation into the workspace, then the tiled kernel,
+  above)."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_block_scaled_quant_amd as mx
+from mxfp4_block_scaled_quant_amd import inputs
+from oracle import layout as L
+from oracle import quant as Q
+from tests.helpers import dev_bf16, host_u8, need_gpu
+from tests.test_gpu_gemm import _check
+
+pytestmark = pytest.mark.gpu
+
+
+def _strided_u8(a, pad):
+    """Device uint8 copy of the 2-D array `a` inside rows padded by `pad` bytes."""
+    rows, cols = a.shape
+    buf = np.zeros((rows, cols + pad), dtype=np.uint8)
+    buf[:, :cols] = a
+    return torch.from_numpy(buf).cuda()[:, :cols]
+
+
+@pytest.mark.parametrize("rows,K,pad", [(1, 32, 0), (37, 4128, 3), (300, 256, 0), (64, 14336, 16),
+                                        (17, 640, 1)])
+def test_shuffle_scales_bit_exact(rows, K, pad):
+    need_gpu()
+    x = inputs.activations(rows, K, 5, edge=True)
+    _, s = Q.quant_1x32(x)
+    out = mx.mxfp4_shuffle_scales(_strided_u8(s, pad), rows, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(out), L.scales_to_gemm_layout(s))
+
+
+CASES = [
+    # name, M, N, K, kwargs, (ldq pad, lds pad)
+    ("m1_1024x5120", 1, 1024, 5120, dict(seed=0, outliers=True), (0, 0)),
+    ("m5_17x96", 5, 17, 96, dict(seed=9, with_bias=True), (16, 1)),
+    ("m16_520x1056_bias", 16, 520, 1056, dict(seed=6, outliers=True, with_bias=True), (0, 0)),
+    ("m37_96x4128_edge", 37, 96, 4128, dict(seed=5, edge=True, with_bias=True), (32, 5)),
+    ("m64_300x640", 64, 300, 640, dict(seed=6, with_bias=True), (0, 0)),
+    ("m65_257x2080", 65, 257, 2080, dict(seed=10, outliers=True), (16, 2)),      # tiled path
+    ("m300_128x256_edge", 300, 128, 256, dict(seed=5, edge=True), (0, 0)),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K,kw,pads", CASES, ids=[c[0] for c in CASES])
+def test_linear_prequantized(name, M, N, K, kw, pads):
+    need_gpu()
+    prob = inputs.linear_problem(M, N, K, **kw)
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    q_rm, s_rm = Q.quant_1x32(prob["x"])                 # the producer's output (oracle bytes)
+    xq, xs = _strided_u8(q_rm, pads[0]), _strided_u8(s_rm, pads[1])
+    b = None if prob["bias"] is None else dev_bf16(prob["bias"])
+    y32 = mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.float32)
+    y16 = mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.bfloat16)
+    # the same values in the GEMM layouts through the same kernel
+    mx.set_gemm_path(1 if M <= 64 else 2)
+    try:
+        q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
+        r32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
+        r16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16)
+    finally:
+        mx.set_gemm_path(0)
+    torch.cuda.synchronize()
+    y32n, r32n = y32.cpu().numpy(), r32.cpu().numpy()
+    assert np.array_equal(y32n.view(np.uint32), r32n.view(np.uint32))
+    assert torch.equal(y16.cpu().view(torch.int16), r16.cpu().view(torch.int16))
+    _check(prob, y32n, y16.cpu().view(torch.int16).numpy().view(np.uint16))
