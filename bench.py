@@ -23,7 +23,8 @@ Also reported (same JSON line): the dominant kernel's roofline (the decode
 GEMM on pre-quantised activations at the headline shapes, timed in its own
 graph-replayed loop),
 the full decode sweep (M up to 64: the whole call, the GEMM alone with quant
-apart, and the call on row-major prequantised activations), the
+apart, the call on row-major prequantised activations, and the GEMM writing
+MXFP4 for the next layer), the
 prefill sweep (M in {512, 2048, 8192}: TFLOP/s and fraction of the 10.1
 PFLOP/s dense FP4 peak), the A16WFP4 BMM sweep (MLA K-up / V-up on 16 heads),
 and the CPU oracle timed on a bounded sample of the headline workload.
@@ -395,6 +396,10 @@ def main():
             cps = weights[(N, K)]
             tp = per_launch_time(lambda i: mx.mxfp4_linear_prequantized(
                 qr, sr, cps[i].w_pre, cps[i].ws_pre, N, b, torch.bfloat16, out=out), len(cps), 400)
+            oq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+            osc = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+            tf4 = per_launch_time(lambda i: mx.mxfp4_gemm_a4w4_mxfp4_out(
+                q, s, cps[i].w_pre, cps[i].ws_pre, M, N, K, b, out_fp4=oq, out_scales=osc), len(cps), 400)
             pb = pipeline_bytes(M, N, K, True)
             decode_rows.append(dict(M=M, N=N, K=K,
                                     linear_us=round(tl * 1e6, 3),
@@ -405,6 +410,7 @@ def main():
                                     hbm_frac=round(gb / t / PEAK_HBM, 4),
                                     quant_us=round(tq * 1e6, 3),
                                     prequantized_us=round(tp * 1e6, 3),
+                                    mxfp4_out_us=round(tf4 * 1e6, 3),
                                     tflops=round(2 * M * N * K / tl / 1e12, 2)))
     head_rows = [r for r in decode_rows if r["M"] in HEADLINE_M]
     dom_bytes = sum(gemm_bytes(r["M"], r["N"], r["K"], True) for r in head_rows)
@@ -422,14 +428,21 @@ def main():
                 out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 cps = weights[(N, K)][:4]
                 t = gemm_only_time(M, N, K, q, s, None, out, cps, reps_target=40)
+                oq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+                osc = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+                tf4 = per_launch_time(lambda i: mx.mxfp4_gemm_a4w4_mxfp4_out(
+                    q, s, cps[i].w_pre, cps[i].ws_pre, M, N, K, None, out_fp4=oq, out_scales=osc),
+                    len(cps), 40)
                 tq = quant_time(x, q, s, reps_target=64)
                 fl = 2 * M * N * K
                 prefill_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 2),
                                          tflops=round(fl / t / 1e12, 1),
                                          fp4_peak_frac=round(fl / t / PEAK_FP4, 4),
                                          quant_us=round(tq * 1e6, 2),
+                                         mxfp4_out_us=round(tf4 * 1e6, 2),
+                                         mxfp4_out_tflops=round(fl / tf4 / 1e12, 1),
                                          quant_GBps=round(quant_bytes(M, K) / tq / 1e9, 1)))
-                del x, q, s, out
+                del x, q, s, out, oq, osc
         torch.cuda.empty_cache()
     big = [r for r in prefill_rows if r["M"] >= 2048]
     prefill_summary = None

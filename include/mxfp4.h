@@ -181,6 +181,28 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * W4A4 GEMM with MXFP4 output for the next layer (the producer side of the
+ * prequantised input of P2 §2: the next layer's activations leave this
+ * GEMM already quantised, instead of as bf16 that a separate quantisation
+ * reads back).  The output row y = round_bf16(sum_k dq(A) dq(W) + bias) is
+ * quantised per 1x32 block along N exactly as mxfp4_quant_1x32 would
+ * quantise the bf16 output of mxfp4_gemm_a4w4 (bitwise the same bytes),
+ * inside the GEMM's epilogue.
+ *
+ *   a_fp4, a_scales, w_pre, ws_pre, bias: as for mxfp4_gemm_a4w4
+ *   out_fp4     packed FP4 [M, N/2], row stride ldq BYTES (N/2 <= ldq,
+ *               ldq % 4 == 0, 4-byte aligned)
+ *   out_scales  E8M0 [M, N/32], row stride lds BYTES (N/32 <= lds)
+ *   (ldq, lds < 2^23); the ROWMAJOR form mxfp4_linear_prequantized reads.
+ *   M >= 0 (M == 0 enqueues nothing), N >= 32, N % 32 == 0, K > 0,
+ *   K % 32 == 0; workspace as for mxfp4_gemm_a4w4.
+ */
+int mxfp4_gemm_a4w4_mxfp4_out(const void* a_fp4, const void* a_scales, const void* w_pre,
+                              const void* ws_pre, const void* bias, void* out_fp4, int64_t ldq,
+                              void* out_scales, int64_t lds, int64_t M, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Scale re-layout for activations quantised elsewhere (P2 §2: a fused
  * producer hands over (packed FP4, row-major E8M0 scales); the scales are
  * swizzled into the GEMM's order and padded with E8M0 1.0 before the GEMM).

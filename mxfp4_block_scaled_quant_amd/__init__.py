@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
 * :func:`mxfp4_gemm_a4w4` -- W4A4 GEMM with optional bias, bf16/fp32 out
 * :func:`mxfp4_linear` -- bf16 activations -> quant + GEMM (+ bias) in one call,
   the quantisation fused into the GEMM kernel for M <= 16
+* :func:`mxfp4_gemm_a4w4_mxfp4_out` -- the GEMM writing MXFP4 (row-major FP4 +
+  E8M0) for the next layer
 * :func:`mxfp4_shuffle_scales` -- row-major E8M0 scales -> the GEMM scale layout
 * :func:`mxfp4_linear_prequantized` -- the linear from row-major packed FP4 +
   scales handed over by a producer
@@ -62,6 +64,8 @@ _SIGNATURES = {
     "mxfp4_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_linear": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
                               _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
+    "mxfp4_gemm_a4w4_mxfp4_out": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp,
+                                           _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
     "mxfp4_shuffle_scales": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
     "mxfp4_linear_prequantized_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_linear_prequantized": (_c_int, [_c_vp, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp, _c_vp,
@@ -228,6 +232,32 @@ def mxfp4_linear(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: 
         _ptr(x), x.stride(0), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0),
         code, M, N, K, _ptr(workspace), ws_bytes, _stream(x.device)))
     return out
+
+
+def mxfp4_gemm_a4w4_mxfp4_out(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre: torch.Tensor,
+                              ws_pre: torch.Tensor, M: int, N: int, K: int,
+                              bias: Optional[torch.Tensor] = None,
+                              out_fp4: Optional[torch.Tensor] = None,
+                              out_scales: Optional[torch.Tensor] = None):
+    """(q [M, N/2], scales [M, N/32]) uint8: the GEMM's rows quantised per 1x32
+    along N (bitwise mxfp4_quant_1x32 of the bf16 output, ROWMAJOR)."""
+    _require_cuda(a_fp4, "a_fp4")
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
+        raise ValueError("bias must be bf16 [N]")
+    if out_fp4 is None:
+        out_fp4 = torch.empty((M, N // 2), dtype=torch.uint8, device=a_fp4.device)
+    if out_scales is None:
+        out_scales = torch.empty((M, N // 32), dtype=torch.uint8, device=a_fp4.device)
+    for t, name in ((out_fp4, "out_fp4"), (out_scales, "out_scales")):
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D uint8 with unit stride along N")
+    ws_bytes = int(lib().mxfp4_gemm_workspace_bytes(M, N, K))
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_fp4.device) if ws_bytes else None
+    _check("mxfp4_gemm_a4w4_mxfp4_out", lib().mxfp4_gemm_a4w4_mxfp4_out(
+        _ptr(a_fp4), _ptr(a_scales), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out_fp4),
+        out_fp4.stride(0), _ptr(out_scales), out_scales.stride(0), M, N, K, _ptr(workspace),
+        ws_bytes, _stream(a_fp4.device)))
+    return out_fp4, out_scales
 
 
 def mxfp4_shuffle_scales(scales: torch.Tensor, rows: int, K: int,

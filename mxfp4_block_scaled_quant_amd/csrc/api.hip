@@ -189,6 +189,10 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   p.x_bytes = 0;
   p.a_rowmajor = 0;
   p.lda = p.lds = 0;
+  p.scales_vec = 0;
+  p.out_fp4 = 0;
+  p.out_scales = nullptr;
+  p.ldos = 0;
   int path = get_gemm_path_override();
   if (path == 0) path = M <= 64 ? 1 : 2;
   if (path == 1 && M > 64) path = 2;  // the decode kernel covers at most 64 rows
@@ -244,6 +248,10 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   p.Ns = (int)cdiv(N, 16);
   p.a_rowmajor = 0;
   p.lda = p.lds = 0;
+  p.scales_vec = 0;
+  p.out_fp4 = 0;
+  p.out_scales = nullptr;
+  p.ldos = 0;
   if (fused) {
     p.a = nullptr;
     p.as = nullptr;
@@ -263,6 +271,59 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   p.ldx = 0;
   p.x_bytes = 0;
   return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+}
+
+int mxfp4_gemm_a4w4_mxfp4_out(const void* a_fp4, const void* a_scales, const void* w_pre,
+                              const void* ws_pre, const void* bias, void* out_fp4, int64_t ldq,
+                              void* out_scales, int64_t lds, int64_t M, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N <= 0 || N % 32 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (ldq < N / 2 || lds < N / 32) return MXFP4_ERR_SHAPE;
+  // 256 output rows (one prefill tile) stay addressable by 32-bit offsets
+  if (ldq > kMaxBuf / 256 || lds > kMaxBuf / 256) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
+      gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (workspace_bytes < mxfp4_gemm_workspace_bytes(M, N, K)) return MXFP4_ERR_WORKSPACE;
+  if (M == 0) return MXFP4_OK;
+  if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out_fp4 || !out_scales) return MXFP4_ERR_NULL;
+  if (!aligned(a_fp4, 16) || !aligned(a_scales, 4) || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
+      !aligned(out_fp4, 4) || ldq % 4 || (bias && !aligned(bias, 2)))
+    return MXFP4_ERR_ALIGN;
+  int cus = 0;
+  int st = check_device(&cus);
+  if (st) return st;
+  GemmArgs p;
+  p.cus = cus;
+  p.a = (const uint8_t*)a_fp4;
+  p.as = (const uint8_t*)a_scales;
+  p.w = (const uint8_t*)w_pre;
+  p.ws = (const uint8_t*)ws_pre;
+  p.bias = (const uint16_t*)bias;
+  p.out = out_fp4;
+  p.ldo = ldq;
+  p.out_f32 = 0;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.Kt = (int)cdiv(K, 128);
+  p.G = (int)cdiv(p.Kt, 4);
+  p.Ns = (int)cdiv(N, 16);
+  p.x = nullptr;
+  p.ldx = 0;
+  p.x_bytes = 0;
+  p.a_rowmajor = 0;
+  p.lda = p.lds = 0;
+  p.scales_vec = 0;
+  p.out_fp4 = 1;
+  p.out_scales = (uint8_t*)out_scales;
+  p.ldos = lds;
+  int path = get_gemm_path_override();
+  if (path == 0) path = M <= 64 ? 1 : 2;
+  if (path == 1 && M > 64) path = 2;
+  hipStream_t s = (hipStream_t)stream;
+  return launched(path == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
 }
 
 int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t K, void* out,
@@ -328,6 +389,9 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   p.x = nullptr;
   p.ldx = 0;
   p.x_bytes = 0;
+  p.out_fp4 = 0;
+  p.out_scales = nullptr;
+  p.ldos = 0;
   if (M <= 64) {
     // the small-M kernel gathers the row-major operands itself: one launch
     p.a = (const uint8_t*)x_fp4;
@@ -335,6 +399,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
     p.a_rowmajor = 1;
     p.lda = (uint32_t)ldq;
     p.lds = (uint32_t)lds;
+    p.scales_vec = lds % 16 == 0 && aligned(x_scales, 16) && (K / 32) % 16 == 0;
     return launched(launch_gemm_decode(p, s));
   }
   // larger M: permute into the GEMM layouts in the workspace, then the GEMM
@@ -346,6 +411,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   p.as = sc;
   p.a_rowmajor = 0;
   p.lda = p.lds = 0;
+  p.scales_vec = 0;
   return launched(launch_gemm_prefill(p, s));
 }
 

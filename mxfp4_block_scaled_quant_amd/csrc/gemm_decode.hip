@@ -78,6 +78,50 @@ __device__ __forceinline__ void reduce_store(v4f* red, const v4f (&acc)[MT][NS],
 // lds bytes) and are gathered into the same MFMA operands: lane l's 16 bytes
 // of row r, block kb are one contiguous piece of the row, and its scale
 // dword is assembled from the 4 K-steps' bytes.  Same values, same MFMAs.
+// MXFP4 output (two strips = 32 columns per workgroup, one 1x32 block per
+// row): the summed rows are rounded to bf16 into an LDS staging area, then
+// 4 threads per row each take 8 of the block's values, combine the block's
+// amax, and encode it like the quantisation kernels (scale byte from the
+// amax's exponent, scaled conversion): 4 code bytes per thread, the scale
+// byte from the first.  Bitwise the bf16 output quantised afterwards.
+template <int MT>
+__device__ __forceinline__ void reduce_store_fp4(v4f* red, const v4f (&acc)[MT][2], const GemmArgs& p, int s0) {
+  constexpr int NS = 2;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int KW = blockDim.x >> 6;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) red[(wv * MT * NS + i * NS + j) * 64 + lane] = acc[i][j];
+  __syncthreads();
+  uint16_t* stg = reinterpret_cast<uint16_t*>(red + KW * MT * NS * 64);  // [MT*16][32] bf16
+  constexpr int TOTAL = MT * NS * 64 * 4;
+  for (int idx = threadIdx.x; idx < TOTAL; idx += blockDim.x) {
+    const int l = idx & 63;
+    const int reg = (idx >> 6) & 3;
+    const int tile = idx >> 8;
+    const int i = tile / NS, j = tile % NS;
+    float v = 0.f;
+    for (int w = 0; w < KW; ++w) v += red[(w * MT * NS + tile) * 64 + l][reg];
+    const int m = i * 16 + 4 * (l >> 4) + reg;
+    const int n = (s0 + j) * 16 + (l & 15);
+    if (p.bias && n < p.N) v += bf16_to_f32(p.bias[n]);
+    stg[m * 32 + j * 16 + (l & 15)] = f32_to_bf16_rne(v);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MT * 64; idx += blockDim.x) {
+    const int m = idx >> 2, piece = idx & 3;
+    const int4 v = *reinterpret_cast<const int4*>(stg + m * 32 + piece * 8);
+    const uint32_t b = e8m0_of_amax_bits(quad_amax_bits((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w));
+    const uint32_t code = e2m1_pack8((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w, e8m0_value(b));
+    if (m < p.M && s0 * 16 < p.N) {
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.out) + (int64_t)m * p.ldo + s0 * 8 + piece * 4) = code;
+      if (piece == 0) p.out_scales[(int64_t)m * p.ldos + (s0 >> 1)] = (uint8_t)b;
+    }
+  }
+}
+
 template <int MT, int NS, int GPR, int MAXW, bool AROW>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int gpw) {
   extern __shared__ v4f red[];  // [KW][MT * NS][64]
@@ -131,11 +175,21 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
           const int row = i * 16 + (lane & 15);
           const bool ok = gv && row < p.M;
           uint32_t word = 0;
+          if (p.scales_vec) {
+            // the group's 16 scale bytes of the row in one load (whole
+            // groups: K % 512 == 0); this lane's block kb is byte kb of
+            // each dword
+            const int4 v = buf_load16(ras, ok ? (uint32_t)row * p.lds + (uint32_t)(g * 16) : kOOB);
+            const uint32_t sh = (uint32_t)(lane >> 4) * 8u;
+            word = ((uint32_t)v.x >> sh & 0xFFu) | ((uint32_t)v.y >> sh & 0xFFu) << 8 |
+                   ((uint32_t)v.z >> sh & 0xFFu) << 16 | ((uint32_t)v.w >> sh & 0xFFu) << 24;
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int c = (g * 4 + j) * 4 + (lane >> 4);
-            const uint32_t off = (ok && c < nblk) ? (uint32_t)row * p.lds + (uint32_t)c : kOOB;
-            word |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, off, 0, 0) << (8 * j);
+            for (int j = 0; j < 4; ++j) {
+              const int c = (g * 4 + j) * 4 + (lane >> 4);
+              const uint32_t off = (ok && c < nblk) ? (uint32_t)row * p.lds + (uint32_t)c : kOOB;
+              word |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, off, 0, 0) << (8 * j);
+            }
           }
           sa[q][i] = word;
         } else {
@@ -181,6 +235,12 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         }
   }
 
+  if constexpr (NS == 2) {
+    if (p.out_fp4) {
+      reduce_store_fp4<MT>(red, acc, p, s0);
+      return;
+    }
+  }
   reduce_store<MT, NS>(red, acc, p, s0);
 }
 
@@ -307,7 +367,8 @@ __global__ __launch_bounds__(64 * MAXW) void linear_decode_kernel(GemmArgs p, in
 template <int MT, int NS, int GPR, int MAXW>
 static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_t stream) {
   const dim3 grid((unsigned)((p.Ns + NS - 1) / NS));
-  const size_t lds = (size_t)kw * MT * NS * 64 * sizeof(v4f);
+  // partial tiles, plus the bf16 staging rows of the MXFP4 output
+  const size_t lds = (size_t)kw * MT * NS * 64 * sizeof(v4f) + (p.out_fp4 ? (size_t)MT * 16 * 32 * 2 : 0);
   if (p.a_rowmajor)
     gemm_decode_kernel<MT, NS, GPR, MAXW, true><<<grid, 64 * kw, lds, stream>>>(p, gpw);
   else
@@ -326,7 +387,7 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   constexpr int MAXW = MT <= 2 ? 16 : 8;
   const int gpw = (p.G + MAXW - 1) / MAXW;
   const int kw = (p.G + gpw - 1) / gpw;
-  const bool one_strip = p.Ns >= 1024 && p.M <= 8;
+  const bool one_strip = p.Ns >= 1024 && p.M <= 8 && !p.out_fp4;  // MXFP4 output: 32 columns per workgroup
   if constexpr (MT == 1) {
     if (gpw >= 2)
       return one_strip ? launch_decode_t<MT, 1, 2, MAXW>(p, kw, gpw, stream)

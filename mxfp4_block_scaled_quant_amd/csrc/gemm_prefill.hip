@@ -397,10 +397,12 @@ __device__ __forceinline__ void main_step(const GemmArgs& p, Pipe& P, v4i (&bf_c
 // epilogue waits for them instead.
 template <int MODE>
 struct OutMode {
-  static constexpr bool kF32 = MODE >= 2;
-  static constexpr bool kStaged = MODE == 0;
+  static constexpr bool kF32 = MODE == 2 || MODE == 3;
+  static constexpr bool kFp4 = MODE == 4;
+  static constexpr bool kStaged = MODE == 0 || MODE == 4;
   static constexpr bool kVec = MODE == 2;
-  static constexpr int kStores = kStaged ? 2 * kWM : kVec ? kWM * kWN : 4 * kWM * kWN;
+  // per 16-row block: 2 row-piece stores (bf16), or 2 code + 2 scale stores (MXFP4)
+  static constexpr int kStores = MODE == 0 ? 2 * kWM : kFp4 ? 4 * kWM : kVec ? kWM * kWN : 4 * kWM * kWN;
   static constexpr bool kDrain = !kStaged && !kVec;
   static constexpr int kInFlight = kDrain ? 0 : kStores;  // stores the next tile's waits count
   static constexpr bool kBiasLds = !kDrain;  // bias staged in LDS (whole pairs: N % 4 == 0)
@@ -460,6 +462,65 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& p, const Tile& t
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (int64_t)rb * p.ldo * 2, (uint32_t)(nrows * p.ldo * 2));
     __builtin_amdgcn_raw_buffer_store_b128(r0, ro, voff0, 0, MXFP4_STORE_AUX);
     __builtin_amdgcn_raw_buffer_store_b128(r1, ro, voff1, 0, MXFP4_STORE_AUX);
+  }
+}
+
+// MXFP4 epilogue (mode 4): as mode 0 up to the row pieces read back from the
+// staging rows.  A lane then holds 8 consecutive bf16 values of a row, and
+// the 4 lanes of a quad hold one 1x32 block along N: the block's amax is
+// combined by two quad permutes, the scale byte taken from its exponent and
+// the 8 values encoded by the scaled conversion, as in the quantisation
+// kernels.  Each lane stores its 4 code bytes, the quad's first lane the
+// scale byte (the other lanes' scale stores go to an out-of-range offset, so
+// every store is issued and the waits' counts stay exact).
+__device__ __forceinline__ void epilogue_fp4(const GemmArgs& p, const Tile& tl, v4f (&acc)[kWM][kWN], int wv,
+                                             int wm, int wn) {
+  const int lane = (int)lane_here();
+  const int row0 = tl.ms * 16 + wm * 128;
+  const int n = (tl.s0 + wn * kWN) * 16 + (lane & 7) * 8;  // this lane's 8 columns
+  v2i bl[kWN];
+  read_bias(bl, wv, lane);
+  const uint32_t wst = kEpiLds + (uint32_t)wv * 16 * kEpiRowB;
+  const uint32_t waddr = wst + (uint32_t)(lane & 15) * kEpiRowB + (uint32_t)(lane >> 4) * 8;
+  const uint32_t raddr = wst + (uint32_t)(lane >> 3) * kEpiRowB + (uint32_t)(lane & 7) * 16;
+  const uint32_t ldq = (uint32_t)p.ldo, lds = (uint32_t)p.ldos;
+  const uint32_t doff0 = n < p.N ? (uint32_t)(lane >> 3) * ldq + (uint32_t)(n >> 1) : kOOB;
+  const uint32_t doff1 = n < p.N ? doff0 + 8 * ldq : kOOB;
+  const bool first = (lane & 3) == 0;
+  const uint32_t soff0 = (n < p.N && first) ? (uint32_t)(lane >> 3) * lds + (uint32_t)(n >> 5) : kOOB;
+  const uint32_t soff1 = (n < p.N && first) ? soff0 + 8 * lds : kOOB;
+  uint8_t* const out = reinterpret_cast<uint8_t*>(p.out);
+#pragma unroll
+  for (int i = 0; i < kWM; ++i) {
+#pragma unroll
+    for (int j = 0; j < kWN; ++j) {
+      const float b0 = __uint_as_float((uint32_t)bl[j].x << 16), b1 = __uint_as_float((uint32_t)bl[j].x & 0xFFFF0000u);
+      const float b2 = __uint_as_float((uint32_t)bl[j].y << 16), b3 = __uint_as_float((uint32_t)bl[j].y & 0xFFFF0000u);
+      const uint32_t lo = pack_bf16x2(acc[i][j][0] + b0, acc[i][j][1] + b1);
+      const uint32_t hi = pack_bf16x2(acc[i][j][2] + b2, acc[i][j][3] + b3);
+      const v2i d = {(int)lo, (int)hi};
+      if (j == 0) ds_write8<0>(waddr, d);
+      if (j == 1) ds_write8<32>(waddr, d);
+      if (j == 2) ds_write8<64>(waddr, d);
+      if (j == 3) ds_write8<96>(waddr, d);
+    }
+    v4i r0, r1;
+    ds_read16<0>(r0, raddr);
+    ds_read16<8 * kEpiRowB>(r1, raddr);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1));
+    const uint32_t b0 = e8m0_of_amax_bits(quad_amax_bits((uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w));
+    const uint32_t b1 = e8m0_of_amax_bits(quad_amax_bits((uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w));
+    const uint32_t c0 = e2m1_pack8((uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w, e8m0_value(b0));
+    const uint32_t c1 = e2m1_pack8((uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w, e8m0_value(b1));
+    const int rb = row0 + i * 16;
+    // (uniform: see epilogue_staged)
+    const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, p.M - rb)));
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(out + (int64_t)rb * p.ldo, (uint32_t)nrows * ldq);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.out_scales + (int64_t)rb * p.ldos, (uint32_t)nrows * lds);
+    __builtin_amdgcn_raw_buffer_store_b32(c0, rd, doff0, 0, MXFP4_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b32(c1, rd, doff1, 0, MXFP4_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b0, rs, soff0, 0, MXFP4_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b1, rs, soff1, 0, MXFP4_STORE_AUX);
   }
 }
 
@@ -616,7 +677,9 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int ti
 
   for (int k = 0;;) {
     for (int g = 0; g < G; ++g) group_body<kStores, kBiasLds>(p, P, c, cn, g, wv, wm, wn, ra, lane16);
-    if (OutMode<MODE>::kStaged)
+    if (OutMode<MODE>::kFp4)
+      epilogue_fp4(p, c, P.acc, wv, wm, wn);
+    else if (OutMode<MODE>::kStaged)
       epilogue_staged(p, c, P.acc, wv, wm, wn);
     else
       epilogue<MODE>(p, c, P.acc, wv, wm, wn);
@@ -638,13 +701,15 @@ hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream) {
   const int ntiles = tiles_m * tiles_n;
   const int grid = ntiles < p.cus ? ntiles : p.cus;
   const bool a16 = ((uintptr_t)p.out & 15) == 0;
-  const int mode = p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
+  const int mode = p.out_fp4 ? 4
+                 : p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
                              : ((p.N % 8 == 0 && p.ldo % 8 == 0 && a16) ? 0 : 1);
   const dim3 g((unsigned)grid), b(64 * kWaves);
   switch (mode) {
     case 0: gemm_prefill_kernel<0><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
     case 1: gemm_prefill_kernel<1><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
     case 2: gemm_prefill_kernel<2><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
+    case 4: gemm_prefill_kernel<4><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
     default: gemm_prefill_kernel<3><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
   }
   return hipGetLastError();

@@ -102,6 +102,17 @@ __device__ __forceinline__ uint32_t e2m1_pack8(uint32_t w0, uint32_t w1, uint32_
   return r;
 }
 
+// The largest |bf16| bit pattern of a block held as 8 values by each of
+// the 4 lanes of a quad (lanes 4q..4q+3), in every lane of the quad: a
+// packed max over the lane's dwords, then two quad permutes (DPP, no LDS).
+__device__ __forceinline__ uint32_t quad_amax_bits(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  uint32_t m = absmax_pairs(absmax_pairs(absmax_pairs(absmax_pairs(0u, w0), w1), w2), w3);
+  uint32_t a = max(m & 0xFFFFu, m >> 16);
+  a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0xB1, 0xF, 0xF, true));  // lane ^ 1
+  a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xF, 0xF, true));  // lane ^ 2
+  return a;
+}
+
 // A whole 1x32 block held by one lane (four 16-byte pieces in element order)
 // -> its 16 code bytes (the lane's operand of the block-scaled FP4 MFMA) and
 // its scale byte.

@@ -29,6 +29,12 @@ struct GemmArgs {
   // with row stride lda bytes, as [M, K/32] with row stride lds bytes.
   int a_rowmajor;
   uint32_t lda, lds;
+  int scales_vec;  // row-major scales: lds % 16 == 0, 16-byte aligned, K % 512 == 0
+  // MXFP4 output (out_fp4 != 0): out is packed FP4 [M, N/2] with row stride
+  // ldo BYTES, out_scales E8M0 [M, N/32] with row stride ldos bytes.
+  int out_fp4;
+  uint8_t* out_scales;
+  int64_t ldos;
 };
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);

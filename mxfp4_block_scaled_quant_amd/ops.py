@@ -11,6 +11,8 @@ queries, and works with symbolic sizes.
     torch.ops.mxfp4.preshuffle_weight(w_fp4, w_scales, N, K, batch) -> (w_pre, ws_pre)
     torch.ops.mxfp4.gemm_a4w4(a, a_scales, w_pre, ws_pre, M, N, K, bias, out_dtype) -> [M, N]
     torch.ops.mxfp4.linear(x, w_pre, ws_pre, N, bias, out_dtype) -> [M, N]
+    torch.ops.mxfp4.gemm_a4w4_mxfp4_out(a, a_scales, w_pre, ws_pre, M, N, K, bias)
+        -> (q [M, N/2], scales [M, N/32])
     torch.ops.mxfp4.shuffle_scales(scales, rows, K) -> GEMM-layout scales
     torch.ops.mxfp4.linear_prequantized(x_fp4, x_scales, w_pre, ws_pre, N, bias,
         out_dtype) -> [M, N]
@@ -29,7 +31,7 @@ import torch
 from torch import Tensor
 
 from . import (MXFP4_LAYOUT_GEMM, MXFP4_LAYOUT_ROWMAJOR, a16wfp4_bmm, mxfp4_gemm_a4w4,
-               mxfp4_linear, mxfp4_linear_prequantized, mxfp4_preshuffle_weight,
+               mxfp4_gemm_a4w4_mxfp4_out, mxfp4_linear, mxfp4_linear_prequantized, mxfp4_preshuffle_weight,
                mxfp4_quant_1x32, mxfp4_shuffle_scales)
 
 __all__ = ["gemm_data_bytes", "gemm_scale_bytes"]
@@ -103,6 +105,18 @@ def linear(x: Tensor, w_pre: Tensor, ws_pre: Tensor, N: int, bias: Optional[Tens
 @linear.register_fake
 def _(x, w_pre, ws_pre, N, bias=None, out_dtype=torch.bfloat16):
     return x.new_empty((x.shape[0], N), dtype=out_dtype)
+
+
+@torch.library.custom_op("mxfp4::gemm_a4w4_mxfp4_out", mutates_args=())
+def gemm_a4w4_mxfp4_out(a: Tensor, a_scales: Tensor, w_pre: Tensor, ws_pre: Tensor, M: int,
+                        N: int, K: int, bias: Optional[Tensor] = None) -> Tuple[Tensor, Tensor]:
+    q, s = mxfp4_gemm_a4w4_mxfp4_out(a, a_scales, w_pre, ws_pre, M, N, K, bias)
+    return q, s
+
+
+@gemm_a4w4_mxfp4_out.register_fake
+def _(a, a_scales, w_pre, ws_pre, M, N, K, bias=None):
+    return (a.new_empty((M, N // 2), dtype=torch.uint8), a.new_empty((M, N // 32), dtype=torch.uint8))
 
 
 @torch.library.custom_op("mxfp4::shuffle_scales", mutates_args=())

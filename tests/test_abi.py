@@ -146,6 +146,22 @@ def test_linear_validation(lib):
     assert call(M=0, x=None) == 0
 
 
+def test_mxfp4_out_validation(lib):
+    f = lib.mxfp4_gemm_a4w4_mxfp4_out
+
+    def call(a=P, as_=P, w=P, ws=P, bias=None, q=P, ldq=16, s=P, lds=1, M=4, N=32, K=64):
+        return f(a, as_, w, ws, bias, q, ldq, s, lds, M, N, K, None, 0, None)
+
+    assert call(N=48) == 2            # N % 32
+    assert call(ldq=8) == 2           # ldq < N/2
+    assert call(lds=0) == 2           # lds < N/32
+    assert call(ldq=1 << 23) == 2
+    assert call(s=None) == 1
+    assert call(ldq=18) == 3          # ldq % 4
+    assert call(q=P_ODD.value + 2) == 3
+    assert call(M=0, a=None) == 0
+
+
 def test_shuffle_scales_and_prequantized_validation(lib):
     f = lib.mxfp4_shuffle_scales
     assert f(P, 4, 8, 100, P, None) == 2        # K % 32

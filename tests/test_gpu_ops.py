@@ -38,6 +38,7 @@ def test_opcheck_every_op():
         (torch.ops.mxfp4.linear.default, (x[:1], W.w_pre, W.ws_pre, N, None, torch.float32)),
         (torch.ops.mxfp4.a16wfp4_bmm.default, (xb, Wb.w_pre, Wb.ws_pre, 64, True, torch.bfloat16)),
         (torch.ops.mxfp4.shuffle_scales.default, (sr.reshape(M, K // 32), M, K)),
+        (torch.ops.mxfp4.gemm_a4w4_mxfp4_out.default, (q, s, W.w_pre, W.ws_pre, M, 64, K, None)),
         (torch.ops.mxfp4.linear_prequantized.default,
          (qr, sr.reshape(M, K // 32), W.w_pre, W.ws_pre, N, b, torch.float32)),
         (torch.ops.mxfp4.linear_prequantized.default,

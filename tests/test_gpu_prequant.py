@@ -44,7 +44,10 @@ def test_shuffle_scales_bit_exact(rows, K, pad):
 
 CASES = [
     # name, M, N, K, kwargs, (ldq pad, lds pad)
-    ("m1_1024x5120", 1, 1024, 5120, dict(seed=0, outliers=True), (0, 0)),
+    ("m1_1024x5120", 1, 1024, 5120, dict(seed=0, outliers=True), (0, 0)),         # 16-byte scale loads
+    ("m16_1024x5120", 16, 1024, 5120, dict(seed=1, outliers=True, with_bias=True), (16, 16)),
+    ("m37_300x2048_lds8", 37, 300, 2048, dict(seed=2), (0, 8)),                   # byte loads (lds % 16)
+    ("m64_96x2048_lds16", 64, 96, 2048, dict(seed=3, with_bias=True), (32, 16)),
     ("m5_17x96", 5, 17, 96, dict(seed=9, with_bias=True), (16, 1)),
     ("m16_520x1056_bias", 16, 520, 1056, dict(seed=6, outliers=True, with_bias=True), (0, 0)),
     ("m37_96x4128_edge", 37, 96, 4128, dict(seed=5, edge=True, with_bias=True), (32, 5)),
