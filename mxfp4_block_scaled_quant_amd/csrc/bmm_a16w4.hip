@@ -13,9 +13,10 @@
 //
 // Two kernels.  The streaming kernel (shapes whose weight slice fits in
 // registers, which covers the MLA K-up 512 x 192 and V-up 256 x 512 heads):
-// a 512-thread workgroup owns one head and a run of 16-row m-tiles; each of
-// its 8 waves dequantises its 1/8 of the head's output columns once into
-// registers (bf16 MFMA fragments), and the activation m-tiles stream through
+// a 512-thread workgroup owns one head (for M <= 64 one 128-column block of
+// it) and a run of 16-row m-tiles; each of its 8 waves dequantises its 1/8
+// of the workgroup's output columns once into registers (bf16 MFMA
+// fragments), and the activation m-tiles stream through
 // LDS stages by buffer->LDS loads (in the MFMA's lane order), one barrier
 // per m-tile, so activations are read from HBM once, weights once per
 // workgroup, and output written once.  Waves 0-3 issue all activation loads
@@ -338,10 +339,12 @@ __device__ __forceinline__ void stage_store(const BmmArgs& p, int b, int mt, int
 }  // namespace
 
 // KF: maximum K-fragments (K/32) held per column tile; NT: 16-column tiles
-// per wave.  Grid: B heads x S workgroups per head; workgroup s of head b
-// takes m-tiles [s*T, min((s+1)*T, nmt)).
+// per wave.  Grid: B heads x S workgroups per head x NB column blocks;
+// workgroup (b, s, nb) takes m-tiles [s*T, min((s+1)*T, nmt)) and the
+// 8*NT column tiles from 8*NT*nb (NB > 1 when there are few m-tiles: more
+// workgroups, each with a smaller weight slice to load and dequantise).
 template <int KF, int NT, bool F32, bool VEC>
-__global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, int T) {
+__global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, int T, int NB) {
   constexpr int KD = (KF + 3) / 4;  // loads per loading wave per m-tile
   constexpr int esz = F32 ? 4 : 2;
   using L = BmmLds<KF, NT, esz>;
@@ -355,8 +358,10 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
   const uint32_t lane = lane_here();
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool loader = wv < 4;
-  const int b = blockIdx.x / S;
-  const int s = blockIdx.x % S;
+  const int nb = blockIdx.x % NB;
+  const int b = (blockIdx.x / NB) / S;
+  const int s = (blockIdx.x / NB) % S;
+  const int cb = nb * kWavesS * NT;  // first column tile of this workgroup
   const int kf = p.K >> 5;
   const int nmt = (p.M + 15) >> 4;
   const int mt0 = s * T;
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
 
   // Weights of this wave's column tiles, loaded first (their wait then does
   // not cover the activation loads issued after them).
-  const int s0 = wv * NT;  // first 16-column strip
+  const int s0 = cb + wv * NT;  // first 16-column strip
   const uint32_t q = lane >> 4, r = lane & 15u;
   const auto rw = make_rsrc(p.w + (int64_t)b * p.Ns * p.Kt * 1024, (uint32_t)p.Ns * p.Kt * 1024u);
   const auto rs = make_rsrc(p.ws + (int64_t)b * p.Ns * p.G * 256, (uint32_t)p.Ns * p.G * 256u);
@@ -426,8 +431,8 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
     } else if (i > 0) {
       // Storing waves: m-tile i-1 of source waves wv-4 and wv.
       const uint32_t buf = (uint32_t)((i - 1) & 1) * L::kStgBuf;
-      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, (wv - 4) * NT, slot + buf - 4 * L::kBlock, lane);
-      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, wv * NT, slot + buf, lane);
+      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, cb + (wv - 4) * NT, slot + buf - 4 * L::kBlock, lane);
+      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, cb + wv * NT, slot + buf, lane);
     }
     // PA partial sums per column tile (fragment c adds into part c % PA), so
     // several independent accumulation chains keep the MFMA pipe busy; the
@@ -476,8 +481,8 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
   barrier_nofence();
   if (!loader && cnt > 0) {
     const uint32_t buf = (uint32_t)((cnt - 1) & 1) * L::kStgBuf;
-    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, (wv - 4) * NT, slot + buf - 4 * L::kBlock, lane);
-    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, wv * NT, slot + buf, lane);
+    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, cb + (wv - 4) * NT, slot + buf - 4 * L::kBlock, lane);
+    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, cb + wv * NT, slot + buf, lane);
   }
   // Loads issued past the last m-tile (empty descriptors) still write LDS:
   // let them finish before the workgroup ends.
@@ -510,15 +515,23 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
   const int nt = (p.Ns + kWavesS - 1) / kWavesS;
   const int esz = out_f32 ? 4 : 2;
   const bool offsets_ok = (15 * som + N) * esz <= 0x7FFFFFFF && (15 * sxm + K) * 2 <= 0x7FFFFFFF;
-  int cfg = 0;
+  const int nmt = (int)((M + 15) / 16);
+  // Few m-tiles (M <= 64): one column tile per wave and the head's columns
+  // split over NB workgroups (the activations, small here, are read once per
+  // block).  Measured on MI355X: M = 1 K-up 5.8 -> 3.6 us, V-up 7.4 -> 5.5 us;
+  // slower from 16 m-tiles on.
+  const bool small = nmt <= 4;
+  int cfg = 0, NB = 1;
   if (offsets_ok) {
-    if (nt <= 4 && kf == 6) cfg = 4;  // MLA K-up heads (K = 192)
+    if (small && kf <= 32) {
+      cfg = kf == 6 ? 5 : kf <= 8 ? 6 : kf <= 16 ? 7 : 3;
+      NB = (p.Ns + kWavesS - 1) / kWavesS;
+    } else if (nt <= 4 && kf == 6) cfg = 4;  // MLA K-up heads (K = 192)
     else if (nt <= 4 && kf <= 8) cfg = 1;
     else if (nt <= 2 && kf <= 16) cfg = 2;
     else if (nt <= 1 && kf <= 32) cfg = 3;
   }
   if (cfg) {
-    const int nmt = (int)((M + 15) / 16);
     // Workgroups per head: enough to fill the device, each with whole m-tiles.
     int S = (int)((cus + B - 1) / B);
     if (S > nmt) S = nmt;
@@ -528,17 +541,20 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
     // vector mode: whole 16-byte pieces of output rows
     const int per = 16 / esz;
     const bool vec = N % per == 0 && som % per == 0 && sob % per == 0 && ((uintptr_t)out & 15) == 0;
-    const dim3 grid((unsigned)(B * S)), block(64 * kWavesS);
-#define MXFP4_BMM_LAUNCH(KF_, NT_)                                                                   \
-  do {                                                                                               \
-    if (out_f32 && vec) bmm_stream_kernel<KF_, NT_, true, true><<<grid, block, 0, stream>>>(p, S, T); \
-    else if (out_f32) bmm_stream_kernel<KF_, NT_, true, false><<<grid, block, 0, stream>>>(p, S, T);  \
-    else if (vec) bmm_stream_kernel<KF_, NT_, false, true><<<grid, block, 0, stream>>>(p, S, T);      \
-    else bmm_stream_kernel<KF_, NT_, false, false><<<grid, block, 0, stream>>>(p, S, T);              \
+    const dim3 grid((unsigned)(B * S * NB)), block(64 * kWavesS);
+#define MXFP4_BMM_LAUNCH(KF_, NT_)                                                                        \
+  do {                                                                                                    \
+    if (out_f32 && vec) bmm_stream_kernel<KF_, NT_, true, true><<<grid, block, 0, stream>>>(p, S, T, NB); \
+    else if (out_f32) bmm_stream_kernel<KF_, NT_, true, false><<<grid, block, 0, stream>>>(p, S, T, NB);  \
+    else if (vec) bmm_stream_kernel<KF_, NT_, false, true><<<grid, block, 0, stream>>>(p, S, T, NB);      \
+    else bmm_stream_kernel<KF_, NT_, false, false><<<grid, block, 0, stream>>>(p, S, T, NB);              \
   } while (0)
     if (cfg == 4) MXFP4_BMM_LAUNCH(6, 4);
     else if (cfg == 1) MXFP4_BMM_LAUNCH(8, 4);
     else if (cfg == 2) MXFP4_BMM_LAUNCH(16, 2);
+    else if (cfg == 5) MXFP4_BMM_LAUNCH(6, 1);
+    else if (cfg == 6) MXFP4_BMM_LAUNCH(8, 1);
+    else if (cfg == 7) MXFP4_BMM_LAUNCH(16, 1);
     else MXFP4_BMM_LAUNCH(32, 1);
 #undef MXFP4_BMM_LAUNCH
     return hipGetLastError();

@@ -49,6 +49,8 @@ CASES = [
     ("vup_M64", 16, 64, 256, 512, True),
     ("vup_M256", 16, 256, 256, 512, True),
     ("ragged_3x37x96x160", 3, 37, 96, 160, False),
+    ("colblocks_2x20x200x256", 2, 20, 200, 256, True),      # two column blocks, the last ragged
+    ("colblocks_5x3x392x512", 5, 3, 392, 512, False),
     ("ragged_2x70x30x4128", 2, 70, 30, 4128, True),
 ]
 
