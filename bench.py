@@ -319,7 +319,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the W4A4 linear and the BMM run on a single MI355X "
-              "and this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+              "and the library has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
     import mxfp4_block_scaled_quant_amd as mx
