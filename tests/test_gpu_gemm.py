@@ -180,3 +180,37 @@ def test_gemm_weight_scales_exact(path, K):
         assert np.array_equal(y32.cpu().numpy(), dq.T.astype(np.float32))      # -0.0 == 0.0, inf == inf
     unsigned_zero = lambda b: np.where((b & 0x7FFF) == 0, 0, b)
     assert np.array_equal(unsigned_zero(host_bf16_bits(y16)), unsigned_zero(F.f64_to_bf16(dq.T)))
+
+
+@pytest.mark.parametrize("path", [1, 2], ids=["smallM", "tiled"])
+@pytest.mark.parametrize("dtype,pad", [(torch.bfloat16, 8), (torch.bfloat16, 3), (torch.float32, 4),
+                                       (torch.float32, 1)],
+                         ids=["bf16_pad8", "bf16_pad3", "f32_pad4", "f32_pad1"])
+def test_gemm_strided_output(path, dtype, pad):
+    # out is a view with row stride N + pad inside a sentinel-filled buffer:
+    # every output mode (16-byte row pieces, single elements; bf16 / fp32)
+    # writes exactly the [M, N] window, bitwise as into a contiguous output.
+    need_gpu()
+    M = 37 if path == 1 else 300
+    N, K = 96, 4128
+    prob = inputs.linear_problem(M, N, K, 5, edge=True, with_bias=True)
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    b = dev_bf16(prob["bias"])
+    q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
+    buf = torch.full((M, N + pad), -7.0, dtype=dtype, device="cuda")
+    mx.set_gemm_path(path)
+    try:
+        ref = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, dtype)
+        mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, dtype, out=buf[:, :N])
+        lin = torch.full((M, N + pad), -7.0, dtype=dtype, device="cuda")
+        mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, dtype, out=lin[:, :N])
+    finally:
+        mx.set_gemm_path(0)
+    torch.cuda.synchronize()
+    iview = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(buf[:, :N].contiguous().view(iview), ref.view(iview))
+    assert torch.all(buf[:, N:] == -7.0)
+    assert torch.all(lin[:, N:] == -7.0)
+    _check(prob, mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, torch.float32).cpu().numpy(),
+           host_bf16_bits(lin[:, :N].contiguous().to(torch.bfloat16)) if dtype == torch.bfloat16 else
+           host_bf16_bits(mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, torch.bfloat16)))
