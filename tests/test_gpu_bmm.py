@@ -120,3 +120,25 @@ def test_bmm_dequant_exact_every_scale():
     from oracle import formats as F
     unsigned_zero = lambda b: np.where((b & 0x7FFF) == 0, 0, b)
     assert np.array_equal(unsigned_zero(host_bf16_bits(y16)[0]), unsigned_zero(F.f64_to_bf16(dq.T)))
+
+
+@pytest.mark.parametrize("name,B,M,N,K", [("kup_M37", 16, 37, 512, 192), ("vup_M70", 16, 70, 256, 512),
+                                          ("small_M3", 4, 3, 200, 256)])
+def test_bmm_strided_activations_and_output(name, B, M, N, K):
+    # x as a view with padded rows and heads (sxm = K + 8, sxb = (M + 3) * sxm),
+    # out as a view with padded rows inside a sentinel buffer: bitwise the
+    # contiguous call, padding untouched.
+    need_gpu()
+    prob = inputs.bmm_problem(B, M, N, K, 7)
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    big = np.zeros((B, M + 3, K + 8), dtype=np.uint16)
+    big[:, :M, :K] = prob["x"]
+    xs = dev_bf16(big)[:, :M, :K]
+    ref = mx.a16wfp4_bmm(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, out_dtype=torch.float32)
+    ob = torch.full((B, M, N + 6), -7.0, dtype=torch.float32, device="cuda")   # row stride even (documented)
+    mx.a16wfp4_bmm(xs, W.w_pre, W.ws_pre, N, out=ob[:, :, :N], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(ob[:, :, :N].contiguous().view(torch.int32), ref.view(torch.int32))
+    assert torch.all(ob[:, :, N:] == -7.0)
+    y16 = mx.a16wfp4_bmm(xs, W.w_pre, W.ws_pre, N)
+    _check(prob, ref.cpu().numpy(), host_bf16_bits(y16))
