@@ -197,6 +197,23 @@ __device__ __forceinline__ void barrier_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// 4 x 4 transpose between a lane's four registers and the wave's four
+// 16-lane rows: afterwards register j of row q holds what register q of row j
+// held.  gfx950's lane-swap instructions: the 32-lane swap exchanges the upper
+// half of its first operand with the lower half of its second; the 16-lane
+// swap exchanges the odd rows of its first operand with the even rows of its
+// second.  Together they transpose the 2 x 2 blocks, then each block.
+__device__ __forceinline__ void transpose_rows4(uint32_t (&d)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  d[0] = c[0];
+  d[1] = c[1];
+  d[2] = e[0];
+  d[3] = e[1];
+}
+
 template <int OFF>
 __device__ __forceinline__ void ds_read16(v4i& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
@@ -371,21 +388,25 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
   // Weights of this wave's column tiles, loaded first (their wait then does
   // not cover the activation loads issued after them).
   const int s0 = cb + wv * NT;  // first 16-column strip
-  const uint32_t q = lane >> 4, r = lane & 15u;
+  const uint32_t r = lane & 15u;
   const auto rw = make_rsrc(p.w + (int64_t)b * p.Ns * p.Kt * 1024, (uint32_t)p.Ns * p.Kt * 1024u);
   const auto rs = make_rsrc(p.ws + (int64_t)b * p.Ns * p.G * 256, (uint32_t)p.Ns * p.G * 256u);
   // Scale dword (kb*16 + r) of group g holds the scales of K-fragments
   // c = 16g + kb + 4i, i = 0..3 (byte i): 4 dwords per 16 fragments.
   constexpr int KG = (KF + 15) / 16;  // scale groups
-  uint32_t wword[NT][KF], wsc[NT][KG * 4];
+  constexpr int KU = (KF + 3) / 4;    // 1 KiB weight units per column tile
+  int4 wunit[NT][KU];
+  uint32_t wsc[NT][KG * 4];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int st = s0 + j;
+    // Each 1 KiB unit (16 rows x 4 blocks) in one load, lane l taking slot
+    // l (block l/16 of row l%16: contiguous across the wave); transposed
+    // once loaded (below).  Units past K load zeros.
 #pragma unroll
-    for (int c = 0; c < KF; ++c) {
-      const int t = c >> 2, kb = c & 3;
-      const bool ok = st < p.Ns && c < kf;
-      wword[j][c] = buf_load4(rw, ok ? (uint32_t)((st * p.Kt + t) * 1024 + (kb * 16 + r) * 16 + q * 4) : kOOB);
+    for (int t = 0; t < KU; ++t) {
+      const bool ok = st < p.Ns && t * 4 < kf;
+      wunit[j][t] = buf_load16(rw, ok ? (uint32_t)((st * p.Kt + t) * 1024) + lane * 16u : kOOB);
     }
 #pragma unroll
     for (int g = 0; g < KG; ++g)
@@ -402,6 +423,22 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
     for (int x = 0; x < kStages - 1; ++x)
       issue_xtile<KD, KF, L::kStage, L::kTrash>(p, b, mt0 + x, x < cnt ? nmt : 0, x, kf, wv, lane);
   }
+
+  // Each unit transposed across the four 16-lane rows: lane (q, r) then
+  // holds dword q of each of the unit's four blocks of row r, its MFMA
+  // operand (blocks past K are zero in the preshuffled data).
+  uint32_t wword[NT][KF];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int t = 0; t < KU; ++t) {
+      uint32_t d[4] = {(uint32_t)wunit[j][t].x, (uint32_t)wunit[j][t].y, (uint32_t)wunit[j][t].z,
+                       (uint32_t)wunit[j][t].w};
+      transpose_rows4(d);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        if (t * 4 + kb < KF) wword[j][t * 4 + kb] = d[kb];
+    }
 
   // Dequantise the weights (exact).  An invalid fragment loaded zeros: code
   // 0 gives 0.  (One fragment at a time: the scheduling barriers keep the
