@@ -17,9 +17,10 @@
 // it) and a run of 16-row m-tiles; each of its 8 waves dequantises its 1/8
 // of the workgroup's output columns once into registers (bf16 MFMA
 // fragments), and the activation m-tiles stream through
-// LDS stages by buffer->LDS loads (in the MFMA's lane order), one barrier
-// per m-tile, so activations are read from HBM once, weights once per
-// workgroup, and output written once.  Waves 0-3 issue all activation loads
+// two LDS stages by buffer->LDS loads (in the MFMA's lane order: m-tile i+1
+// loads while m-tile i is computed), one barrier per m-tile, so activations
+// are read from HBM once, weights once per workgroup, and output written
+// once.  Waves 0-3 issue all activation loads
 // and waves 4-7 all output stores (through a double-buffered LDS staging
 // area, as whole 16-byte pieces of rows): a wave's memory counter retires
 // loads and stores in issue order, so a wave that both stores and waits
@@ -157,24 +158,26 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 constexpr int kWavesS = 8;
 
 // LDS of one instance (KF K-fragments, NT column tiles, output element
-// size ESZ): stages of KF KiB (fragment c of a stage at c KiB; as many as
-// fit, up to 8, so loads run far enough ahead of the m-tiles), a 1 KiB
+// size ESZ): two stages of KF KiB (fragment c of a stage at c KiB), a 1 KiB
 // target for padding loads, then two output staging buffers, each with a
 // 16-row block per wave (rows of NT*16 elements plus 16 bytes to spread
-// banks).
+// banks).  Two stages, not more: measured on MI355X, deeper rings (3 to 8
+// m-tiles, the loads issued further ahead) were slower at every MLA shape
+// (K-up / V-up, M = 4096: 20.7 / 21.4 us with two stages, 21.3 / 22.1 with
+// three, 22.7 / 25.8 with eight), since the larger start-up burst of every
+// workgroup delays its first m-tile; one m-tile of compute covers the next
+// one's load.
 template <int KF, int NT, int ESZ>
 struct BmmLds {
   static constexpr int kRowB = NT * 16 * ESZ;
   static constexpr int kRowStride = kRowB + 16;
   static constexpr int kBlock = 16 * kRowStride;         // one wave's staged block
   static constexpr int kStgBuf = kWavesS * kBlock;       // one staging buffer
-  static constexpr int kStageArea = 160 * 1024 - 1024 - 2 * kStgBuf;
   static constexpr int kStage = KF * 1024;
-  static constexpr int kStages = kStageArea / kStage < 8 ? kStageArea / kStage : 8;
+  static constexpr int kStages = 2;
   static constexpr int kTrash = kStages * kStage;
   static constexpr int kStg = kTrash + 1024;
   static constexpr int kBytes = kStg + 2 * kStgBuf;
-  static_assert(kStages >= 3, "LDS stages");
   static_assert(kBytes <= 160 * 1024, "LDS per workgroup");
 };
 
@@ -365,10 +368,8 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
   constexpr int KD = (KF + 3) / 4;  // loads per loading wave per m-tile
   constexpr int esz = F32 ? 4 : 2;
   using L = BmmLds<KF, NT, esz>;
-  // Stages in use: as many as LDS holds, with the loading waves' wait below
-  // within the counter's range (63).
-  constexpr int kVmStages = 2 + 63 / KD;
-  constexpr int kStages = L::kStages < kVmStages ? L::kStages : kVmStages;
+  constexpr int kStages = L::kStages;
+  static_assert((kStages - 2) * KD <= 63, "loading waves' wait within the counter's range");
   // The stage, trash and staging addresses are absolute: this is the
   // kernel's only LDS allocation, so it starts at address 0.
   __shared__ int4 lds_raw[L::kBytes / 16];
