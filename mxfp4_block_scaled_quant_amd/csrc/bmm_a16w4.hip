@@ -17,10 +17,9 @@
 // it) and a run of 16-row m-tiles; each of its 8 waves dequantises its 1/8
 // of the workgroup's output columns once into registers (bf16 MFMA
 // fragments), and the activation m-tiles stream through
-// two LDS stages by buffer->LDS loads (in the MFMA's lane order: m-tile i+1
-// loads while m-tile i is computed), one barrier per m-tile, so activations
-// are read from HBM once, weights once per workgroup, and output written
-// once.  Waves 0-3 issue all activation loads
+// a ring of two or three LDS stages by buffer->LDS loads (in the MFMA's
+// lane order), one barrier per m-tile, so activations are read from HBM
+// once, weights once per workgroup, and output written once.  Waves 0-3 issue all activation loads
 // and waves 4-7 all output stores (through a double-buffered LDS staging
 // area, as whole 16-byte pieces of rows): a wave's memory counter retires
 // loads and stores in issue order, so a wave that both stores and waits
@@ -158,23 +157,24 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 constexpr int kWavesS = 8;
 
 // LDS of one instance (KF K-fragments, NT column tiles, output element
-// size ESZ): two stages of KF KiB (fragment c of a stage at c KiB), a 1 KiB
-// target for padding loads, then two output staging buffers, each with a
-// 16-row block per wave (rows of NT*16 elements plus 16 bytes to spread
-// banks).  Two stages, not more: measured on MI355X, deeper rings (3 to 8
-// m-tiles, the loads issued further ahead) were slower at every MLA shape
-// (K-up / V-up, M = 4096: 20.7 / 21.4 us with two stages, 21.3 / 22.1 with
-// three, 22.7 / 25.8 with eight), since the larger start-up burst of every
-// workgroup delays its first m-tile; one m-tile of compute covers the next
-// one's load.
-template <int KF, int NT, int ESZ>
+// size ESZ, NS stages): NS stages of KF KiB (fragment c of a stage at c
+// KiB), a 1 KiB target for padding loads, then two output staging buffers,
+// each with a 16-row block per wave (rows of NT*16 elements plus 16 bytes to
+// spread banks).  A shallow ring: measured on MI355X with activations read
+// from HBM, a three-stage ring beats deeper ones (K-up / V-up, M = 4096:
+// 23.2 / 24.1 us with three stages, 23.3 / 24.9 with four, 24.5 / 28.1 with
+// eight: the larger start-up burst of every workgroup delays its first
+// m-tile), and with up to four m-tiles per workgroup two stages do (M =
+// 1024: 9.1 / 9.8 us against 9.4 / 10.5; M = 256: 5.1 / 5.7 against 5.3 /
+// 6.0).
+template <int KF, int NT, int ESZ, int NS>
 struct BmmLds {
   static constexpr int kRowB = NT * 16 * ESZ;
   static constexpr int kRowStride = kRowB + 16;
   static constexpr int kBlock = 16 * kRowStride;         // one wave's staged block
   static constexpr int kStgBuf = kWavesS * kBlock;       // one staging buffer
   static constexpr int kStage = KF * 1024;
-  static constexpr int kStages = 2;
+  static constexpr int kStages = NS;
   static constexpr int kTrash = kStages * kStage;
   static constexpr int kStg = kTrash + 1024;
   static constexpr int kBytes = kStg + 2 * kStgBuf;
@@ -363,11 +363,11 @@ __device__ __forceinline__ void stage_store(const BmmArgs& p, int b, int mt, int
 // workgroup (b, s, nb) takes m-tiles [s*T, min((s+1)*T, nmt)) and the
 // 8*NT column tiles from 8*NT*nb (NB > 1 when there are few m-tiles: more
 // workgroups, each with a smaller weight slice to load and dequantise).
-template <int KF, int NT, bool F32, bool VEC>
+template <int KF, int NT, bool F32, bool VEC, int NS>
 __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, int T, int NB) {
   constexpr int KD = (KF + 3) / 4;  // loads per loading wave per m-tile
   constexpr int esz = F32 ? 4 : 2;
-  using L = BmmLds<KF, NT, esz>;
+  using L = BmmLds<KF, NT, esz, NS>;
   constexpr int kStages = L::kStages;
   static_assert((kStages - 2) * KD <= 63, "loading waves' wait within the counter's range");
   // The stage, trash and staging addresses are absolute: this is the
@@ -580,20 +580,26 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
     const int per = 16 / esz;
     const bool vec = N % per == 0 && som % per == 0 && sob % per == 0 && ((uintptr_t)out & 15) == 0;
     const dim3 grid((unsigned)(B * S * NB)), block(64 * kWavesS);
-#define MXFP4_BMM_LAUNCH(KF_, NT_)                                                                        \
-  do {                                                                                                    \
-    if (out_f32 && vec) bmm_stream_kernel<KF_, NT_, true, true><<<grid, block, 0, stream>>>(p, S, T, NB); \
-    else if (out_f32) bmm_stream_kernel<KF_, NT_, true, false><<<grid, block, 0, stream>>>(p, S, T, NB);  \
-    else if (vec) bmm_stream_kernel<KF_, NT_, false, true><<<grid, block, 0, stream>>>(p, S, T, NB);      \
-    else bmm_stream_kernel<KF_, NT_, false, false><<<grid, block, 0, stream>>>(p, S, T, NB);              \
+#define MXFP4_BMM_LAUNCH_NS(KF_, NT_, NS_)                                                                      \
+  do {                                                                                                          \
+    if (out_f32 && vec) bmm_stream_kernel<KF_, NT_, true, true, NS_><<<grid, block, 0, stream>>>(p, S, T, NB);  \
+    else if (out_f32) bmm_stream_kernel<KF_, NT_, true, false, NS_><<<grid, block, 0, stream>>>(p, S, T, NB);   \
+    else if (vec) bmm_stream_kernel<KF_, NT_, false, true, NS_><<<grid, block, 0, stream>>>(p, S, T, NB);       \
+    else bmm_stream_kernel<KF_, NT_, false, false, NS_><<<grid, block, 0, stream>>>(p, S, T, NB);               \
+  } while (0)
+#define MXFP4_BMM_LAUNCH(KF_, NT_)                   \
+  do {                                               \
+    if (T <= 4) MXFP4_BMM_LAUNCH_NS(KF_, NT_, 2);    \
+    else MXFP4_BMM_LAUNCH_NS(KF_, NT_, 3);           \
   } while (0)
     if (cfg == 4) MXFP4_BMM_LAUNCH(6, 4);
     else if (cfg == 1) MXFP4_BMM_LAUNCH(8, 4);
     else if (cfg == 2) MXFP4_BMM_LAUNCH(16, 2);
-    else if (cfg == 5) MXFP4_BMM_LAUNCH(6, 1);
-    else if (cfg == 6) MXFP4_BMM_LAUNCH(8, 1);
-    else if (cfg == 7) MXFP4_BMM_LAUNCH(16, 1);
+    else if (cfg == 5) MXFP4_BMM_LAUNCH_NS(6, 1, 2);
+    else if (cfg == 6) MXFP4_BMM_LAUNCH_NS(8, 1, 2);
+    else if (cfg == 7) MXFP4_BMM_LAUNCH_NS(16, 1, 2);
     else MXFP4_BMM_LAUNCH(32, 1);
+#undef MXFP4_BMM_LAUNCH_NS
 #undef MXFP4_BMM_LAUNCH
     return hipGetLastError();
   }
