@@ -52,6 +52,10 @@ CASES = [
     ("colblocks_2x20x200x256", 2, 20, 200, 256, True),      # two column blocks, the last ragged
     ("colblocks_5x3x392x512", 5, 3, 392, 512, False),
     ("ragged_2x70x30x4128", 2, 70, 30, 4128, True),
+    # 81 m-tiles over 16 workgroups per head: six per workgroup (the
+    # three-stage ring), the last workgroup with three, the last tile 7 rows
+    ("kup_M1287", 16, 1287, 512, 192, False),
+    ("vup_M1287", 16, 1287, 256, 512, True),
 ]
 
 
@@ -123,7 +127,7 @@ def test_bmm_dequant_exact_every_scale():
 
 
 @pytest.mark.parametrize("name,B,M,N,K", [("kup_M37", 16, 37, 512, 192), ("vup_M70", 16, 70, 256, 512),
-                                          ("small_M3", 4, 3, 200, 256)])
+                                          ("small_M3", 4, 3, 200, 256), ("kup_M1287", 16, 1287, 512, 192)])
 def test_bmm_strided_activations_and_output(name, B, M, N, K):
     # x as a view with padded rows and heads (sxm = K + 8, sxb = (M + 3) * sxm),
     # out as a view with padded rows inside a sentinel buffer: bitwise the
