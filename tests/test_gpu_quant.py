@@ -126,6 +126,20 @@ def test_quant_strided_input_and_output():
     assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
 
 
+@pytest.mark.parametrize("layout,M,K", [(0, 1001, 4128), (1, 1990, 4128)], ids=["rowmajor", "gemm"])
+def test_quant_multi_unit_ragged(layout, M, K):
+    # Sizes that take the launches handing several row segments (row-major:
+    # 9009 of them, not a multiple of the 16 per workgroup; the last segment
+    # of every row is one block) or 1 KiB units (GEMM: 4500, the last 16-row
+    # strip holding 6 rows) to each wave or workgroup; every byte against
+    # the oracle, strided input included.
+    need_gpu()
+    x = inputs.activations(M, K, 9, outliers=True, edge=True)
+    q, s = _gpu_quant(x, layout, ldx_pad=40)
+    q_ref, s_ref = _expect(x, layout)
+    assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
+
+
 def test_quant_full_prefill_size_sampled_rows():
     # The largest activation of the prefill sweep (8192 x 14336), launched as
     # the GEMM path launches it; the oracle checks sampled rows exactly.
