@@ -341,7 +341,12 @@ __device__ __forceinline__ void stage_store(const BmmArgs& p, int b, int mt, int
   for (int e = 0; e < PER; ++e) {
     asm volatile("" : "+v"(v[e]));
     if (VEC) {
-      __builtin_amdgcn_raw_buffer_store_b128(v[e], ro, ok[e] && n[e] < p.N ? base[e] : kOOB, 0, 0);
+      // Staged rows of whole 128-byte lines go out non-temporal (the output
+      // is not read again here): measured K-up (128 bytes per row) M = 1024
+      // 9.0 -> 7.7 us, M = 4096 22.4 -> 22.0 us; half-line rows (V-up) were
+      // slower that way (M = 4096 23.4 -> 24.9 us), so they keep the default.
+      constexpr int kAux = CPR * 16 >= 128 ? 2 : 0;
+      __builtin_amdgcn_raw_buffer_store_b128(v[e], ro, ok[e] && n[e] < p.N ? base[e] : kOOB, 0, kAux);
     } else {
 #pragma unroll
       for (int x = 0; x < EPP; ++x) {

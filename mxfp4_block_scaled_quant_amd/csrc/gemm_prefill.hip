@@ -62,6 +62,11 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 #ifndef MXFP4_STORE_AUX
 #define MXFP4_STORE_AUX 0
 #endif
+// Cache policy of the staged bf16 epilogue's stores (whole 128-byte row
+// pieces, not read again by this kernel): non-temporal.  Measured on MI355X:
+// 1-2% faster at five of the six M >= 2048 prefill shapes (e.g. M = 8192,
+// N = 5120, K = 14336 295 -> 289 us), no change at the sixth.
+constexpr int kStagedStoreAux = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Fragment registers: a native 4 x 32-bit vector, so inline assembly can take
@@ -460,8 +465,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& p, const Tile& t
     // would turn every store into a waterfall loop over the descriptor)
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, p.M - rb)));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (int64_t)rb * p.ldo * 2, (uint32_t)(nrows * p.ldo * 2));
-    __builtin_amdgcn_raw_buffer_store_b128(r0, ro, voff0, 0, MXFP4_STORE_AUX);
-    __builtin_amdgcn_raw_buffer_store_b128(r1, ro, voff1, 0, MXFP4_STORE_AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(r0, ro, voff0, 0, kStagedStoreAux);
+    __builtin_amdgcn_raw_buffer_store_b128(r1, ro, voff1, 0, kStagedStoreAux);
   }
 }
 
