@@ -4,8 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-prefill] [--no-bmm]
     python bench.py --traffic-pass          (workload of the counter runs)
+    python bench.py --prefill-pass          (workload of the prefill counter runs)
     python bench.py --traffic-summary FETCH.csv WRITE.csv CMD...   (CPU only)
     python bench.py --trace-summary STATS.csv TRACE.csv MARKER.csv BENCH.log CMD...  (CPU only)
+    python bench.py --prefill-summary TRACE.csv COUNTERS.csv CMD...  (CPU only)
 
 Headline (the metric's M <= 16 decode regime): one step is one pass over the
 decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
@@ -191,6 +193,36 @@ def traffic_pass():
     print(json.dumps({"traffic_pass": plan}), flush=True)
 
 
+PREFILL_PASS_M = 8192
+PREFILL_PASS_REPS = 4
+
+
+def prefill_pass():
+    """The workload of the prefill counter runs (run under rocprofv3): the
+    prefill GEMM at M = 8192 for each (N, K) of the sweep, PREFILL_PASS_REPS
+    launches each, on the sweep's inputs (activations seed 3 with outliers,
+    weights seed 2, no bias, bf16 out)."""
+    import mxfp4_block_scaled_quant_amd as mx
+    from mxfp4_block_scaled_quant_amd import inputs
+    mx.lib()
+    dev = torch.device("cuda:0")
+    plan = []
+    M = PREFILL_PASS_M
+    for (N, K) in DECODE_NK:
+        W = mx.quantize_weight(inputs.bits_to_torch_bf16(inputs.weights(N, K, 2)).to(dev))
+        x = inputs.bits_to_torch_bf16(inputs.activations(M, K, 3, outliers=True)).to(dev)
+        q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(PREFILL_PASS_REPS):
+            mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, None, torch.bfloat16, out=out)
+        torch.cuda.synchronize()
+        plan.append((M, N, K, PREFILL_PASS_REPS))
+        del W, x, q, s, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"prefill_pass": plan}), flush=True)
+
+
 def _counter_rows(csv_path):
     import csv
     rows = []
@@ -310,11 +342,78 @@ def trace_summary(stats_csv, trace_csv, marker_csv, bench_log, command):
     print(f"wrote {PROFILE_MD}: trace {trace_us:.3f} us vs launch_us {roof.get('launch_us')}")
 
 
+PREFILL_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                          "gemm_prefill_kernel__M8192_counters.md")
+
+
+def prefill_counter_summary(trace_csv, pmc_csv, command):
+    """The committed prefill counter summary (PREFILL_MD): per launch of
+    prefill_pass, the kernel-trace duration, the shader clock the launch ran
+    at (GRBM_GUI_ACTIVE summed over the 8 XCDs / 8 / the counter run's own
+    duration) and the MFMA pipes' busy share (SQ_VALU_MFMA_BUSY_CYCLES summed
+    over the 1024 SIMDs / (1024 x those cycles)).  A 16x16x128 FP4 MFMA keeps
+    its pipe 16 cycles for 65536 FLOP, so the algorithmic MFMA cycles of a
+    GEMM are 2MNK/65536 x 16 = MNK/2048."""
+    import csv
+    trace = [r for r in csv.DictReader(open(trace_csv)) if "gemm_prefill_kernel" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    pmc = {}
+    for r in csv.DictReader(open(pmc_csv)):
+        if "gemm_prefill_kernel" not in r["Kernel_Name"]:
+            continue
+        d = pmc.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    pmc = [pmc[k] for k in sorted(pmc)]
+    M = PREFILL_PASS_M
+    shapes = [(N, K) for (N, K) in DECODE_NK for _ in range(PREFILL_PASS_REPS)]
+    assert len(trace) == len(pmc) == len(shapes), (len(trace), len(pmc), len(shapes))
+    rows = []
+    for (N, K), t, c in zip(shapes, trace, pmc):
+        us = (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3
+        cyc = c["GRBM_GUI_ACTIVE"] / 8
+        ghz = cyc / (c["us"] * 1e3)
+        alg = M * N * K / 2048
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc)
+        pf = 2.0 * M * N * K / (us * 1e-6) / 1e15
+        rows.append(dict(N=N, K=K, trace_us=round(us, 1), pflops=round(pf, 3), frac=round(pf / 10.1, 3),
+                         counter_run_us=round(c["us"], 1), clock_ghz=round(ghz, 3),
+                         mfma_cycles=int(c["SQ_VALU_MFMA_BUSY_CYCLES"]), algorithmic_mfma_cycles=int(alg),
+                         mfma_busy=round(busy, 3), frac_at_clock=round(pf / (10.1 * ghz / 2.4), 3)))
+    lines = ["# gemm_prefill_kernel — clock and MFMA occupancy at M = 8192", "",
+             "Workload `python bench.py --prefill-pass`: the prefill GEMM (bf16 out, no bias) at",
+             f"M = {M} for each (N, K), {PREFILL_PASS_REPS} launches back to back, on the prefill sweep's inputs",
+             "(activations seed 3 with outliers, weights seed 2). One kernel-trace run and one",
+             "counter run (`GRBM_GUI_ACTIVE` and `SQ_VALU_MFMA_BUSY_CYCLES` in one pass):", "",
+             "```", *command, "```", "",
+             "- clock = GRBM_GUI_ACTIVE / 8 XCDs / the counter run's duration of that launch;",
+             "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x those cycles);",
+             "- algorithmic MFMA cycles = M N K / 2048 (16 cycles per 16x16x128 FP4 MFMA of",
+             "  65536 FLOP): equal to the counter means no MFMA beyond the product's own;",
+             "- frac = PFLOP/s (trace duration) / 10.1; frac at clock = the same against",
+             "  10.1 PF x clock / 2.4 GHz.", "",
+             "| N | K | trace us | PFLOP/s | frac | counter-run us | clock GHz | MFMA cycles | algorithmic | MFMA busy | frac at clock |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['N']} | {r['K']} | {r['trace_us']} | {r['pflops']} | {r['frac']} | {r['counter_run_us']} | "
+                     f"{r['clock_ghz']} | {r['mfma_cycles']} | {r['algorithmic_mfma_cycles']} | {r['mfma_busy']} | "
+                     f"{r['frac_at_clock']} |")
+    lines += ["", "```json", json.dumps(dict(kernel="gemm_prefill_kernel", M=M, launches=rows)), "```", ""]
+    with open(PREFILL_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {PREFILL_MD}")
+    for r in rows:
+        print(r)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--prefill-summary":
+        return prefill_counter_summary(sys.argv[2], sys.argv[3], sys.argv[4:])
     if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
         return trace_summary(*sys.argv[2:6], sys.argv[6:])
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-pass":
         return traffic_pass()
+    if len(sys.argv) > 1 and sys.argv[1] == "--prefill-pass":
+        return prefill_pass()
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-summary":
         return traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4:])
     ap = argparse.ArgumentParser()
