@@ -84,7 +84,12 @@ size_t mxfp4_scale_bytes(int64_t rows, int64_t K, int layout);
 size_t mxfp4_weight_bytes(int64_t batch, int64_t N, int64_t K);
 size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K);
 
-/* Workspace bytes mxfp4_gemm_a4w4 needs for this shape (may be 0). */
+/* Workspace bytes mxfp4_gemm_a4w4 and mxfp4_gemm_a4w4_mxfp4_out need for
+ * this shape: 0 where the GEMM runs on whole output tiles (every M <= 64
+ * call, and most larger ones), else the split schedule's (see
+ * mxfp4_gemm_a4w4), sized for up to 256 compute units: 256 KiB per
+ * workgroup (up to 64 MiB) plus 4 bytes per split tile and per workgroup.
+ * Depends on the mxfp4_debug_set_gemm_path setting.  0 on invalid shapes. */
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -145,9 +150,21 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
  *   bias      bf16 [N] or NULL
  *   out       [M, N], row stride ldo ELEMENTS, bf16 or fp32 per out_dtype
  *             (N <= ldo < 2^22 for bf16, < 2^21 for fp32; 4-byte aligned)
- *   workspace may be NULL when mxfp4_gemm_workspace_bytes() returns 0.
+ *   workspace mxfp4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned
+ *             (NULL when that is 0); scratch owned by the call until it
+ *             completes on `stream`: its contents need no initialisation
+ *             and are not kept.  Calls that overlap in time (other streams)
+ *             need workspaces of their own.
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
- * Results are identical run to run (no atomics; fixed reduction order).
+ * For M > 64, where whole 256 x 256 output tiles would leave the last round
+ * of compute units at most half full and K is long enough to pay for it,
+ * the tiles short of whole rounds are each cut along K into equal slices
+ * for the otherwise idle workgroups (split-K): a split tile's fp32 partial
+ * sums meet in the workspace and are added in K order by the last
+ * workgroup to finish a slice (found by an atomic ticket), so results are
+ * still identical run to run, whatever order the slices finish in.  The
+ * call then launches a small kernel that clears the workspace's counters
+ * before the GEMM (no memset: the pair can be captured into a graph).
  */
 int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales,
                     const void* w_pre, const void* ws_pre, const void* bias,
@@ -265,8 +282,12 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm,
  * Test hook, not part of the method: force the GEMM kernel used by
  * mxfp4_gemm_a4w4 -- 1 = the small-M streaming kernel (M <= 64 only; larger
  * M still uses the tiled kernel), 2 = the LDS-tiled kernel, 0 = choose by M
- * (the default).  Process-wide and not synchronised with calls in flight on
- * other threads.  Returns MXFP4_ERR_ARG for other values.
+ * (the default); 3 = the tiled kernel on whole tiles only, 4 = the tiled
+ * kernel with the split schedule wherever the tiles leave a round of
+ * compute units part-empty and a tile has more than 512 of K (also for the
+ * tiled kernel's share of mxfp4_linear and mxfp4_linear_prequantized).  Process-wide and not synchronised with calls
+ * in flight on other threads; query workspace sizes after setting it.
+ * Returns MXFP4_ERR_ARG for other values.
  */
 int mxfp4_debug_set_gemm_path(int path);
 

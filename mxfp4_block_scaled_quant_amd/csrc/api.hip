@@ -109,9 +109,24 @@ size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K) {
   return (size_t)(batch * gemm_scale_bytes(N, K));
 }
 
+// Which GEMM kernel a call of M rows takes: 1 = small-M, 2 = large-M.
+static int gemm_path(int64_t M) {
+  const int path = get_gemm_path_override();
+  if (path == 1 && M <= 64) return 1;
+  if (path >= 2) return 2;
+  return M <= 64 ? 1 : 2;
+}
+
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
-  return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf) return 0;
+  return gemm_path(M) == 2 ? gemm_prefill_workspace_bytes(M, N, K) : 0;
+}
+
+// Quantised activations in the GEMM layouts, then the GEMM's workspace, in
+// one workspace: byte offsets of the scales and of the GEMM's part.
+static size_t act_scales_offset(int64_t M, int64_t K) { return (size_t)cdiv(gemm_data_bytes(M, K), 256) * 256; }
+static size_t act_gemm_offset(int64_t M, int64_t K) {
+  return (act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K) + 255) / 256 * 256;
 }
 
 int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
@@ -159,16 +174,18 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
       gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
     return MXFP4_ERR_SHAPE;
-  if (workspace_bytes < mxfp4_gemm_workspace_bytes(M, N, K)) return MXFP4_ERR_WORKSPACE;
+  const size_t need = mxfp4_gemm_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return MXFP4_ERR_WORKSPACE;
   if (M == 0) return MXFP4_OK;
-  if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out) return MXFP4_ERR_NULL;
+  if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out || (need && !workspace)) return MXFP4_ERR_NULL;
   if (!aligned(a_fp4, 16) || !aligned(a_scales, 4) || !aligned(w_pre, 16) ||
-      !aligned(ws_pre, 4) || !aligned(out, 4) || (bias && !aligned(bias, 2)))
+      !aligned(ws_pre, 4) || !aligned(out, 4) || (bias && !aligned(bias, 2)) ||
+      (workspace && !aligned(workspace, 16)))
     return MXFP4_ERR_ALIGN;
   int cus = 0;
   int st = check_device(&cus);
   if (st) return st;
-  GemmArgs p;
+  GemmArgs p{};
   p.cus = cus;
   p.a = (const uint8_t*)a_fp4;
   p.as = (const uint8_t*)a_scales;
@@ -193,18 +210,17 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   p.out_fp4 = 0;
   p.out_scales = nullptr;
   p.ldos = 0;
-  int path = get_gemm_path_override();
-  if (path == 0) path = M <= 64 ? 1 : 2;
-  if (path == 1 && M > 64) path = 2;  // the decode kernel covers at most 64 rows
+  p.work = (uint8_t*)workspace;
+  p.work_bytes = workspace ? workspace_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
-  return launched(path == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+  return launched(gemm_path(M) == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
 }
 
 size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
   if (M == 0 || linear_fused(M, N, K)) return 0;
-  return (size_t)(cdiv(gemm_data_bytes(M, K), 256) * 256 + gemm_scale_bytes(M, K)) +
-         mxfp4_gemm_workspace_bytes(M, N, K);
+  const size_t g = M <= 64 ? 0 : mxfp4_gemm_workspace_bytes(M, N, K);
+  return g ? act_gemm_offset(M, K) + g : act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K);
 }
 
 int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre,
@@ -232,7 +248,7 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   int st = check_device(&cus);
   if (st) return st;
   hipStream_t s = (hipStream_t)stream;
-  GemmArgs p;
+  GemmArgs p{};
   p.cus = cus;
   p.w = (const uint8_t*)w_pre;
   p.ws = (const uint8_t*)ws_pre;
@@ -262,7 +278,7 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   }
   // Larger M: quantise into the workspace, then the GEMM kernel for that M.
   uint8_t* q = (uint8_t*)workspace;
-  uint8_t* sc = q + cdiv(gemm_data_bytes(M, K), 256) * 256;
+  uint8_t* sc = q + act_scales_offset(M, K);
   st = launched(launch_quant_1x32(x, M, K, ldx, q, 0, sc, MXFP4_LAYOUT_GEMM, s));
   if (st) return st;
   p.a = q;
@@ -270,6 +286,8 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
   p.x = nullptr;
   p.ldx = 0;
   p.x_bytes = 0;
+  p.work = q + act_gemm_offset(M, K);
+  p.work_bytes = workspace_bytes > act_gemm_offset(M, K) ? workspace_bytes - act_gemm_offset(M, K) : 0;
   return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
 }
 
@@ -285,16 +303,18 @@ int mxfp4_gemm_a4w4_mxfp4_out(const void* a_fp4, const void* a_scales, const voi
   if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
       gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
     return MXFP4_ERR_SHAPE;
-  if (workspace_bytes < mxfp4_gemm_workspace_bytes(M, N, K)) return MXFP4_ERR_WORKSPACE;
+  const size_t need = mxfp4_gemm_workspace_bytes(M, N, K);
+  if (workspace_bytes < need) return MXFP4_ERR_WORKSPACE;
   if (M == 0) return MXFP4_OK;
-  if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out_fp4 || !out_scales) return MXFP4_ERR_NULL;
+  if (!a_fp4 || !a_scales || !w_pre || !ws_pre || !out_fp4 || !out_scales || (need && !workspace))
+    return MXFP4_ERR_NULL;
   if (!aligned(a_fp4, 16) || !aligned(a_scales, 4) || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
-      !aligned(out_fp4, 4) || ldq % 4 || (bias && !aligned(bias, 2)))
+      !aligned(out_fp4, 4) || ldq % 4 || (bias && !aligned(bias, 2)) || (workspace && !aligned(workspace, 16)))
     return MXFP4_ERR_ALIGN;
   int cus = 0;
   int st = check_device(&cus);
   if (st) return st;
-  GemmArgs p;
+  GemmArgs p{};
   p.cus = cus;
   p.a = (const uint8_t*)a_fp4;
   p.as = (const uint8_t*)a_scales;
@@ -319,11 +339,10 @@ int mxfp4_gemm_a4w4_mxfp4_out(const void* a_fp4, const void* a_scales, const voi
   p.out_fp4 = 1;
   p.out_scales = (uint8_t*)out_scales;
   p.ldos = lds;
-  int path = get_gemm_path_override();
-  if (path == 0) path = M <= 64 ? 1 : 2;
-  if (path == 1 && M > 64) path = 2;
+  p.work = (uint8_t*)workspace;
+  p.work_bytes = workspace ? workspace_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
-  return launched(path == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+  return launched(gemm_path(M) == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
 }
 
 int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t K, void* out,
@@ -342,8 +361,8 @@ int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t 
 size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
   if (M <= 64) return 0;
-  return (size_t)(cdiv(gemm_data_bytes(M, K), 256) * 256 + gemm_scale_bytes(M, K)) +
-         mxfp4_gemm_workspace_bytes(M, N, K);
+  const size_t g = gemm_prefill_workspace_bytes(M, N, K);
+  return g ? act_gemm_offset(M, K) + g : act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K);
 }
 
 int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scales, int64_t lds,
@@ -372,7 +391,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   int st = check_device(&cus);
   if (st) return st;
   hipStream_t s = (hipStream_t)stream;
-  GemmArgs p;
+  GemmArgs p{};
   p.cus = cus;
   p.w = (const uint8_t*)w_pre;
   p.ws = (const uint8_t*)ws_pre;
@@ -404,7 +423,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   }
   // larger M: permute into the GEMM layouts in the workspace, then the GEMM
   uint8_t* q = (uint8_t*)workspace;
-  uint8_t* sc = q + cdiv(gemm_data_bytes(M, K), 256) * 256;
+  uint8_t* sc = q + act_scales_offset(M, K);
   st = launched(launch_preshuffle_strided(x_fp4, ldq, x_scales, lds, 1, M, K, q, sc, s));
   if (st) return st;
   p.a = q;
@@ -412,6 +431,8 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   p.a_rowmajor = 0;
   p.lda = p.lds = 0;
   p.scales_vec = 0;
+  p.work = q + act_gemm_offset(M, K);
+  p.work_bytes = workspace_bytes > act_gemm_offset(M, K) ? workspace_bytes - act_gemm_offset(M, K) : 0;
   return launched(launch_gemm_prefill(p, s));
 }
 
@@ -438,9 +459,10 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, cons
                                    out_dtype == MXFP4_OUT_F32, B, M, N, K, (hipStream_t)stream, cus));
 }
 
-// Test hook: force the decode (1) or prefill (2) GEMM kernel, 0 = by M.
+// Test hook: force the decode (1) or prefill (2) GEMM kernel, 0 = by M; 3
+// and 4: the prefill kernel with whole tiles only / the split schedule.
 int mxfp4_debug_set_gemm_path(int path) {
-  if (path < 0 || path > 2) return MXFP4_ERR_ARG;
+  if (path < 0 || path > 4) return MXFP4_ERR_ARG;
   set_gemm_path_override(path);
   return MXFP4_OK;
 }

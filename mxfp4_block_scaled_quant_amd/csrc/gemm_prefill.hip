@@ -27,7 +27,22 @@
 //    (buffer stores, out-of-range lanes masked by offset) while the next
 //    tile's operands are already in flight;
 //  * tiles are ordered in groups of 8 row-tiles; each XCD's workgroups take
-//    consecutive tiles, so the tiles in flight on an XCD share its L2.
+//    consecutive tiles, so the tiles in flight on an XCD share its L2;
+//  * split schedule, where whole tiles would leave the last round of
+//    workgroups part-empty: the r tiles short of whole rounds are each cut
+//    along K into s slices of whole groups of 4 K-steps (s = workgroups / r,
+//    at most the groups a tile has), and each workgroup takes one slice
+//    before its whole tiles.  Slices are dealt slice-major (workgroup
+//    j r + t takes slice j of tile t), so the workgroups of one slice run
+//    at the same K at the same time, like whole tiles, and share operands in
+//    L2; and the slices come first, so their parts' memory traffic overlaps
+//    other workgroups' whole tiles.  Each slice takes an arrival ticket for
+//    its tile; every slice but the last to arrive stores its fp32
+//    accumulators to the workspace (device-scope stores) and raises a flag;
+//    the last adds the slices in K order (so the sum does not depend on
+//    arrival order) and runs the tile's epilogue.  Only that last slice
+//    ever waits, and only for slices whose workgroups already hold a
+//    ticket, so the wait always ends.
 //
 // Every register counts: at two waves per SIMD a wave has 256 registers, 128
 // of them accumulators and 64 operand fragments.
@@ -57,7 +72,8 @@ constexpr int kScaleLds = kStageBytes;
 constexpr int kBiasLds = kScaleLds + kUnits * 256;  // + 8 KiB
 constexpr int kEpiRowB = 144;                        // epilogue staging row stride (bytes)
 constexpr int kEpiLds = kBiasLds + kWaves * 256;     // + 2 KiB
-constexpr int kLdsBytes = kEpiLds + kWaves * 16 * kEpiRowB;  // + 18 KiB: 156 KiB in all
+constexpr int kSkLds = kEpiLds + kWaves * 16 * kEpiRowB;     // + 18 KiB
+constexpr int kLdsBytes = kSkLds + 16;                        // + the arrival rank: 156 KiB in all
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 #ifndef MXFP4_STORE_AUX
 #define MXFP4_STORE_AUX 0
@@ -67,6 +83,24 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 // 1-2% faster at five of the six M >= 2048 prefill shapes (e.g. M = 8192,
 // N = 5120, K = 14336 295 -> 289 us), no change at the sixth.
 constexpr int kStagedStoreAux = 2;
+
+// Split schedule of one launch: tiles [0, r) of the tile order are cut into
+// s slices each (r = 0: whole tiles only).  Workspace: one fp32 part slot of
+// a tile per slice (slot = the slice's workgroup), then an arrival counter
+// per split tile and a ready flag per slot, zeroed before every launch.
+struct SkArgs {
+  int r, s;
+  uint8_t* part;
+  uint32_t* ctrl;
+  uint32_t* flags;
+};
+constexpr uint32_t kPartBytes = kBM * kBN * 4;  // 256 KiB: one tile's fp32 accumulators
+// Cache policy of the part stores and loads: device scope (sc1), as the
+// memory model's relaxed device-scope atomics: written through, and read
+// past, the XCD-local caches, so another XCD's part is seen once its flag
+// is.  (Measured: no slower than cached accesses.)
+constexpr int kPartAux = 16;
+constexpr int kSpinLimit = 1 << 20;  // ready-flag polls before giving up (a guard: about a second)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // Fragment registers: a native 4 x 32-bit vector, so inline assembly can take
@@ -96,15 +130,19 @@ __device__ __forceinline__ v4f mfma_fp4v(v4i a, v4i b, uint32_t sa, uint32_t sb,
 // tile past the end).  Buffer descriptors are derived from it where a load is
 // issued, after any selection between tiles: a select between descriptors
 // becomes a vector select, which then costs a waterfall loop per load.
+// A work item: the groups [g0, g1) of 4 K-steps of one tile (a slice of a
+// split tile unless that is all G of them).
 struct Tile {
   int ms, mstrips, s0, strips;
+  int g0, g1;
 };
 
-// Linear tile L: tiles run down groups of kGroupM row-tiles, then across
-// columns.
+// Linear tile L (all its groups): tiles run down groups of kGroupM
+// row-tiles, then across columns.
 __device__ __forceinline__ Tile tile_at(const GemmArgs& p, int L, int tiles_m, int tiles_n) {
-  Tile t = {0, 0, 0, 0};
+  Tile t = {0, 0, 0, 0, 0, 0};
   if (L >= tiles_m * tiles_n) return t;
+  t.g1 = p.G;
   const int group = L / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(tiles_m - first_m, kGroupM);
@@ -114,6 +152,27 @@ __device__ __forceinline__ Tile tile_at(const GemmArgs& p, int L, int tiles_m, i
   t.s0 = (r / gm) * kTilesB;
   t.strips = min(kTilesB, p.Ns - t.s0);
   return t;
+}
+
+// This workgroup's share of a launch: first, if slot < r s, slice
+// slot / r of split tile slot % r (nsk = 1); then the whole tiles
+// r + k grid + slot.
+struct Share {
+  int slot, grid, nsk, n;
+};
+
+// Groups [g0, g1) of slice j of s: the G groups cut as evenly as whole
+// groups allow.
+__device__ __forceinline__ Tile work_at(const GemmArgs& p, const SkArgs& sk, const Share& s, int i, int tiles_m,
+                                        int tiles_n) {
+  if (i < s.nsk) {
+    const int j = s.slot / sk.r;
+    Tile tl = tile_at(p, s.slot - j * sk.r, tiles_m, tiles_n);
+    tl.g0 = j * p.G / sk.s;
+    tl.g1 = (j + 1) * p.G / sk.s;
+    return tl;
+  }
+  return tile_at(p, sk.r + (i - s.nsk) * s.grid + s.slot, tiles_m, tiles_n);
 }
 
 // This wave's buffer->LDS load of unit q (of its 4) of K-step t of tile
@@ -196,6 +255,9 @@ __device__ __forceinline__ void ds_read8(v2i& v, uint32_t addr) {
 template <int OFF>
 __device__ __forceinline__ void ds_write8(uint32_t addr, v2i v) {
   asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF));
+}
+__device__ __forceinline__ void ds_write4(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v));
 }
 
 // lgkmcnt(N) waits that the given registers depend on, so no MFMA reading
@@ -594,33 +656,140 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const Tile& tl, v4f 
   if (OM::kDrain) wait_vm<0>();
 }
 
-// The four K-steps of group g of tile c, loading four steps on (from tile
-// cn when g is the tile's last group).
+// The four K-steps of group g of work item c, loading four steps on (from
+// item cn when g is c's last group).
 template <int kStores, bool kBias>
 __device__ __forceinline__ void group_body(const GemmArgs& p, Pipe& P, const Tile& c, const Tile& cn, int g,
                                            int wv, int wm, int wn, const ReadAddr& ra, uint32_t lane16) {
-  const bool last = g + 1 == p.G;
+  const bool last = g + 1 == c.g1;
   Tile dt;
   dt.ms = last ? cn.ms : c.ms;
   dt.mstrips = last ? cn.mstrips : c.mstrips;
   dt.s0 = last ? cn.s0 : c.s0;
   dt.strips = last ? cn.strips : c.strips;
-  const int t4 = last ? 0 : 4 * (g + 1);
-  // 1 in the tile's first group, from a scalar instruction the compiler
+  const int t4 = last ? 4 * cn.g0 : 4 * (g + 1);
+  // 1 in the item's first group, from a scalar instruction the compiler
   // cannot see through (it would peel the first group to fold the test,
   // which costs register copies around the loop).
   int first;
-  asm volatile("s_cmp_eq_u32 %1, 0\n\ts_cselect_b32 %0, 1, 0" : "=s"(first) : "s"(g) : "scc");
+  asm volatile("s_cmp_eq_u32 %1, %2\n\ts_cselect_b32 %0, 1, 0" : "=s"(first) : "s"(g), "s"(c.g0) : "scc");
   main_step<0, kStores, kBias>(p, P, P.b0, P.b1, dt, c, t4 + 0, first, wv, wm, wn, ra, lane16);
   main_step<1, kStores, kBias>(p, P, P.b1, P.b0, dt, c, t4 + 1, first, wv, wm, wn, ra, lane16);
   main_step<2, kStores, kBias>(p, P, P.b0, P.b1, dt, c, t4 + 2, first, wv, wm, wn, ra, lane16);
   main_step<3, kStores, kBias>(p, P, P.b1, P.b0, dt, c, t4 + 3, first, wv, wm, wn, ra, lane16);
 }
 
+// kStores stores that write nothing (no records in the descriptor), as
+// inline assembly so identical stores are not merged: they stand for an
+// epilogue's stores in the counts of the next item's waits.
+template <int kStores>
+__device__ __forceinline__ void drop_stores() {
+  const v4i none = {0, 0, 0, 0x00020000};
+  const uint32_t zero = 0;
+#pragma unroll
+  for (int q = 0; q < kStores; ++q)
+    asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(zero), "v"(kOOB), "s"(none) : "memory");
+}
+
+// End of this workgroup's slice (kme of S = sk.s) of split tile t: take the
+// tile's arrival ticket.  Not the last to arrive: store the accumulators
+// to this workgroup's part slot, raise its flag, and return false (no
+// epilogue; the stores the next item's waits count are stood in for).  The
+// last: wait for the other slices' flags, sum the slices in K order into acc
+// (with two slices, acc plus the other: the same either way) and return
+// true.  Slice k of tile t is workgroup (and part slot) k r + t.
+// acc[i][j] (+)= the part at byte offset o of the part buffer, 8 loads in
+// flight at a time (all 32 at once would not fit beside the accumulators).
+template <bool kAdd>
+__device__ __forceinline__ void add_part(v4f (&acc)[kWM][kWN], __amdgpu_buffer_rsrc_t rp, uint32_t o) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    v4i v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = __builtin_amdgcn_raw_buffer_load_b128(rp, o + (uint32_t)(h * 8 + e) * 1024u, 0, kPartAux);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = (h * 8 + e) / kWN, j = (h * 8 + e) % kWN;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[i][j][r] = kAdd ? acc[i][j][r] + __uint_as_float((uint32_t)v[e][r]) : __uint_as_float((uint32_t)v[e][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int kStores>
+__device__ bool sk_combine(const SkArgs& sk, const Share& s, Pipe& P, int wv) {
+  // Let every LDS read and memory operation this wave has in flight land
+  // (the next item's fragments and loads), so nothing below races them.
+  // (Naming the fragment registers here, as the loop's waits do, would make
+  // them new values on this path only, and the merge after it would copy
+  // them all.)
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  const int S = sk.s, kme = s.slot / sk.r, t = s.slot - kme * sk.r;
+  const uint32_t lane = lane_here();
+  if (wv == 0 && lane == 0) {
+    const uint32_t r = __hip_atomic_fetch_add(sk.ctrl + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ds_write4(kSkLds, r);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  barrier_nofence();
+  uint32_t rank;
+  ds_read4<0>(rank, kSkLds);
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(rank));
+  // (all waves must read the rank before wave 0 may write the next one: the
+  // next write follows at least one more barrier, in the next item's loop)
+  const bool last = (int)__builtin_amdgcn_readfirstlane(rank) == S - 1;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(sk.part, (uint32_t)s.grid * kPartBytes);
+  const uint32_t lofs = (uint32_t)wv * (kPartBytes / kWaves) + lane * 16u;
+  if (!last || S > 2) {
+    const int my = s.slot;
+    const uint32_t o = (uint32_t)my * kPartBytes + lofs;
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+#pragma unroll
+      for (int j = 0; j < kWN; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            (v4i){(int)__float_as_uint(P.acc[i][j][0]), (int)__float_as_uint(P.acc[i][j][1]),
+                  (int)__float_as_uint(P.acc[i][j][2]), (int)__float_as_uint(P.acc[i][j][3])},
+            rp, o + (uint32_t)(i * kWN + j) * 1024u, 0, kPartAux);
+    wait_vm<0>();
+    barrier_nofence();
+    if (wv == 0 && lane == 0) __hip_atomic_store(sk.flags + my, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!last) {
+      wait_vm<0>();
+      drop_stores<kStores>();
+      return false;
+    }
+  }
+  for (int k = 0; k < S; ++k) {
+    if (k == kme) continue;
+    const int id = k * sk.r + t;
+    for (int it = 0; it < kSpinLimit; ++it) {
+      const uint32_t f = __hip_atomic_load(sk.flags + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readfirstlane(f) != 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  if (S == 2) {
+    add_part<true>(P.acc, rp, (uint32_t)((1 - kme) * sk.r + t) * kPartBytes + lofs);
+  } else {
+    // every part, this one's too, is in the workspace: p_0 + p_1 + ... in order
+    add_part<false>(P.acc, rp, (uint32_t)t * kPartBytes + lofs);
+    for (int k = 1; k < S; ++k) add_part<true>(P.acc, rp, (uint32_t)(k * sk.r + t) * kPartBytes + lofs);
+  }
+  return true;
+}
+
+__global__ void sk_clear_kernel(uint32_t* words, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) words[i] = 0;
+}
+
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n, SkArgs sk) {
   constexpr int kStores = OutMode<MODE>::kInFlight;
   constexpr bool kBiasLds = OutMode<MODE>::kBiasLds;
   // The stage and scale addresses above are absolute LDS addresses: this is
@@ -633,14 +802,19 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int ti
   const int wm = wv >> 2, wn = wv & 3;
   const int G = p.G;
 
-  // Tile list of this workgroup: tiles L = k * grid + slot, k = 0, 1, ...
   // Workgroups are dealt to the 8 XCDs round-robin; with a grid that is a
   // multiple of 8, slot numbers are remapped so each XCD's workgroups hold
-  // consecutive slots (and so consecutive tiles at every k).
+  // consecutive slots (and so consecutive tiles, or slices of consecutive
+  // tiles).
   const int ntiles = tiles_m * tiles_n;
-  const int grid = gridDim.x;
-  const int slot = (grid & 7) == 0 ? (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int ntile_wg = (ntiles - slot + grid - 1) / grid;
+  Share s;
+  s.grid = gridDim.x;
+  s.slot = (s.grid & 7) == 0 ? (blockIdx.x & 7) * (s.grid >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  {
+    s.nsk = s.slot < sk.r * sk.s ? 1 : 0;
+    const int rest = ntiles - sk.r;
+    s.n = s.nsk + (rest > s.slot ? (rest - s.slot + s.grid - 1) / s.grid : 0);
+  }
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)&lds_raw[0];
   const uint32_t lane16 = lane * 16;
@@ -651,29 +825,20 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int ti
   Pipe P;
   zero_acc(P.acc);
 
-  Tile c = tile_at(p, slot, tiles_m, tiles_n);
-  Tile cn = tile_at(p, slot + grid, tiles_m, tiles_n);
+  Tile c = work_at(p, sk, s, 0, tiles_m, tiles_n);
+  Tile cn = work_at(p, sk, s, 1, tiles_m, tiles_n);
 
-  // Prologue: scales of group 0 and steps 0..3 of the first tile in flight;
-  // then as many dropped stores (out-of-range offset) as an epilogue leaves
-  // in flight, so every tile's first group counts the same operations.
-  // Once the scales and step 0 have landed everywhere, read them in the
+  // Prologue: scales of the first item's first group and its first 4 steps
+  // in flight; then as many dropped stores as an epilogue leaves in flight,
+  // so every item's first group counts the same operations.  Once the
+  // scales and the first step have landed everywhere, read them in the
   // order the loop expects.
-  issue_scales(p, c, 0, wv);
-  issue_step(p, c, 0, 0, wv, lane16);
-  issue_step(p, c, 1, 1, wv, lane16);
-  issue_step(p, c, 2, 2, wv, lane16);
-  issue_step(p, c, 3, 3, wv, lane16);
-  {
-    // Inline assembly, so identical stores are not merged into one; the
-    // descriptor has no records (base 0, size 0), so every store is dropped
-    // without touching memory.
-    const v4i none = {0, 0, 0, 0x00020000};
-    const uint32_t zero = 0;
-#pragma unroll
-    for (int q = 0; q < kStores; ++q)
-      asm volatile("buffer_store_dword %0, %1, %2, 0 offen" ::"v"(zero), "v"(kOOB), "s"(none) : "memory");
-  }
+  issue_scales(p, c, c.g0, wv);
+  issue_step(p, c, 0, 4 * c.g0 + 0, wv, lane16);
+  issue_step(p, c, 1, 4 * c.g0 + 1, wv, lane16);
+  issue_step(p, c, 2, 4 * c.g0 + 2, wv, lane16);
+  issue_step(p, c, 3, 4 * c.g0 + 3, wv, lane16);
+  drop_stores<kStores>();
   wait_vm<3 * kLoadsPerWave + kStores>();
   barrier_nofence();
   read_scales(P.sa, P.sb, wm, wn);
@@ -681,41 +846,114 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int ti
   read_second_half<0>(P.af, ra);
 
   for (int k = 0;;) {
-    for (int g = 0; g < G; ++g) group_body<kStores, kBiasLds>(p, P, c, cn, g, wv, wm, wn, ra, lane16);
-    if (OutMode<MODE>::kFp4)
-      epilogue_fp4(p, c, P.acc, wv, wm, wn);
-    else if (OutMode<MODE>::kStaged)
-      epilogue_staged(p, c, P.acc, wv, wm, wn);
-    else
-      epilogue<MODE>(p, c, P.acc, wv, wm, wn);
-    if (++k == ntile_wg) break;
+    for (int g = c.g0; g < c.g1; ++g) group_body<kStores, kBiasLds>(p, P, c, cn, g, wv, wm, wn, ra, lane16);
+    const bool out = k >= s.nsk || sk_combine<kStores>(sk, s, P, wv);
+    if (out) {
+      if (OutMode<MODE>::kFp4)
+        epilogue_fp4(p, c, P.acc, wv, wm, wn);
+      else if (OutMode<MODE>::kStaged)
+        epilogue_staged(p, c, P.acc, wv, wm, wn);
+      else
+        epilogue<MODE>(p, c, P.acc, wv, wm, wn);
+    }
+    if (++k == s.n) break;
+    // The next item's first fragments and scales, already read in the last
+    // group, are read again from LDS (they stay there until the next
+    // group's first barrier): so their registers are free across the
+    // epilogue and the combine.
+    read_scales(P.sa, P.sb, wm, wn);
+    read_first_half<0>(P.af, P.b0, ra);
+    read_second_half<0>(P.af, ra);
     zero_acc(P.acc);
     c = cn;
-    cn = tile_at(p, slot + (k + 1) * grid, tiles_m, tiles_n);
+    cn = work_at(p, sk, s, k + 1, tiles_m, tiles_n);
   }
-  // The loads issued past the last tile (empty descriptors) still write
+  // The loads issued past the last item (empty descriptors) still write
   // zeros to LDS: let them and the LDS reads finish before the workgroup
   // ends.
   wait_lgkm<0>(P.af[4], P.af[5], P.af[6], P.af[7]);
   wait_vm<0>();
 }
 
+namespace {
+
+constexpr int kMaxSkGrid = 256;  // the split schedule's workgroups (and workspace) at most
+
+struct PrefillPlan {
+  int grid, r, s;
+  size_t bytes;  // workspace
+};
+
+// sched: 0 = by the measured rule below, 1 = whole tiles, 2 = split wherever
+// the tiles leave a round part-empty and a tile has more than one group.
+// The rule, from both schedules timed on MI355X (256 CUs) at M = 512 ...
+// 8192 for (N, K) = (14336, 5120), (5120, 14336), (34816, 5120): moving a
+// slice's 256 KiB part costs about as much as 7 groups of MFMAs, so split
+// where the r leftover tiles fill at most half a round and each slice keeps
+// at least 7 groups (3584 of K), or at least 4 where the leftover tiles fill
+// at most a quarter of a round (whole tiles then leave most compute units
+// idle).  Measured: K = 14336 gains 6-20% (M = 512: 79.9 -> 64.3 us; M =
+// 8192: 289 -> 267 us); K = 5120 (slices of at most 5 groups) loses 3-39%
+// and stays on whole tiles.
+PrefillPlan plan_prefill(int M, int N, int K, int cus, int sched) {
+  const int tiles_m = (M + kBM - 1) / kBM;
+  const int tiles_n = ((N + 15) / 16 * 16 + kBN - 1) / kBN;
+  const int T = tiles_m * tiles_n;
+  const int G = ((K + 127) / 128 + 3) / 4;
+  const int C = cus < kMaxSkGrid ? cus : kMaxSkGrid;
+  PrefillPlan whole = {T < cus ? T : cus, 0, 0, 0};
+  if (sched == 1 || C < 2) return whole;
+  const int r = T % C;
+  int s = r ? C / r : 0;
+  if (s > G) s = G;
+  if (s < 2) return whole;
+  if (sched == 0 && (2 * r > C || (G / s < 7 && (4 * r > C || G / s < 4)))) return whole;
+  PrefillPlan pl;
+  pl.r = r;
+  pl.s = s;
+  pl.grid = T >= C ? C : r * s;
+  const size_t words = (size_t)r + (size_t)pl.grid;
+  pl.bytes = ((size_t)pl.grid * kPartBytes + words * 4 + 255) / 256 * 256;
+  return pl;
+}
+
+int prefill_sched() {
+  const int path = get_gemm_path_override();
+  return path == 3 ? 1 : path == 4 ? 2 : 0;
+}
+
+}  // namespace
+
+size_t gemm_prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return plan_prefill((int)M, (int)N, (int)K, kMaxSkGrid, prefill_sched()).bytes;
+}
+
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = (p.Ns * 16 + kBN - 1) / kBN;
-  const int ntiles = tiles_m * tiles_n;
-  const int grid = ntiles < p.cus ? ntiles : p.cus;
+  PrefillPlan pl = plan_prefill(p.M, p.N, p.K, p.cus, prefill_sched());
+  if (pl.r && (!p.work || p.work_bytes < pl.bytes)) pl = plan_prefill(p.M, p.N, p.K, p.cus, 1);
+  SkArgs sk = {0, 1, nullptr, nullptr, nullptr};
+  if (pl.r) {
+    sk.r = pl.r;
+    sk.s = pl.s;
+    sk.part = p.work;
+    sk.ctrl = reinterpret_cast<uint32_t*>(p.work + (size_t)pl.grid * kPartBytes);
+    sk.flags = sk.ctrl + pl.r;
+    // a kernel, not a memset: the launch may be captured into a graph
+    sk_clear_kernel<<<1, 256, 0, stream>>>(sk.ctrl, pl.r + pl.grid);
+  }
   const bool a16 = ((uintptr_t)p.out & 15) == 0;
   const int mode = p.out_fp4 ? 4
                  : p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
                              : ((p.N % 8 == 0 && p.ldo % 8 == 0 && a16) ? 0 : 1);
-  const dim3 g((unsigned)grid), b(64 * kWaves);
+  const dim3 g((unsigned)pl.grid), b(64 * kWaves);
   switch (mode) {
-    case 0: gemm_prefill_kernel<0><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
-    case 1: gemm_prefill_kernel<1><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
-    case 2: gemm_prefill_kernel<2><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
-    case 4: gemm_prefill_kernel<4><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
-    default: gemm_prefill_kernel<3><<<g, b, 0, stream>>>(p, tiles_m, tiles_n); break;
+    case 0: gemm_prefill_kernel<0><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    case 1: gemm_prefill_kernel<1><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    case 2: gemm_prefill_kernel<2><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    case 4: gemm_prefill_kernel<4><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    default: gemm_prefill_kernel<3><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
   }
   return hipGetLastError();
 }

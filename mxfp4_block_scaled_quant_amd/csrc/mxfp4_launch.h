@@ -35,10 +35,17 @@ struct GemmArgs {
   int out_fp4;
   uint8_t* out_scales;
   int64_t ldos;
+  // Workspace of the large-M kernel's split schedule (it falls back to whole
+  // tiles when this is smaller than gemm_prefill_workspace_bytes asks).
+  uint8_t* work;
+  size_t work_bytes;
 };
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream);
+// Workspace the large-M kernel's split schedule takes for this shape on up
+// to 256 compute units (0: whole tiles only).
+size_t gemm_prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // Activation quantisation fused into the small-M GEMM (M <= 4), and whether
 // that beats quantisation + GEMM for a shape.
 hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream);
@@ -61,7 +68,9 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
 
 // Kernel-selection overrides used only by the tests and the benchmark to
 // exercise each GEMM path on every shape: 0 = automatic by M, 1 = decode
-// kernel, 2 = prefill kernel.
+// kernel, 2 = prefill kernel (schedule by estimate), 3 = prefill kernel with
+// whole tiles only, 4 = prefill kernel with the split schedule wherever a
+// tile has more than one group of 4 K-steps.
 void set_gemm_path_override(int path);
 int get_gemm_path_override();
 

@@ -216,5 +216,69 @@ def test_valid_call_without_gpu_reports_device(lib):
 
 
 def test_debug_path_hook(lib):
-    assert lib.mxfp4_debug_set_gemm_path(3) == 7
-    assert lib.mxfp4_debug_set_gemm_path(0) == 0
+    assert lib.mxfp4_debug_set_gemm_path(5) == 7
+    assert lib.mxfp4_debug_set_gemm_path(-1) == 7
+    for path in (4, 3, 2, 1, 0):
+        assert lib.mxfp4_debug_set_gemm_path(path) == 0
+
+
+# The large-M kernel's split schedule (256 compute units): the r tiles short
+# of whole rounds are cut along K into s = 256 / r slices, one per workgroup,
+# where the slices stay long enough to pay for their parts' traffic; its
+# workspace is one fp32 256 x 256 part per workgroup, then a counter per
+# split tile and a flag per workgroup, rounded up to 256 bytes.
+def _split_bytes(grid, r):
+    return (grid * 256 * 256 * 4 + 4 * (r + grid) + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("M,N,K,grid,r", [
+    (8192, 5120, 14336, 256, 128),     # 640 tiles: 128 left over, 2 slices of 14 groups
+    (512, 5120, 14336, 240, 40),       # 40 tiles, 6 slices of 4-5 groups
+    (2048, 5120, 14336, 0, 0),         # 160 tiles: more than half a round left over
+    (2048, 34816, 5120, 0, 0),         # 1088 tiles: slices of 2-3 groups would not pay
+    (512, 14336, 5120, 0, 0),          # 112 tiles, slices of 5 groups: not paid either
+    (8192, 14336, 5120, 0, 0),         # 1792 tiles: whole rounds
+    (37, 96, 4128, 0, 0),              # one tile: slices of one group
+    (64, 5120, 14336, 0, 0),           # M <= 64: the small-M kernel
+])
+def test_split_schedule_workspace(lib, M, N, K, grid, r):
+    want = _split_bytes(grid, r) if grid else 0
+    assert lib.mxfp4_gemm_workspace_bytes(M, N, K) == want
+    if M > 64:
+        # the quantised activations, then the GEMM's part
+        quant = L.weight_geometry(M, K)[2] + L.gemm_scale_geometry(M, K)[3]
+        assert lib.mxfp4_linear_workspace_bytes(M, N, K) >= quant + want
+        assert lib.mxfp4_linear_prequantized_workspace_bytes(M, N, K) >= quant + want
+
+
+def test_split_schedule_forced_and_whole(lib):
+    try:
+        assert lib.mxfp4_debug_set_gemm_path(3) == 0
+        assert lib.mxfp4_gemm_workspace_bytes(8192, 5120, 14336) == 0
+        assert lib.mxfp4_debug_set_gemm_path(4) == 0
+        # forced: wherever a round is left part-empty and a tile has 2+ groups
+        assert lib.mxfp4_gemm_workspace_bytes(2048, 34816, 5120) == _split_bytes(256, 64)
+        assert lib.mxfp4_gemm_workspace_bytes(300, 520, 1056) == _split_bytes(18, 6)
+        assert lib.mxfp4_gemm_workspace_bytes(37, 96, 4128) == _split_bytes(9, 1)
+        assert lib.mxfp4_gemm_workspace_bytes(300, 128, 256) == 0        # one group: nothing to split
+        assert lib.mxfp4_gemm_workspace_bytes(8192, 14336, 5120) == 0    # whole rounds
+        assert lib.mxfp4_gemm_workspace_bytes(2048, 5120, 14336) == 0    # 256 / 160: one slice
+    finally:
+        lib.mxfp4_debug_set_gemm_path(0)
+
+
+def test_split_schedule_workspace_validation(lib):
+    f = lib.mxfp4_gemm_a4w4
+    need = lib.mxfp4_gemm_workspace_bytes(8192, 5120, 14336)
+    assert need > 0
+
+    def call(work=None, work_bytes=0):
+        return f(P, P, P, P, None, P, 5120, 0, 8192, 5120, 14336, work, work_bytes, None)
+
+    assert call() == 4                                  # workspace missing
+    assert call(P, need - 1) == 4                       # too small
+    assert call(None, need) == 1                        # NULL with a size
+    assert call(P_ODD, need) == 3                       # misaligned
+    g = lib.mxfp4_gemm_a4w4_mxfp4_out
+    assert g(P, P, P, P, None, P, 2560, P, 160, 8192, 5120, 14336, None, 0, None) == 4
+    assert g(P, P, P, P, None, P, 2560, P, 160, 8192, 5120, 14336, P_ODD, need, None) == 3
