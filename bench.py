@@ -194,13 +194,14 @@ def traffic_pass():
 
 
 PREFILL_PASS_M = 8192
-PREFILL_PASS_REPS = 4
+PREFILL_PASS_REPS = 4   # launches per shape the summary reads, after one warm-up launch
 
 
 def prefill_pass():
     """The workload of the prefill counter runs (run under rocprofv3): the
-    prefill GEMM at M = 8192 for each (N, K) of the sweep, PREFILL_PASS_REPS
-    launches each, on the sweep's inputs (activations seed 3 with outliers,
+    prefill GEMM at M = 8192 for each (N, K) of the sweep, one warm-up launch
+    (its counters also catch the activity before it) then PREFILL_PASS_REPS
+    launches, on the sweep's inputs (activations seed 3 with outliers,
     weights seed 2, no bias, bf16 out)."""
     import mxfp4_block_scaled_quant_amd as mx
     from mxfp4_block_scaled_quant_amd import inputs
@@ -214,7 +215,7 @@ def prefill_pass():
         q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
-        for _ in range(PREFILL_PASS_REPS):
+        for _ in range(1 + PREFILL_PASS_REPS):
             mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, None, torch.bfloat16, out=out)
         torch.cuda.synchronize()
         plan.append((M, N, K, PREFILL_PASS_REPS))
@@ -365,8 +366,12 @@ def prefill_counter_summary(trace_csv, pmc_csv, command):
         d[r["Counter_Name"]] = float(r["Counter_Value"])
     pmc = [pmc[k] for k in sorted(pmc)]
     M = PREFILL_PASS_M
+    per = 1 + PREFILL_PASS_REPS
+    assert len(trace) == len(pmc) == per * len(DECODE_NK), (len(trace), len(pmc))
+    keep = [i for i in range(len(trace)) if i % per]   # drop each shape's warm-up launch
+    trace = [trace[i] for i in keep]
+    pmc = [pmc[i] for i in keep]
     shapes = [(N, K) for (N, K) in DECODE_NK for _ in range(PREFILL_PASS_REPS)]
-    assert len(trace) == len(pmc) == len(shapes), (len(trace), len(pmc), len(shapes))
     rows = []
     for (N, K), t, c in zip(shapes, trace, pmc):
         us = (int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3
@@ -381,7 +386,8 @@ def prefill_counter_summary(trace_csv, pmc_csv, command):
                          mfma_busy=round(busy, 3), frac_at_clock=round(pf / (10.1 * ghz / 2.4), 3)))
     lines = ["# gemm_prefill_kernel — clock and MFMA occupancy at M = 8192", "",
              "Workload `python bench.py --prefill-pass`: the prefill GEMM (bf16 out, no bias) at",
-             f"M = {M} for each (N, K), {PREFILL_PASS_REPS} launches back to back, on the prefill sweep's inputs",
+             f"M = {M} for each (N, K), a warm-up launch (not listed) then {PREFILL_PASS_REPS} launches back to",
+             "back, on the prefill sweep's inputs",
              "(activations seed 3 with outliers, weights seed 2). One kernel-trace run and one",
              "counter run (`GRBM_GUI_ACTIVE` and `SQ_VALU_MFMA_BUSY_CYCLES` in one pass):", "",
              "```", *command, "```", "",
@@ -391,6 +397,9 @@ def prefill_counter_summary(trace_csv, pmc_csv, command):
              "  65536 FLOP): equal to the counter means no MFMA beyond the product's own;",
              "- frac = PFLOP/s (trace duration) / 10.1; frac at clock = the same against",
              "  10.1 PF x clock / 2.4 GHz.", "",
+             "At N = 5120, K = 14336 the 640 tiles fill 2.5 rounds of the 256 workgroups: that",
+             "launch takes the split schedule (the 128 leftover tiles in 2 K slices each,",
+             "before 2 rounds of whole tiles); the other two shapes fill whole rounds.", "",
              "| N | K | trace us | PFLOP/s | frac | counter-run us | clock GHz | MFMA cycles | algorithmic | MFMA busy | frac at clock |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
