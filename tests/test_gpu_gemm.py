@@ -4,10 +4,12 @@ Bar: before the bf16 cast (fp32 output) |y - y_ref| <= 2^-18 (sum|a_i b_i| +
 |bias|) per element; after the cast within 1 bf16 ulp of the rounded oracle,
 or, where cancellation makes the pre-cast band wider than that, the rounding
 of a value inside the band; the bf16 output equals the RNE of the kernel's
-fp32 result; no NaN; identical bytes run to run.  Small shapes are checked element by element; the full
-decode / prefill sweeps at sampled rows and columns (the oracle quantises
-only the sampled rows of A and W, which is exact since quantisation is per
-row)."""
+fp32 result; no NaN; identical bytes run to run.  Small shapes are checked
+element by element, through the small-M kernel, the tiled kernel, and the
+tiled kernel with its split-K schedule forced (every tile cut into K
+slices); the full decode / prefill sweeps at sampled rows and columns (the
+oracle quantises only the sampled rows of A and W, which is exact since
+quantisation is per row)."""
 
 import numpy as np
 import pytest
@@ -74,7 +76,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("path", [1, 2], ids=["smallM", "tiled"])
+@pytest.mark.parametrize("path", [1, 2, 4], ids=["smallM", "tiled", "tiled_split"])
 @pytest.mark.parametrize("name,M,N,K,kw", SMALL, ids=[c[0] for c in SMALL])
 def test_linear_small_shapes(name, M, N, K, kw, path):
     need_gpu()
@@ -182,7 +184,7 @@ def test_gemm_weight_scales_exact(path, K):
     assert np.array_equal(unsigned_zero(host_bf16_bits(y16)), unsigned_zero(F.f64_to_bf16(dq.T)))
 
 
-@pytest.mark.parametrize("path", [1, 2], ids=["smallM", "tiled"])
+@pytest.mark.parametrize("path", [1, 2, 4], ids=["smallM", "tiled", "tiled_split"])
 @pytest.mark.parametrize("dtype,pad", [(torch.bfloat16, 8), (torch.bfloat16, 3), (torch.float32, 4),
                                        (torch.float32, 1)],
                          ids=["bf16_pad8", "bf16_pad3", "f32_pad4", "f32_pad1"])
@@ -204,6 +206,10 @@ def test_gemm_strided_output(path, dtype, pad):
         mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, dtype, out=buf[:, :N])
         lin = torch.full((M, N + pad), -7.0, dtype=dtype, device="cuda")
         mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, dtype, out=lin[:, :N])
+        # the fp32 and bf16 results the oracle check pairs, on the same schedule
+        lin32 = mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, torch.float32)
+        lin16 = (lin[:, :N].contiguous() if dtype == torch.bfloat16 else
+                 mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, torch.bfloat16))
     finally:
         mx.set_gemm_path(0)
     torch.cuda.synchronize()
@@ -211,6 +217,4 @@ def test_gemm_strided_output(path, dtype, pad):
     assert torch.equal(buf[:, :N].contiguous().view(iview), ref.view(iview))
     assert torch.all(buf[:, N:] == -7.0)
     assert torch.all(lin[:, N:] == -7.0)
-    _check(prob, mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, torch.float32).cpu().numpy(),
-           host_bf16_bits(lin[:, :N].contiguous().to(torch.bfloat16)) if dtype == torch.bfloat16 else
-           host_bf16_bits(mx.mxfp4_linear(dev_bf16(prob["x"]), W.w_pre, W.ws_pre, N, b, torch.bfloat16)))
+    _check(prob, lin32.cpu().numpy(), host_bf16_bits(lin16))
