@@ -628,6 +628,9 @@ def main():
                 tq = quant_time(x, q, s, reps_target=64)
                 fl = 2 * M * N * K
                 prefill_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 2),
+                                         # split-K of the leftover tiles (it needs a workspace)
+                                         schedule="split" if mx.lib().mxfp4_gemm_workspace_bytes(M, N, K)
+                                         else "whole",
                                          tflops=round(fl / t / 1e12, 1),
                                          fp4_peak_frac=round(fl / t / PEAK_FP4, 4),
                                          quant_us=round(tq * 1e6, 2),
