@@ -70,7 +70,9 @@ enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_F32 = 1 };
 /* Static string naming a status code (never NULL). */
 const char* mxfp4_status_str(int status);
 
-/* ABI version: major * 100 + minor. */
+/* ABI version: major * 100 + minor.  1.02: the GEMM entry points may ask
+ * for a workspace (mxfp4_gemm_workspace_bytes) for large M; the debug path
+ * hook takes 3 and 4. */
 int mxfp4_abi_version(void);
 
 /* Bytes of the packed FP4 data / the scales for `rows` x K in `layout`:

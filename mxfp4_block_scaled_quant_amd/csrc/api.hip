@@ -83,7 +83,7 @@ const char* mxfp4_status_str(int status) {
   }
 }
 
-int mxfp4_abi_version(void) { return 101; }
+int mxfp4_abi_version(void) { return 102; }
 
 size_t mxfp4_data_bytes(int64_t rows, int64_t K, int layout) {
   if (rows < 0 || K <= 0 || K % 32) return 0;

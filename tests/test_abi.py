@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.mxfp4_abi_version() == 101
+    assert lib.mxfp4_abi_version() == 102
     for s in range(8):
         assert lib.mxfp4_status_str(s)
     assert lib.mxfp4_status_str(99) == b"unknown status"
