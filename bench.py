@@ -5,6 +5,8 @@
                     [--no-prefill] [--no-bmm]
     python bench.py --traffic-pass          (workload of the counter runs)
     python bench.py --prefill-pass          (workload of the prefill counter runs)
+    python bench.py --hbm-pass              (workload of the quantisation / BMM counter runs)
+    python bench.py --hbm-summary FETCH.csv WRITE.csv CMD...  (CPU only)
     python bench.py --traffic-summary FETCH.csv WRITE.csv CMD...   (CPU only)
     python bench.py --trace-summary STATS.csv TRACE.csv MARKER.csv BENCH.log CMD...  (CPU only)
     python bench.py --prefill-summary TRACE.csv COUNTERS.csv CMD...  (CPU only)
@@ -191,6 +193,118 @@ def traffic_pass():
         del copies, W
         torch.cuda.empty_cache()
     print(json.dumps({"traffic_pass": plan}), flush=True)
+
+
+HBM_PASS_QUANT = [(8192, 5120, "gemm"), (8192, 14336, "gemm"), (8192, 5120, "rowmajor")]
+HBM_PASS_BMM_M = 4096
+HBM_PASS_REPS = 3
+
+
+def _calibration_copy(dev):
+    src = torch.arange(CALIB_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def hbm_pass():
+    """The workload of the quantisation / BMM counter runs (FETCH_SIZE, then
+    WRITE_SIZE, under rocprofv3 --pmc): inputs and weights prepared first,
+    then the calibration copy, then HBM_PASS_REPS launches each of the
+    activation quantisation at the prefill sweep's largest M (both scale
+    layouts) and of the A16WFP4 BMM (K-up and V-up, 16 heads) at M = 4096,
+    on the sweeps' inputs.  The summary reads only the launches after the
+    calibration copy."""
+    import mxfp4_block_scaled_quant_amd as mx
+    from mxfp4_block_scaled_quant_amd import inputs
+    mx.lib()
+    dev = torch.device("cuda:0")
+    quant = []
+    for (M, K, layout) in HBM_PASS_QUANT:
+        x = inputs.bits_to_torch_bf16(inputs.activations(M, K, 3, outliers=True)).to(dev)
+        lay = mx.MXFP4_LAYOUT_GEMM if layout == "gemm" else mx.MXFP4_LAYOUT_ROWMAJOR
+        q, sc = mx.mxfp4_quant_1x32(x, lay)
+        quant.append((x, lay, q, sc))
+    M = HBM_PASS_BMM_M
+    bmm = []
+    for name, N, K, bm in BMM_CASES:
+        w = inputs.bits_to_torch_bf16(inputs.bmm_problem(BMM_HEADS, 1, N, K, 4)["w"].reshape(BMM_HEADS * N, K)).to(dev)
+        W = mx.quantize_weight(w.reshape(BMM_HEADS, N, K))
+        x = inputs.bits_to_torch_bf16(inputs.bmm_problem(BMM_HEADS, M, N, K, 4)["x"]).to(dev)
+        out = (torch.empty((M, BMM_HEADS, N), dtype=torch.bfloat16, device=dev) if bm
+               else torch.empty((BMM_HEADS, M, N), dtype=torch.bfloat16, device=dev))
+        bmm.append((W, x, out, N, bm))
+    torch.cuda.synchronize()
+    _calibration_copy(dev)
+    for (x, lay, q, sc) in quant:
+        for _ in range(HBM_PASS_REPS):
+            mx.mxfp4_quant_1x32(x, lay, q=q, scales=sc)
+    for (W, x, out, N, bm) in bmm:
+        for _ in range(HBM_PASS_REPS):
+            mx.a16wfp4_bmm(x, W.w_pre, W.ws_pre, N, out=out, batch_major=bm)
+    torch.cuda.synchronize()
+    print(json.dumps({"hbm_pass": [list(c) for c in HBM_PASS_QUANT] + [c[0] for c in BMM_CASES]}), flush=True)
+
+
+HBM_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                      "quant_and_bmm__hbm_traffic.md")
+
+
+def hbm_summary(fetch_csv, write_csv, command):
+    """The committed HBM-traffic summary of hbm_pass (HBM_MD): per launch,
+    FETCH_SIZE and WRITE_SIZE scaled by the calibration copy, against the
+    algorithmic bytes each kernel must read and write."""
+    per = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r[2] == name]
+        calib = [v for _, k, _, v in rows if "bitwise_not" in k]
+        last_calib = max(d for d, k, _, _ in rows if "bitwise_not" in k)
+        work = [(k, v) for d, k, _, v in rows if d > last_calib]
+        per[name] = (calib, work)
+    f_cal, f_work = per["FETCH_SIZE"]
+    w_cal, w_work = per["WRITE_SIZE"]
+    ff = CALIB_BYTES / (np.mean(f_cal) * 1024)
+    wf = CALIB_BYTES / (np.mean(w_cal) * 1024)
+    n = HBM_PASS_REPS
+    cases = []
+    for (M, K, layout) in HBM_PASS_QUANT:
+        cases.append((f"quant {layout} M={M} K={K}", 2 * M * K, 17 * M * K / 32))
+    M = HBM_PASS_BMM_M
+    for name, N, K, bm in BMM_CASES:
+        cases.append((f"BMM {name} M={M} N={N} K={K} (16 heads)",
+                      BMM_HEADS * (2 * M * K + N * K * 17 / 32), BMM_HEADS * 2 * M * N))
+    assert len(f_work) == len(w_work) == n * len(cases), (len(f_work), len(w_work))
+    rows = []
+    for i, (label, alg_r, alg_w) in enumerate(cases):
+        fk = float(np.mean([v for _, v in f_work[i * n:(i + 1) * n]]))
+        wk = float(np.mean([v for _, v in w_work[i * n:(i + 1) * n]]))
+        kern = f_work[i * n][0].split("(")[0].replace("void ", "")
+        rows.append(dict(case=label, kernel=kern, fetch_bytes=round(fk * 1024 * ff),
+                         write_bytes=round(wk * 1024 * wf), algorithmic_read=round(alg_r),
+                         algorithmic_write=round(alg_w),
+                         read_ratio=round(fk * 1024 * ff / alg_r, 4), write_ratio=round(wk * 1024 * wf / alg_w, 4)))
+    lines = ["# Activation quantisation and A16WFP4 BMM — HBM traffic", "",
+             "Two counter runs of the same workload (`python bench.py --hbm-pass`: a calibration",
+             f"copy of {CALIB_BYTES >> 20} MiB, then {n} launches of each case on the sweeps' inputs):", "",
+             "```", *command, "```", "",
+             "Each counter is scaled by what it reads for the calibration copy (known bytes",
+             "read and written) and averaged over the case's launches. Algorithmic bytes:",
+             "quantisation reads 2MK (bf16) and writes 17MK/32 (codes and scales, before",
+             "padding); the BMM reads its activations and the preshuffled weights",
+             "(16 heads) and writes its bf16 output.", "",
+             "| Case | Kernel | HBM read B | algorithmic | ratio | HBM write B | algorithmic | ratio |",
+             "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['case']} | `{r['kernel']}` | {r['fetch_bytes']} | {r['algorithmic_read']} | "
+                     f"{r['read_ratio']} | {r['write_bytes']} | {r['algorithmic_write']} | {r['write_ratio']} |")
+    lines += ["", f"Calibration: FETCH_SIZE scale {ff:.4f}, WRITE_SIZE scale {wf:.4f}.", "",
+              "```json", json.dumps(dict(cases=rows, fetch_scale=round(ff, 4), write_scale=round(wf, 4))), "```", ""]
+    with open(HBM_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {HBM_MD}")
+    for r in rows:
+        print(r)
 
 
 PREFILL_PASS_M = 8192
@@ -415,6 +529,10 @@ def prefill_counter_summary(trace_csv, pmc_csv, command):
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--hbm-pass":
+        return hbm_pass()
+    if len(sys.argv) > 1 and sys.argv[1] == "--hbm-summary":
+        return hbm_summary(sys.argv[2], sys.argv[3], sys.argv[4:])
     if len(sys.argv) > 1 and sys.argv[1] == "--prefill-summary":
         return prefill_counter_summary(sys.argv[2], sys.argv[3], sys.argv[4:])
     if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
