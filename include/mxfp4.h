@@ -72,7 +72,7 @@ const char* mxfp4_status_str(int status);
 
 /* ABI version: major * 100 + minor.  1.02: the GEMM entry points may ask
  * for a workspace (mxfp4_gemm_workspace_bytes) for large M; the debug path
- * hook takes 3 and 4. */
+ * hook takes 3 to 6. */
 int mxfp4_abi_version(void);
 
 /* Bytes of the packed FP4 data / the scales for `rows` x K in `layout`:
@@ -89,8 +89,9 @@ size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K);
 /* Workspace bytes mxfp4_gemm_a4w4 and mxfp4_gemm_a4w4_mxfp4_out need for
  * this shape: 0 where the GEMM runs on whole output tiles (every M <= 64
  * call, and most larger ones), else the split schedule's (see
- * mxfp4_gemm_a4w4), sized for up to 256 compute units: 256 KiB per
- * workgroup (up to 64 MiB) plus 4 bytes per split tile and per workgroup.
+ * mxfp4_gemm_a4w4), sized for up to 256 compute units: one fp32 output
+ * tile per workgroup (256 KiB, or 128 KiB with 128-wide tiles; up to 64 MiB)
+ * plus 4 bytes per split tile and per workgroup.
  * Depends on the mxfp4_debug_set_gemm_path setting.  0 on invalid shapes. */
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -158,8 +159,10 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
  *             and are not kept.  Calls that overlap in time (other streams)
  *             need workspaces of their own.
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
- * For M > 64, where whole 256 x 256 output tiles would leave the last round
- * of compute units at most half full and K is long enough to pay for it,
+ * For M > 64 the output is cut into 256 x 256 tiles, or 256 x 128 where the
+ * wider ones would leave most compute units idle (measured rule).  Where
+ * whole tiles would leave the last round of compute units at most half full
+ * and K is long enough to pay for it,
  * the tiles short of whole rounds are each cut along K into equal slices
  * for the otherwise idle workgroups (split-K): a split tile's fp32 partial
  * sums meet in the workspace and are added in K order by the last
@@ -284,10 +287,11 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm,
  * Test hook, not part of the method: force the GEMM kernel used by
  * mxfp4_gemm_a4w4 -- 1 = the small-M streaming kernel (M <= 64 only; larger
  * M still uses the tiled kernel), 2 = the LDS-tiled kernel, 0 = choose by M
- * (the default); 3 = the tiled kernel on whole tiles only, 4 = the tiled
- * kernel with the split schedule wherever the tiles leave a round of
- * compute units part-empty and a tile has more than 512 of K (also for the
- * tiled kernel's share of mxfp4_linear and mxfp4_linear_prequantized).  Process-wide and not synchronised with calls
+ * (the default); 3 = the tiled kernel on whole 256-wide tiles only, 4 = the
+ * tiled kernel with the split schedule wherever the tiles leave a round of
+ * compute units part-empty and a tile has more than 512 of K; 5 and 6 = the
+ * same with 128-wide tiles (3-6 also for the tiled kernel's share of
+ * mxfp4_linear and mxfp4_linear_prequantized).  Process-wide and not synchronised with calls
  * in flight on other threads; query workspace sizes after setting it.
  * Returns MXFP4_ERR_ARG for other values.
  */

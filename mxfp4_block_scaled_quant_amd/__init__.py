@@ -141,7 +141,8 @@ def weight_scale_bytes(batch: int, N: int, K: int) -> int:
 
 def set_gemm_path(path: int) -> None:
     """Test hook: 1 forces the small-M kernel (M <= 64), 2 the tiled kernel, 0 = by M;
-    3 the tiled kernel on whole tiles only, 4 with the split (split-K) schedule."""
+    3 the tiled kernel on whole 256-wide tiles only, 4 with the split (split-K)
+    schedule; 5 and 6 the same with 128-wide tiles."""
     _check("mxfp4_debug_set_gemm_path", lib().mxfp4_debug_set_gemm_path(path))
 
 

@@ -462,7 +462,7 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, cons
 // Test hook: force the decode (1) or prefill (2) GEMM kernel, 0 = by M; 3
 // and 4: the prefill kernel with whole tiles only / the split schedule.
 int mxfp4_debug_set_gemm_path(int path) {
-  if (path < 0 || path > 4) return MXFP4_ERR_ARG;
+  if (path < 0 || path > 6) return MXFP4_ERR_ARG;
   set_gemm_path_override(path);
   return MXFP4_OK;
 }

@@ -49,52 +49,72 @@
 #include "mxfp4_device.h"
 #include "mxfp4_launch.h"
 
+#ifndef MXFP4_PREFILL_BN
+#define MXFP4_PREFILL_BN 256
+#endif
+#if MXFP4_PREFILL_BN == 256
+#define MXFP4_PREFILL_KERNEL gemm_prefill_kernel
+#define MXFP4_PREFILL_TILES launch_prefill_tiles_256
+#else
+#define MXFP4_PREFILL_KERNEL gemm_prefill_n128_kernel
+#define MXFP4_PREFILL_TILES launch_prefill_tiles_128
+#endif
+
 namespace mxfp4 {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256;
+// Output tile width: 256 (this file as it stands) or 128 (the same source
+// built again with MXFP4_PREFILL_BN = 128, for M where 256-wide tiles
+// leave most compute units idle).  The tile is 256 rows either way.
+constexpr int kBM = 256, kBN = MXFP4_PREFILL_BN;
+static_assert(kBN == 256 || kBN == 128, "tile width");
 constexpr int kTilesA = kBM / 16;            // 16 activation units per K-step
-constexpr int kTilesB = kBN / 16;            // 16 weight units per K-step
-constexpr int kUnits = kTilesA + kTilesB;    // 32 units of 1 KiB per K-step
+constexpr int kTilesB = kBN / 16;            // 16 (8) weight units per K-step
+constexpr int kUnits = kTilesA + kTilesB;    // 32 (24) units of 1 KiB per K-step
 constexpr int kBufs = 4;                     // LDS stages (K-steps in flight)
 constexpr int kWaves = 8;
-constexpr int kLoadsPerWave = kUnits / kWaves;  // 4 buffer->LDS loads per wave per step
-constexpr int kWM = 8, kWN = 4;                 // wave tile: 8 x 4 MFMA tiles (128 x 64)
+constexpr int kLoadsPerWave = kUnits / kWaves;  // 4 (3) buffer->LDS loads per wave per step
+constexpr int kWM = 8, kWN = kBN / 64;          // wave tile: 8 x 4 (8 x 2) MFMA tiles, 128 x 64 (128 x 32)
+constexpr int kScaleLoads = kUnits / 4;         // scale loads of a group (4 tiles each): one per wave (6 of 8)
 constexpr int kGroupM = 8;                   // row-tiles per ordering group
 // LDS: unit u of stage b at u * 4 KiB + b * 1 KiB (so a wave reaches its
 // fragments in all four stages from one base register), then the scales of
-// one group: 16 activation tiles, then 16 weight strips, 256 bytes each; then
-// each wave's 64 bias values of the tile (256 bytes per wave); then each
-// wave's 16-row bf16 staging area of the epilogue.
-constexpr int kStageBytes = kUnits * kBufs * 1024;  // 128 KiB
+// one group: 16 activation tiles, then the weight strips, 256 bytes each;
+// then each wave's bias values of the tile (256 bytes per wave); then each
+// wave's 16-row bf16 staging area of the epilogue; then the arrival rank;
+// then (128-wide) a dummy 1 KiB for the scale loads of waves that have none.
+constexpr int kStageBytes = kUnits * kBufs * 1024;  // 128 (96) KiB
 constexpr int kScaleLds = kStageBytes;
-constexpr int kBiasLds = kScaleLds + kUnits * 256;  // + 8 KiB
-constexpr int kEpiRowB = 144;                        // epilogue staging row stride (bytes)
+constexpr int kBiasLds = kScaleLds + kUnits * 256;  // + 8 (6) KiB
+constexpr int kEpiRowB = kWN * 32 + 16;              // epilogue staging row stride (bytes)
 constexpr int kEpiLds = kBiasLds + kWaves * 256;     // + 2 KiB
-constexpr int kSkLds = kEpiLds + kWaves * 16 * kEpiRowB;     // + 18 KiB
-constexpr int kLdsBytes = kSkLds + 16;                        // + the arrival rank: 156 KiB in all
+constexpr int kSkLds = kEpiLds + kWaves * 16 * kEpiRowB;     // + 18 (10) KiB
+constexpr int kDummyLds = kSkLds + 16;
+constexpr int kLdsBytes = kDummyLds + (kScaleLoads < kWaves ? 1024 : 0);  // 156 KiB in all (113)
 static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 #ifndef MXFP4_STORE_AUX
 #define MXFP4_STORE_AUX 0
 #endif
-// Cache policy of the staged bf16 epilogue's stores (whole 128-byte row
-// pieces, not read again by this kernel): non-temporal.  Measured on MI355X:
-// 1-2% faster at five of the six M >= 2048 prefill shapes (e.g. M = 8192,
-// N = 5120, K = 14336 295 -> 289 us), no change at the sixth.
-constexpr int kStagedStoreAux = 2;
+// Cache policy of the staged bf16 epilogue's stores (not read again by this
+// kernel): non-temporal where a wave's row piece is a whole 128-byte line
+// (256 wide).  Measured on MI355X: 1-2% faster at five of the six M >= 2048
+// prefill shapes (e.g. M = 8192, N = 5120, K = 14336 295 -> 289 us), no
+// change at the sixth; on half lines non-temporal stores were slower.
+constexpr int kStagedStoreAux = kWN == 4 ? 2 : 0;
+// Staged epilogues: a wave's 16-row block is read back as 16-byte pieces of
+// whole rows, kLpr lanes per row (16 kWN columns of bf16), so each lane
+// holds 8 consecutive columns of a row, kWN / 2 pieces per block.
+constexpr int kLpr = 2 * kWN;
+constexpr int kLprShift = kWN == 4 ? 3 : 2;
 
-// Split schedule of one launch: tiles [0, r) of the tile order are cut into
-// s slices each (r = 0: whole tiles only).  Workspace: one fp32 part slot of
-// a tile per slice (slot = the slice's workgroup), then an arrival counter
-// per split tile and a ready flag per slot, zeroed before every launch.
-struct SkArgs {
-  int r, s;
-  uint8_t* part;
-  uint32_t* ctrl;
-  uint32_t* flags;
-};
-constexpr uint32_t kPartBytes = kBM * kBN * 4;  // 256 KiB: one tile's fp32 accumulators
+// Split schedule of one launch (PrefillSplit): tiles [0, r) of the tile
+// order are cut into s slices each (r = 0: whole tiles only).  Workspace:
+// one fp32 part slot of a tile per slice (slot = the slice's workgroup),
+// then an arrival counter per split tile and a ready flag per slot, zeroed
+// before every launch.
+using SkArgs = PrefillSplit;
+constexpr uint32_t kPartBytes = kBM * kBN * 4;  // 256 (128) KiB: one tile's fp32 accumulators
 // Cache policy of the part stores and loads: device scope (sc1), as the
 // memory model's relaxed device-scope atomics: written through, and read
 // past, the XCD-local caches, so another XCD's part is seen once its flag
@@ -183,15 +203,18 @@ __device__ __forceinline__ Tile work_at(const GemmArgs& p, const SkArgs& sk, con
 // goes in the scalar offset (in range whenever the descriptor is not empty).
 __device__ __forceinline__ void issue_unit(const GemmArgs& p, const Tile& tl, int J, int t, int q, int wv,
                                            uint32_t lane16) {
-  const bool is_a = wv < 4;
+  // unit gu of the step's kUnits (activation units first): wave wv loads
+  // units wv * kLoadsPerWave + q (all activation units in waves 0-3 at
+  // 256 wide; at 128 wide wave 5 loads one of each kind)
+  const int gu = wv * kLoadsPerWave + q;
+  const bool is_a = gu < kTilesA;
   const int first = is_a ? tl.ms : tl.s0;
   const int count = t < p.Kt ? (is_a ? tl.mstrips : tl.strips) : 0;
   const uint8_t* base = is_a ? p.a : p.w;
-  const int u = (wv & 3) * kLoadsPerWave + q;
-  const int fb = is_a ? 0 : kTilesA;
+  const int u = is_a ? gu : gu - kTilesA;
   const uint32_t row_bytes = (uint32_t)p.Kt * 1024u;
   const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)(first + u) * row_bytes, u < count ? row_bytes : 0u);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(((fb + u) * kBufs + J) * 1024), 16, lane16, t << 10, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at((gu * kBufs + J) * 1024), 16, lane16, t << 10, 0, 0);
 }
 
 __device__ __forceinline__ void issue_step(const GemmArgs& p, const Tile& tl, int J, int t, int wv,
@@ -201,37 +224,42 @@ __device__ __forceinline__ void issue_step(const GemmArgs& p, const Tile& tl, in
 }
 
 // This wave's one buffer->LDS load of the scales of group g of tile `tl`:
-// waves 0-3 fetch 4 activation tiles each, waves 4-7 4 weight strips each
-// (lane l: tile l/16, bytes (l%16)*16 of its 256).  Tiles past the last
-// strip fall outside the descriptor through the vector offset (zeros), and
-// an empty descriptor covers groups past K; the group goes in the scalar
-// offset.
+// wave w fetches the 4 tiles 4w..4w+3 of the step's units (activation tiles
+// first, then weight strips; lane l: tile l/16, bytes (l%16)*16 of its
+// 256).  Tiles past the last strip fall outside the descriptor through the
+// vector offset (zeros), and an empty descriptor covers groups past K (the
+// group goes in the scalar offset) and, at 128 wide, waves 6-7, whose zeros
+// land in a dummy area: every wave issues the load, so the waits count the
+// same operations in every wave.
 __device__ __forceinline__ void issue_scales(const GemmArgs& p, const Tile& tl, int g, int wv) {
-  const bool is_a = wv < 4;
+  const int gt = wv * 4;
+  const bool is_a = gt < kTilesA;
+  const bool none = gt >= kUnits;
   const int first = is_a ? tl.ms : tl.s0;
-  const int count = is_a ? tl.mstrips : tl.strips;
-  const int rt0 = (wv & 3) * 4;
+  const int count = none ? 0 : is_a ? tl.mstrips : tl.strips;
+  const int rt0 = is_a ? gt : gt - kTilesA;
   const int G = p.G;
   const int left = __builtin_amdgcn_readfirstlane(max(0, count - rt0));
   const __amdgpu_buffer_rsrc_t r =
       make_rsrc((is_a ? p.as : p.ws) + (int64_t)(first + rt0) * G * 256, g < G ? (uint32_t)(left * G * 256) : 0u);
-  const uint32_t lds = kScaleLds + ((is_a ? 0 : kTilesA) + rt0) * 256;
+  const uint32_t lds = none ? (uint32_t)kDummyLds : (uint32_t)(kScaleLds + gt * 256);
   const uint32_t l = lane_here();
   const uint32_t svoff = (l >> 4) * (uint32_t)(G * 256) + (l & 15) * 16;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(lds), 16, svoff, g << 8, 0, 0);
 }
 
-// This wave's buffer->LDS load of the bias of its 64 output columns of tile
-// `tl` (lanes 0-31 one bf16 pair each; N is a multiple of 4 here, so the
-// window ends on a whole pair; no bias: an empty window, zeros).
+// This wave's buffer->LDS load of the bias of its 16 kWN output columns of
+// tile `tl` (lanes 0 .. 8 kWN - 1 one bf16 pair each; N is a multiple of 4
+// here, so the window ends on a whole pair; no bias: an empty window,
+// zeros).
 __device__ __forceinline__ void issue_bias(const GemmArgs& p, const Tile& tl, int wv, int wn) {
   const uint32_t lane = lane_here();
   const int col0 = (tl.s0 + wn * kWN) * 16;
-  const int cols = __builtin_amdgcn_readfirstlane(p.bias ? max(0, min(64, p.N - col0)) : 0);
+  const int cols = __builtin_amdgcn_readfirstlane(p.bias ? max(0, min(16 * kWN, p.N - col0)) : 0);
   const __amdgpu_buffer_rsrc_t r =
       make_rsrc(p.bias ? (const void*)(p.bias + col0) : (const void*)p.a, (uint32_t)(cols * 2));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(kBiasLds + wv * 256), 4, lane < 32 ? lane * 4 : kOOB, 0, 0,
-                                           0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_at(kBiasLds + wv * 256), 4, lane < 8 * kWN ? lane * 4 : kOOB, 0,
+                                           0, 0);
 }
 
 // LDS reads are written as inline assembly with hand-counted lgkmcnt
@@ -268,10 +296,17 @@ __device__ __forceinline__ void wait_lgkm(v4i& a, v4i& b, v4i& c, v4i& d) {
 }
 template <int N>
 __device__ __forceinline__ void wait_lgkm_scales(uint32_t (&sa)[kWM], uint32_t (&sb)[kWN]) {
-  asm volatile("s_waitcnt lgkmcnt(%12)"
-               : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sa[4]), "+v"(sa[5]), "+v"(sa[6]),
-                 "+v"(sa[7]), "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]), "+v"(sb[3])
-               : "i"(N));
+  if constexpr (kWN == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%12)"
+                 : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sa[4]), "+v"(sa[5]), "+v"(sa[6]),
+                   "+v"(sa[7]), "+v"(sb[0]), "+v"(sb[1]), "+v"(sb[2]), "+v"(sb[3])
+                 : "i"(N));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(%10)"
+                 : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sa[4]), "+v"(sa[5]), "+v"(sa[6]),
+                   "+v"(sa[7]), "+v"(sb[0]), "+v"(sb[1])
+                 : "i"(N));
+  }
 }
 
 template <int N>
@@ -322,8 +357,10 @@ template <int BUF>
 __device__ __forceinline__ void read_first_half(v4i (&af)[kWM], v4i (&bf)[kWN], const ReadAddr& ra) {
   ds_read16<0 * 4096 + BUF * 1024>(bf[0], ra.b);
   ds_read16<1 * 4096 + BUF * 1024>(bf[1], ra.b);
-  ds_read16<2 * 4096 + BUF * 1024>(bf[2], ra.b);
-  ds_read16<3 * 4096 + BUF * 1024>(bf[3], ra.b);
+  if constexpr (kWN == 4) {
+    ds_read16<2 * 4096 + BUF * 1024>(bf[2], ra.b);
+    ds_read16<3 * 4096 + BUF * 1024>(bf[3], ra.b);
+  }
   ds_read16<0 * 4096 + BUF * 1024>(af[0], ra.a);
   ds_read16<1 * 4096 + BUF * 1024>(af[1], ra.a);
   ds_read16<2 * 4096 + BUF * 1024>(af[2], ra.a);
@@ -351,8 +388,10 @@ __device__ __forceinline__ void read_scales(uint32_t (&sa)[kWM], uint32_t (&sb)[
   ds_read4<7 * 256>(sa[7], a);
   ds_read4<0 * 256>(sb[0], b);
   ds_read4<1 * 256>(sb[1], b);
-  ds_read4<2 * 256>(sb[2], b);
-  ds_read4<3 * 256>(sb[3], b);
+  if constexpr (kWN == 4) {
+    ds_read4<2 * 256>(sb[2], b);
+    ds_read4<3 * 256>(sb[3], b);
+  }
 }
 
 // MFMAs of activation rows I0..I0+3 of one K-step: acc[i][j] (+)= W-strip j
@@ -444,7 +483,7 @@ __device__ __forceinline__ void main_step(const GemmArgs& p, Pipe& P, v4i (&bf_c
   issue_unit(p, dt, J, td, 2, wv, lane16);
   __builtin_amdgcn_sched_barrier(0);
   mfma_row<J, 7>(P.acc, P.af, bf_cur, P.sa, P.sb);
-  issue_unit(p, dt, J, td, 3, wv, lane16);
+  if constexpr (kLoadsPerWave == 4) issue_unit(p, dt, J, td, 3, wv, lane16);
   __builtin_amdgcn_sched_barrier(0);
   if (J == 3) read_scales(P.sa, P.sb, wm, wn);
   read_second_half<kNext>(P.af, ra);
@@ -468,8 +507,9 @@ struct OutMode {
   static constexpr bool kFp4 = MODE == 4;
   static constexpr bool kStaged = MODE == 0 || MODE == 4;
   static constexpr bool kVec = MODE == 2;
-  // per 16-row block: 2 row-piece stores (bf16), or 2 code + 2 scale stores (MXFP4)
-  static constexpr int kStores = MODE == 0 ? 2 * kWM : kFp4 ? 4 * kWM : kVec ? kWM * kWN : 4 * kWM * kWN;
+  // per 16-row block: kWN / 2 row-piece stores (bf16), or as many code and
+  // as many scale stores (MXFP4)
+  static constexpr int kStores = MODE == 0 ? kWN / 2 * kWM : kFp4 ? kWN * kWM : kVec ? kWM * kWN : 4 * kWM * kWN;
   static constexpr bool kDrain = !kStaged && !kVec;
   static constexpr int kInFlight = kDrain ? 0 : kStores;  // stores the next tile's waits count
   static constexpr bool kBiasLds = !kDrain;  // bias staged in LDS (whole pairs: N % 4 == 0)
@@ -481,27 +521,31 @@ __device__ __forceinline__ void read_bias(v2i (&bl)[kWN], int wv, int lane) {
   const uint32_t ba = kBiasLds + (uint32_t)(lane >> 4) * 8 + (uint32_t)wv * 256;
   ds_read8<0>(bl[0], ba);
   ds_read8<32>(bl[1], ba);
-  ds_read8<64>(bl[2], ba);
-  ds_read8<96>(bl[3], ba);
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bl[0]), "+v"(bl[1]), "+v"(bl[2]), "+v"(bl[3]));
+  if constexpr (kWN == 4) {
+    ds_read8<64>(bl[2], ba);
+    ds_read8<96>(bl[3], ba);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bl[0]), "+v"(bl[1]), "+v"(bl[2]), "+v"(bl[3]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bl[0]), "+v"(bl[1]));
+  }
 }
 
 // Staged bf16 epilogue (mode 0).  Per 16-row block i: each lane writes its
-// 4 x 4 results (bias added in fp32, one rounding) to the wave's staging
-// rows, then reads back two 16-byte pieces of whole rows (8 lanes per
-// 128-byte row) and stores them.  The wave's own LDS operations run in
-// order, so no barrier is needed.
+// 4 x kWN results (bias added in fp32, one rounding) to the wave's staging
+// rows, then reads back kWN / 2 16-byte pieces of whole rows (kLpr lanes
+// per row) and stores them.  The wave's own LDS operations run in order, so
+// no barrier is needed.
 __device__ __forceinline__ void epilogue_staged(const GemmArgs& p, const Tile& tl, v4f (&acc)[kWM][kWN], int wv,
                                                 int wm, int wn) {
   const int lane = (int)lane_here();
   const int row0 = tl.ms * 16 + wm * 128;
-  const int n = (tl.s0 + wn * kWN) * 16 + (lane & 7) * 8;  // this lane's 8 stored columns
+  const int n = (tl.s0 + wn * kWN) * 16 + (lane & (kLpr - 1)) * 8;  // this lane's 8 stored columns
   v2i bl[kWN];
   read_bias(bl, wv, lane);
   const uint32_t wst = kEpiLds + (uint32_t)wv * 16 * kEpiRowB;
   const uint32_t waddr = wst + (uint32_t)(lane & 15) * kEpiRowB + (uint32_t)(lane >> 4) * 8;
-  const uint32_t raddr = wst + (uint32_t)(lane >> 3) * kEpiRowB + (uint32_t)(lane & 7) * 16;
-  const uint32_t voff0 = n < p.N ? (uint32_t)((lane >> 3) * p.ldo + n) * 2 : kOOB;
+  const uint32_t raddr = wst + (uint32_t)(lane >> kLprShift) * kEpiRowB + (uint32_t)(lane & (kLpr - 1)) * 16;
+  const uint32_t voff0 = n < p.N ? (uint32_t)((lane >> kLprShift) * p.ldo + n) * 2 : kOOB;
   const uint32_t voff1 = n < p.N ? voff0 + (uint32_t)(8 * p.ldo) * 2 : kOOB;
   uint8_t* const out = reinterpret_cast<uint8_t*>(p.out);
 #pragma unroll
@@ -520,15 +564,19 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& p, const Tile& t
     }
     v4i r0, r1;
     ds_read16<0>(r0, raddr);
-    ds_read16<8 * kEpiRowB>(r1, raddr);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1));
+    if constexpr (kWN == 4) {
+      ds_read16<8 * kEpiRowB>(r1, raddr);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1));
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0));
+    }
     const int rb = row0 + i * 16;
     // (uniform, but max/min would be computed in a vector register, which
     // would turn every store into a waterfall loop over the descriptor)
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, p.M - rb)));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + (int64_t)rb * p.ldo * 2, (uint32_t)(nrows * p.ldo * 2));
     __builtin_amdgcn_raw_buffer_store_b128(r0, ro, voff0, 0, kStagedStoreAux);
-    __builtin_amdgcn_raw_buffer_store_b128(r1, ro, voff1, 0, kStagedStoreAux);
+    if constexpr (kWN == 4) __builtin_amdgcn_raw_buffer_store_b128(r1, ro, voff1, 0, kStagedStoreAux);
   }
 }
 
@@ -544,17 +592,17 @@ __device__ __forceinline__ void epilogue_fp4(const GemmArgs& p, const Tile& tl, 
                                              int wm, int wn) {
   const int lane = (int)lane_here();
   const int row0 = tl.ms * 16 + wm * 128;
-  const int n = (tl.s0 + wn * kWN) * 16 + (lane & 7) * 8;  // this lane's 8 columns
+  const int n = (tl.s0 + wn * kWN) * 16 + (lane & (kLpr - 1)) * 8;  // this lane's 8 columns
   v2i bl[kWN];
   read_bias(bl, wv, lane);
   const uint32_t wst = kEpiLds + (uint32_t)wv * 16 * kEpiRowB;
   const uint32_t waddr = wst + (uint32_t)(lane & 15) * kEpiRowB + (uint32_t)(lane >> 4) * 8;
-  const uint32_t raddr = wst + (uint32_t)(lane >> 3) * kEpiRowB + (uint32_t)(lane & 7) * 16;
+  const uint32_t raddr = wst + (uint32_t)(lane >> kLprShift) * kEpiRowB + (uint32_t)(lane & (kLpr - 1)) * 16;
   const uint32_t ldq = (uint32_t)p.ldo, lds = (uint32_t)p.ldos;
-  const uint32_t doff0 = n < p.N ? (uint32_t)(lane >> 3) * ldq + (uint32_t)(n >> 1) : kOOB;
+  const uint32_t doff0 = n < p.N ? (uint32_t)(lane >> kLprShift) * ldq + (uint32_t)(n >> 1) : kOOB;
   const uint32_t doff1 = n < p.N ? doff0 + 8 * ldq : kOOB;
   const bool first = (lane & 3) == 0;
-  const uint32_t soff0 = (n < p.N && first) ? (uint32_t)(lane >> 3) * lds + (uint32_t)(n >> 5) : kOOB;
+  const uint32_t soff0 = (n < p.N && first) ? (uint32_t)(lane >> kLprShift) * lds + (uint32_t)(n >> 5) : kOOB;
   const uint32_t soff1 = (n < p.N && first) ? soff0 + 8 * lds : kOOB;
   uint8_t* const out = reinterpret_cast<uint8_t*>(p.out);
 #pragma unroll
@@ -573,21 +621,30 @@ __device__ __forceinline__ void epilogue_fp4(const GemmArgs& p, const Tile& tl, 
     }
     v4i r0, r1;
     ds_read16<0>(r0, raddr);
-    ds_read16<8 * kEpiRowB>(r1, raddr);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1));
-    const uint32_t b0 = e8m0_of_amax_bits(quad_amax_bits((uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w));
-    const uint32_t b1 = e8m0_of_amax_bits(quad_amax_bits((uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w));
-    const uint32_t c0 = e2m1_pack8((uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w, e8m0_value(b0));
-    const uint32_t c1 = e2m1_pack8((uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w, e8m0_value(b1));
+    if constexpr (kWN == 4) {
+      ds_read16<8 * kEpiRowB>(r1, raddr);
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1));
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0));
+    }
     const int rb = row0 + i * 16;
     // (uniform: see epilogue_staged)
     const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(16, p.M - rb)));
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(out + (int64_t)rb * p.ldo, (uint32_t)nrows * ldq);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.out_scales + (int64_t)rb * p.ldos, (uint32_t)nrows * lds);
-    __builtin_amdgcn_raw_buffer_store_b32(c0, rd, doff0, 0, MXFP4_STORE_AUX);
-    __builtin_amdgcn_raw_buffer_store_b32(c1, rd, doff1, 0, MXFP4_STORE_AUX);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b0, rs, soff0, 0, MXFP4_STORE_AUX);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b1, rs, soff1, 0, MXFP4_STORE_AUX);
+    const uint32_t b0 = e8m0_of_amax_bits(quad_amax_bits((uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w));
+    const uint32_t c0 = e2m1_pack8((uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w, e8m0_value(b0));
+    if constexpr (kWN == 4) {
+      const uint32_t b1 = e8m0_of_amax_bits(quad_amax_bits((uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w));
+      const uint32_t c1 = e2m1_pack8((uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w, e8m0_value(b1));
+      __builtin_amdgcn_raw_buffer_store_b32(c0, rd, doff0, 0, MXFP4_STORE_AUX);
+      __builtin_amdgcn_raw_buffer_store_b32(c1, rd, doff1, 0, MXFP4_STORE_AUX);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b0, rs, soff0, 0, MXFP4_STORE_AUX);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b1, rs, soff1, 0, MXFP4_STORE_AUX);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(c0, rd, doff0, 0, MXFP4_STORE_AUX);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)b0, rs, soff0, 0, MXFP4_STORE_AUX);
+    }
   }
 }
 
@@ -703,7 +760,7 @@ __device__ __forceinline__ void drop_stores() {
 template <bool kAdd>
 __device__ __forceinline__ void add_part(v4f (&acc)[kWM][kWN], __amdgpu_buffer_rsrc_t rp, uint32_t o) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
+  for (int h = 0; h < kWM * kWN / 8; ++h) {
     v4i v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -789,7 +846,7 @@ __global__ void sk_clear_kernel(uint32_t* words, int n) {
 }  // namespace
 
 template <int MODE>
-__global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int tiles_m, int tiles_n, SkArgs sk) {
+__global__ __launch_bounds__(512, 1) void MXFP4_PREFILL_KERNEL(GemmArgs p, int tiles_m, int tiles_n, SkArgs sk) {
   constexpr int kStores = OutMode<MODE>::kInFlight;
   constexpr bool kBiasLds = OutMode<MODE>::kBiasLds;
   // The stage and scale addresses above are absolute LDS addresses: this is
@@ -875,17 +932,41 @@ __global__ __launch_bounds__(512, 1) void gemm_prefill_kernel(GemmArgs p, int ti
   wait_vm<0>();
 }
 
+// This tile width's launch on `grid` workgroups: the split schedule's
+// counters cleared first (a kernel, not a memset: the launch may be
+// captured into a graph), then the GEMM in the output mode the call needs.
+hipError_t MXFP4_PREFILL_TILES(const GemmArgs& p, int grid, const PrefillSplit& sk, hipStream_t stream) {
+  const int tiles_m = (p.M + kBM - 1) / kBM;
+  const int tiles_n = (p.Ns * 16 + kBN - 1) / kBN;
+  if (sk.r) sk_clear_kernel<<<1, 256, 0, stream>>>(sk.ctrl, sk.r + grid);
+  const bool a16 = ((uintptr_t)p.out & 15) == 0;
+  const int mode = p.out_fp4 ? 4
+                 : p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
+                             : ((p.N % 8 == 0 && p.ldo % 8 == 0 && a16) ? 0 : 1);
+  const dim3 g((unsigned)grid), b(64 * kWaves);
+  switch (mode) {
+    case 0: MXFP4_PREFILL_KERNEL<0><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    case 1: MXFP4_PREFILL_KERNEL<1><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    case 2: MXFP4_PREFILL_KERNEL<2><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    case 4: MXFP4_PREFILL_KERNEL<4><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+    default: MXFP4_PREFILL_KERNEL<3><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
+  }
+  return hipGetLastError();
+}
+
+#if MXFP4_PREFILL_BN == 256
 namespace {
 
 constexpr int kMaxSkGrid = 256;  // the split schedule's workgroups (and workspace) at most
 
 struct PrefillPlan {
-  int grid, r, s;
+  int bn, grid, r, s;
   size_t bytes;  // workspace
 };
 
-// sched: 0 = by the measured rule below, 1 = whole tiles, 2 = split wherever
-// the tiles leave a round part-empty and a tile has more than one group.
+// The plan at tile width bn.  split: 0 = by the measured rule below, 1 =
+// whole tiles, 2 = split wherever the tiles leave a round part-empty and a
+// tile has more than one group.
 // The rule, from both schedules timed on MI355X (256 CUs) at M = 512 ...
 // 8192 for (N, K) = (14336, 5120), (5120, 14336), (34816, 5120): moving a
 // slice's 256 KiB part costs about as much as 7 groups of MFMAs, so split
@@ -895,67 +976,76 @@ struct PrefillPlan {
 // idle).  Measured: K = 14336 gains 6-20% (M = 512: 79.9 -> 64.3 us; M =
 // 8192: 289 -> 267 us); K = 5120 (slices of at most 5 groups) loses 3-39%
 // and stays on whole tiles.
-PrefillPlan plan_prefill(int M, int N, int K, int cus, int sched) {
+PrefillPlan plan_width(int bn, int M, int N, int K, int cus, int split) {
   const int tiles_m = (M + kBM - 1) / kBM;
-  const int tiles_n = ((N + 15) / 16 * 16 + kBN - 1) / kBN;
+  const int tiles_n = ((N + 15) / 16 * 16 + bn - 1) / bn;
   const int T = tiles_m * tiles_n;
   const int G = ((K + 127) / 128 + 3) / 4;
   const int C = cus < kMaxSkGrid ? cus : kMaxSkGrid;
-  PrefillPlan whole = {T < cus ? T : cus, 0, 0, 0};
-  if (sched == 1 || C < 2) return whole;
+  PrefillPlan whole = {bn, T < cus ? T : cus, 0, 0, 0};
+  if (split == 1 || C < 2) return whole;
   const int r = T % C;
   int s = r ? C / r : 0;
   if (s > G) s = G;
   if (s < 2) return whole;
-  if (sched == 0 && (2 * r > C || (G / s < 7 && (4 * r > C || G / s < 4)))) return whole;
+  if (split == 0 && (2 * r > C || (G / s < 7 && (4 * r > C || G / s < 4)))) return whole;
   PrefillPlan pl;
+  pl.bn = bn;
   pl.r = r;
   pl.s = s;
   pl.grid = T >= C ? C : r * s;
   const size_t words = (size_t)r + (size_t)pl.grid;
-  pl.bytes = ((size_t)pl.grid * kPartBytes + words * 4 + 255) / 256 * 256;
+  pl.bytes = ((size_t)pl.grid * kBM * bn * 4 + words * 4 + 255) / 256 * 256;
   return pl;
 }
 
-int prefill_sched() {
-  const int path = get_gemm_path_override();
-  return path == 3 ? 1 : path == 4 ? 2 : 0;
+// The plan for the kernel-selection override (0: automatic; 3 / 4: 256 wide,
+// whole tiles / split forced; 5 / 6: 128 wide, the same).  Automatic: 128
+// wide where 256-wide tiles fill at most half a round of the compute units
+// and 128-wide ones fit in one, else 256 wide; then that width's split
+// rule.  Measured on MI355X (both widths, both schedules, M = 512 ... 8192,
+// the three sweep shapes): a 128-wide tile does its work 1.27x slower per
+// flop when every compute unit is busy (M = 8192: 263 -> 335 us), so it pays
+// only where 256-wide tiles leave most units idle — M = 512, N = 14336,
+// K = 5120: 33.0 -> 25.7 us; M = 512, N = 5120, K = 14336: 66.3 (256 wide,
+// split) -> 41.5 us (128 wide, split); M = 1024 there: 74.4 -> 55.3 us;
+// with more tiles it lost up to 28% (and won at most 4%, at two shapes this
+// rule leaves at 256).
+PrefillPlan plan_prefill(int M, int N, int K, int cus) {
+  switch (get_gemm_path_override()) {
+    case 3: return plan_width(256, M, N, K, cus, 1);
+    case 4: return plan_width(256, M, N, K, cus, 2);
+    case 5: return plan_width(128, M, N, K, cus, 1);
+    case 6: return plan_width(128, M, N, K, cus, 2);
+    default: break;
+  }
+  const int C = cus < kMaxSkGrid ? cus : kMaxSkGrid;
+  const int tiles_m = (M + kBM - 1) / kBM;
+  const int n16 = (N + 15) / 16 * 16;
+  const int t256 = tiles_m * ((n16 + 255) / 256), t128 = tiles_m * ((n16 + 127) / 128);
+  return plan_width(2 * t256 <= C && t128 <= C ? 128 : 256, M, N, K, cus, 0);
 }
 
 }  // namespace
 
 size_t gemm_prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  return plan_prefill((int)M, (int)N, (int)K, kMaxSkGrid, prefill_sched()).bytes;
+  return plan_prefill((int)M, (int)N, (int)K, kMaxSkGrid).bytes;
 }
 
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream) {
-  const int tiles_m = (p.M + kBM - 1) / kBM;
-  const int tiles_n = (p.Ns * 16 + kBN - 1) / kBN;
-  PrefillPlan pl = plan_prefill(p.M, p.N, p.K, p.cus, prefill_sched());
-  if (pl.r && (!p.work || p.work_bytes < pl.bytes)) pl = plan_prefill(p.M, p.N, p.K, p.cus, 1);
-  SkArgs sk = {0, 1, nullptr, nullptr, nullptr};
+  PrefillPlan pl = plan_prefill(p.M, p.N, p.K, p.cus);
+  if (pl.r && (!p.work || p.work_bytes < pl.bytes)) pl = plan_width(pl.bn, p.M, p.N, p.K, p.cus, 1);
+  PrefillSplit sk = {0, 1, nullptr, nullptr, nullptr};
   if (pl.r) {
     sk.r = pl.r;
     sk.s = pl.s;
     sk.part = p.work;
-    sk.ctrl = reinterpret_cast<uint32_t*>(p.work + (size_t)pl.grid * kPartBytes);
+    sk.ctrl = reinterpret_cast<uint32_t*>(p.work + (size_t)pl.grid * kBM * pl.bn * 4);
     sk.flags = sk.ctrl + pl.r;
-    // a kernel, not a memset: the launch may be captured into a graph
-    sk_clear_kernel<<<1, 256, 0, stream>>>(sk.ctrl, pl.r + pl.grid);
   }
-  const bool a16 = ((uintptr_t)p.out & 15) == 0;
-  const int mode = p.out_fp4 ? 4
-                 : p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
-                             : ((p.N % 8 == 0 && p.ldo % 8 == 0 && a16) ? 0 : 1);
-  const dim3 g((unsigned)pl.grid), b(64 * kWaves);
-  switch (mode) {
-    case 0: gemm_prefill_kernel<0><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
-    case 1: gemm_prefill_kernel<1><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
-    case 2: gemm_prefill_kernel<2><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
-    case 4: gemm_prefill_kernel<4><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
-    default: gemm_prefill_kernel<3><<<g, b, 0, stream>>>(p, tiles_m, tiles_n, sk); break;
-  }
-  return hipGetLastError();
+  return pl.bn == 128 ? launch_prefill_tiles_128(p, pl.grid, sk, stream)
+                      : launch_prefill_tiles_256(p, pl.grid, sk, stream);
 }
+#endif
 
 }  // namespace mxfp4

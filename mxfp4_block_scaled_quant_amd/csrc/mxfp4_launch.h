@@ -43,6 +43,18 @@ struct GemmArgs {
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream);
+// The large-M kernel's split (split-K) schedule of one launch: tiles [0, r)
+// cut into s K slices (r = 0: whole tiles), parts, counters and flags in the
+// workspace.
+struct PrefillSplit {
+  int r, s;
+  uint8_t* part;
+  uint32_t* ctrl;
+  uint32_t* flags;
+};
+// The large-M kernel at output-tile width 256 / 128 on `grid` workgroups.
+hipError_t launch_prefill_tiles_256(const GemmArgs& p, int grid, const PrefillSplit& sk, hipStream_t stream);
+hipError_t launch_prefill_tiles_128(const GemmArgs& p, int grid, const PrefillSplit& sk, hipStream_t stream);
 // Workspace the large-M kernel's split schedule takes for this shape on up
 // to 256 compute units (0: whole tiles only).
 size_t gemm_prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -70,7 +82,8 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
 // exercise each GEMM path on every shape: 0 = automatic by M, 1 = decode
 // kernel, 2 = prefill kernel (schedule by estimate), 3 = prefill kernel with
 // whole tiles only, 4 = prefill kernel with the split schedule wherever a
-// tile has more than one group of 4 K-steps.
+// tile has more than one group of 4 K-steps; 5 and 6: the same as 3 and 4
+// with 128-wide output tiles.
 void set_gemm_path_override(int path);
 int get_gemm_path_override();
 

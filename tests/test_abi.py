@@ -216,33 +216,36 @@ def test_valid_call_without_gpu_reports_device(lib):
 
 
 def test_debug_path_hook(lib):
-    assert lib.mxfp4_debug_set_gemm_path(5) == 7
+    assert lib.mxfp4_debug_set_gemm_path(7) == 7
     assert lib.mxfp4_debug_set_gemm_path(-1) == 7
-    for path in (4, 3, 2, 1, 0):
+    for path in (6, 5, 4, 3, 2, 1, 0):
         assert lib.mxfp4_debug_set_gemm_path(path) == 0
 
 
-# The large-M kernel's split schedule (256 compute units): the r tiles short
-# of whole rounds are cut along K into s = 256 / r slices, one per workgroup,
-# where the slices stay long enough to pay for their parts' traffic; its
-# workspace is one fp32 256 x 256 part per workgroup, then a counter per
-# split tile and a flag per workgroup, rounded up to 256 bytes.
-def _split_bytes(grid, r):
-    return (grid * 256 * 256 * 4 + 4 * (r + grid) + 255) // 256 * 256
+# The large-M kernel's plan (256 compute units): 128-wide output tiles where
+# 256-wide ones fill at most half a round and 128-wide ones fit in one; then
+# the split schedule: the r tiles short of whole rounds are cut along K into
+# s = 256 / r slices, one per workgroup, where the slices stay long enough to
+# pay for their parts' traffic; its workspace is one fp32 256 x bn part per
+# workgroup, then a counter per split tile and a flag per workgroup, rounded
+# up to 256 bytes.
+def _split_bytes(grid, r, bn=256):
+    return (grid * 256 * bn * 4 + 4 * (r + grid) + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("M,N,K,grid,r", [
-    (8192, 5120, 14336, 256, 128),     # 640 tiles: 128 left over, 2 slices of 14 groups
-    (512, 5120, 14336, 240, 40),       # 40 tiles, 6 slices of 4-5 groups
-    (2048, 5120, 14336, 0, 0),         # 160 tiles: more than half a round left over
-    (2048, 34816, 5120, 0, 0),         # 1088 tiles: slices of 2-3 groups would not pay
-    (512, 14336, 5120, 0, 0),          # 112 tiles, slices of 5 groups: not paid either
-    (8192, 14336, 5120, 0, 0),         # 1792 tiles: whole rounds
-    (37, 96, 4128, 0, 0),              # one tile: slices of one group
-    (64, 5120, 14336, 0, 0),           # M <= 64: the small-M kernel
+@pytest.mark.parametrize("M,N,K,grid,r,bn", [
+    (8192, 5120, 14336, 256, 128, 256),  # 640 tiles: 128 left over, 2 slices of 14 groups
+    (512, 5120, 14336, 240, 80, 128),    # 40 tiles, 128 wide: 80, 3 slices of 9-10 groups
+    (1024, 5120, 14336, 0, 0, 128),      # 128 wide: 160 tiles, more than half a round
+    (2048, 5120, 14336, 0, 0, 256),      # 160 tiles: more than half a round left over
+    (2048, 34816, 5120, 0, 0, 256),      # 1088 tiles: slices of 2-3 groups would not pay
+    (512, 14336, 5120, 0, 0, 128),       # 112 tiles; 128 wide: 224 whole tiles
+    (8192, 14336, 5120, 0, 0, 256),      # 1792 tiles: whole rounds
+    (37, 96, 4128, 0, 0, 128),           # one tile: slices of one group
+    (64, 5120, 14336, 0, 0, 0),          # M <= 64: the small-M kernel
 ])
-def test_split_schedule_workspace(lib, M, N, K, grid, r):
-    want = _split_bytes(grid, r) if grid else 0
+def test_split_schedule_workspace(lib, M, N, K, grid, r, bn):
+    want = _split_bytes(grid, r, bn) if grid else 0
     assert lib.mxfp4_gemm_workspace_bytes(M, N, K) == want
     if M > 64:
         # the quantised activations, then the GEMM's part
@@ -263,6 +266,10 @@ def test_split_schedule_forced_and_whole(lib):
         assert lib.mxfp4_gemm_workspace_bytes(300, 128, 256) == 0        # one group: nothing to split
         assert lib.mxfp4_gemm_workspace_bytes(8192, 14336, 5120) == 0    # whole rounds
         assert lib.mxfp4_gemm_workspace_bytes(2048, 5120, 14336) == 0    # 256 / 160: one slice
+        assert lib.mxfp4_debug_set_gemm_path(6) == 0                      # 128 wide, split forced
+        assert lib.mxfp4_gemm_workspace_bytes(2048, 5120, 14336) == _split_bytes(256, 64, 128)
+        assert lib.mxfp4_debug_set_gemm_path(5) == 0                      # 128 wide, whole tiles
+        assert lib.mxfp4_gemm_workspace_bytes(512, 5120, 14336) == 0
     finally:
         lib.mxfp4_debug_set_gemm_path(0)
 

@@ -44,6 +44,10 @@ CASES = [
     ("tiled_300x512x1056", 300, 512, 1056, 2, dict(outliers=True, pads=(4, 5))),
     ("tiled_257x96x2080", 257, 96, 2080, 2, dict(seed=10)),
     ("tiled_37x288x4128", 37, 288, 4128, 2, dict(seed=5, bias=False)),
+    # 128-wide output tiles (5), and with the split schedule forced (6)
+    ("tiled128_300x512x1056", 300, 512, 1056, 5, dict(outliers=True, pads=(4, 5))),
+    ("tiled128_split_257x96x2080", 257, 96, 2080, 6, dict(seed=10)),
+    ("tiled128_37x288x4128", 37, 288, 4128, 5, dict(seed=5, bias=False)),
 ]
 
 

@@ -25,6 +25,7 @@ from tests.test_gpu_gemm import _check, _run
 pytestmark = pytest.mark.gpu
 
 SPLIT, WHOLE = 4, 3   # set_gemm_path: tiled kernel, split schedule / whole tiles only
+SPLIT128, WHOLE128 = 6, 5   # the same with 128-wide output tiles
 
 CASES = [
     # name, M, N, K, problem kwargs: 2 x 3 tiles of 3 groups (3 slices each),
@@ -35,16 +36,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("split,whole", [(SPLIT, WHOLE), (SPLIT128, WHOLE128)], ids=["w256", "w128"])
 @pytest.mark.parametrize("name,M,N,K,kw", CASES, ids=[c[0] for c in CASES])
-def test_split_matches_oracle(name, M, N, K, kw):
+def test_split_matches_oracle(name, M, N, K, kw, split, whole):
     need_gpu()
-    print(f"[split] {name}", flush=True)
+    print(f"[split] {name} path {split}", flush=True)
     prob = inputs.linear_problem(M, N, K, **kw)
-    y32, y16 = _run(prob, SPLIT)
+    y32, y16 = _run(prob, split)
     _check(prob, y32, y16)
     # the same operands on whole tiles: both within the oracle's bar, and
     # apart only by the order of the fp32 sums
-    w32, w16 = _run(prob, WHOLE)
+    w32, w16 = _run(prob, whole)
     _check(prob, w32, w16)
 
 
