@@ -4,7 +4,8 @@ A tile split along K between workgroups meets in the workspace: the last
 workgroup to finish a slice adds the others in K order.  Forced on small
 shapes (every tile is cut into as many slices as idle workgroups allow, at
 most one per group of 4 K-steps: 3, 5 and 9 slices per tile here), the
-results must meet the oracle's bar like the whole-tile schedule's
+results, at both output-tile widths (256 and 128 columns), must meet the
+oracle's bar like the whole-tile schedule's
 (tests/test_gpu_gemm.py), be identical run to run (the sum does not depend
 on which slice finishes last), not read a part left
 by an earlier call, and replay correctly from a captured graph (the
@@ -50,7 +51,8 @@ def test_split_matches_oracle(name, M, N, K, kw, split, whole):
     _check(prob, w32, w16)
 
 
-def test_split_identical_run_to_run_and_no_stale_parts():
+@pytest.mark.parametrize("split", [SPLIT, SPLIT128], ids=["w256", "w128"])
+def test_split_identical_run_to_run_and_no_stale_parts(split):
     # Two problems of one shape alternate through the same workspace sizes:
     # A, B, A.  Each result meets the oracle's bar, and the two runs of A are
     # bitwise equal (the parts are summed in K order, and nothing of B's
@@ -59,9 +61,9 @@ def test_split_identical_run_to_run_and_no_stale_parts():
     M, N, K = 37, 96, 4128
     pa = inputs.linear_problem(M, N, K, 5, edge=True, with_bias=True)
     pb = inputs.linear_problem(M, N, K, 7, outliers=True, with_bias=True)
-    a1 = _run(pa, SPLIT)
-    b1 = _run(pb, SPLIT)
-    a2 = _run(pa, SPLIT)
+    a1 = _run(pa, split)
+    b1 = _run(pb, split)
+    a2 = _run(pa, split)
     _check(pa, *a1)
     _check(pb, *b1)
     assert np.array_equal(a1[0].view(np.uint32), a2[0].view(np.uint32))
@@ -90,7 +92,8 @@ def test_split_mxfp4_out_is_the_quantised_bf16_output():
     assert np.array_equal(host_u8(os_), s_ref)
 
 
-def test_split_linear_entry_points():
+@pytest.mark.parametrize("split", [SPLIT, SPLIT128], ids=["w256", "w128"])
+def test_split_linear_entry_points(split):
     # mxfp4_linear (quantisation into the workspace, then the GEMM with its
     # part of the workspace after it) and mxfp4_linear_prequantized.
     need_gpu()
@@ -99,7 +102,7 @@ def test_split_linear_entry_points():
     W = mx.quantize_weight(dev_bf16(prob["w"]))
     b = dev_bf16(prob["bias"])
     x = dev_bf16(prob["x"])
-    mx.set_gemm_path(SPLIT)
+    mx.set_gemm_path(split)
     try:
         assert mx.linear_workspace_bytes(M, N, K) > mx.linear_workspace_bytes(M, N, 256)
         y32 = mx.mxfp4_linear(x, W.w_pre, W.ws_pre, N, b, torch.float32)
@@ -113,7 +116,8 @@ def test_split_linear_entry_points():
     assert np.array_equal(y32.cpu().numpy().view(np.uint32), p32.cpu().numpy().view(np.uint32))
 
 
-def test_split_graph_replays():
+@pytest.mark.parametrize("split", [SPLIT, SPLIT128], ids=["w256", "w128"])
+def test_split_graph_replays(split):
     # The counter-clearing kernel and the GEMM captured together; replays
     # with new operands copied in between (eager work and synchronisation
     # between replays), each checked against the eager call on the same
@@ -127,7 +131,7 @@ def test_split_graph_replays():
     q_in = torch.empty_like(qs[0][0])
     s_in = torch.empty_like(qs[0][1])
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    mx.set_gemm_path(SPLIT)
+    mx.set_gemm_path(split)
     try:
         eager = [mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32) for q, s in qs]
         q_in.copy_(qs[0][0])
