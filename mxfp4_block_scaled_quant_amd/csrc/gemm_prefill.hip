@@ -5,10 +5,13 @@
 // equal to the dequantised reference), organised for the MFMA roofline:
 //
 //  * persistent: one 512-thread workgroup per compute unit walks a list of
-//    256 x 256 output tiles.  Its 8 waves (two per SIMD, so one can issue
-//    while the other waits) form a 2 x 4 grid of 128 x 64 wave tiles, 8 x 4
-//    MFMA tiles of 16 x 16 each (128 fp32 accumulators per lane);
-//  * operands stream through four single-K-step LDS stages (32 KiB each):
+//    256 x 256 output tiles (or 256 x 128: this source built again with
+//    MXFP4_PREFILL_BN = 128, for shapes where 256-wide tiles would leave
+//    most compute units idle).  Its 8 waves (two per SIMD, so one can issue
+//    while the other waits) form a 2 x 4 grid of 128 x 64 (128 x 32) wave
+//    tiles, 8 x 4 (8 x 2) MFMA tiles of 16 x 16 each (128 (64) fp32
+//    accumulators per lane);
+//  * operands stream through four single-K-step LDS stages (32 (24) KiB each):
 //    every 1 KiB operand unit of the GEMM layouts (activations and weights
 //    alike) is fetched by one buffer_load_dwordx4 ... lds, so LDS holds
 //    fragments in the lane order the MFMA consumes (conflict-free
@@ -45,7 +48,7 @@
 //    ticket, so the wait always ends.
 //
 // Every register counts: at two waves per SIMD a wave has 256 registers, 128
-// of them accumulators and 64 operand fragments.
+// of them accumulators and 64 operand fragments (256 wide).
 #include "mxfp4_device.h"
 #include "mxfp4_launch.h"
 
