@@ -42,6 +42,7 @@ CASES = [
     ("smallM_37x96x4128", 37, 96, 4128, 1, dict(seed=5, pads=(8, 1))),
     ("smallM_64x320x1056", 64, 320, 1056, 1, dict(bias=False)),
     ("tiled_300x512x1056", 300, 512, 1056, 2, dict(outliers=True, pads=(4, 5))),
+    ("tiled256_300x512x1056", 300, 512, 1056, 3, dict(outliers=True, pads=(4, 5))),
     ("tiled_257x96x2080", 257, 96, 2080, 2, dict(seed=10)),
     ("tiled_37x288x4128", 37, 288, 4128, 2, dict(seed=5, bias=False)),
     # 128-wide output tiles (5), and with the split schedule forced (6)
