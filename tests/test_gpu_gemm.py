@@ -88,6 +88,19 @@ def test_linear_small_shapes(name, M, N, K, kw, path):
     _check(prob, y32, y16)
 
 
+@pytest.mark.parametrize("M", [17, 32, 33, 48, 49, 63, 65, 256])
+def test_linear_row_boundaries(M):
+    # The automatic kernel choice on each side of its row boundaries: each
+    # row-tile count (16 rows) of the small-M kernel up to 64 rows, then the
+    # large-M kernel from 65 rows to one full 256-row tile (257 rows is a
+    # small-shape case above); 17 strips of 16 columns, a ragged last scale
+    # group and a ragged last K-step.
+    need_gpu()
+    prob = inputs.linear_problem(M, 272, 1056, 11, outliers=True, with_bias=True)
+    y32, y16 = _run(prob, 0)
+    _check(prob, y32, y16)
+
+
 def test_linear_deterministic():
     need_gpu()
     prob = inputs.linear_problem(300, 520, 1056, 6, outliers=True, with_bias=True)
