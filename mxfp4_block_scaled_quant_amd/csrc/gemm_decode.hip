@@ -380,14 +380,14 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // (4 K-steps), the groups split evenly and loaded in rounds of two groups
 // (one group beyond a single row tile, for registers); two strips per
 // workgroup reuse each activation tile unless the strips are plentiful and
-// M tiny.  At most 16 waves per workgroup up to two row tiles; 8 with three
-// (at their register count a compute unit holds three workgroups of a few
-// waves, which beat one of more waves with fewer load rounds each); 12 with
-// four (a compute unit holds 12 of those waves either way, and fewer load
-// rounds per wave win).
+// M tiny.  At most 16 waves per workgroup at one row tile; 8 with two or
+// three (at their register counts a compute unit holds several workgroups
+// of a few waves, which beat fewer workgroups of more waves with fewer
+// load rounds each); 12 with four (a compute unit holds 12 of those waves
+// either way, and fewer load rounds per wave win).
 template <int MT>
 static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
-  constexpr int MAXW = MT <= 2 ? 16 : MT == 3 ? 8 : 12;
+  constexpr int MAXW = MT == 1 ? 16 : MT == 4 ? 12 : 8;
   const int gpw = (p.G + MAXW - 1) / MAXW;
   const int kw = (p.G + gpw - 1) / gpw;
   const bool one_strip = p.Ns >= 1024 && p.M <= 8 && !p.out_fp4;  // MXFP4 output: 32 columns per workgroup
