@@ -19,6 +19,7 @@ import mxfp4_block_scaled_quant_amd as mx
 from mxfp4_block_scaled_quant_amd import inputs
 from oracle import formats as F
 from oracle import linalg as G
+from oracle import quant as Q
 from tests.helpers import (check_bf16_cast, check_f32_tolerance, dev_bf16, host_bf16_bits,
                            need_gpu, tolerance_bound)
 
@@ -99,6 +100,26 @@ def test_linear_row_boundaries(M):
     prob = inputs.linear_problem(M, 272, 1056, 11, outliers=True, with_bias=True)
     y32, y16 = _run(prob, 0)
     _check(prob, y32, y16)
+
+
+@pytest.mark.parametrize("M,K", [(16, 8192), (32, 4096), (48, 4096), (64, 6144)])
+def test_decode_widest_wave_split(M, K):
+    # The small-M kernel at its most waves per workgroup for each row-tile
+    # count (one 512-wide scale group per wave: 16, 8, 8 and 12 waves), its
+    # largest LDS reduction; bf16 / fp32 output against the oracle, and the
+    # MXFP4 output bitwise the quantisation of the bf16 output.
+    need_gpu()
+    N = 320
+    prob = inputs.linear_problem(M, N, K, 12, outliers=True, with_bias=True)
+    y32, y16 = _run(prob, 0)
+    _check(prob, y32, y16)
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
+    oq, os_ = mx.mxfp4_gemm_a4w4_mxfp4_out(q, s, W.w_pre, W.ws_pre, M, N, K, dev_bf16(prob["bias"]))
+    torch.cuda.synchronize()
+    q_ref, s_ref = Q.quant_1x32(y16)
+    assert np.array_equal(oq.cpu().numpy(), q_ref)
+    assert np.array_equal(os_.cpu().numpy(), s_ref)
 
 
 def test_linear_deterministic():
