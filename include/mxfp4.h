@@ -71,8 +71,10 @@ enum { MXFP4_OUT_BF16 = 0, MXFP4_OUT_F32 = 1 };
 const char* mxfp4_status_str(int status);
 
 /* ABI version: major * 100 + minor.  1.02: the GEMM entry points may ask
- * for a workspace (mxfp4_gemm_workspace_bytes) for large M; the debug path
- * hook takes 3 to 6. */
+ * for a workspace (mxfp4_gemm_workspace_bytes) for large M.  1.03: the
+ * workspace's first word reports a give-up of the split schedule's bounded
+ * wait; overlapping BMM output strides are rejected; the kernel-selection
+ * test hook moved to mxfp4_testing.h and acts per thread. */
 int mxfp4_abi_version(void);
 
 /* Bytes of the packed FP4 data / the scales for `rows` x K in `layout`:
@@ -89,10 +91,12 @@ size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K);
 /* Workspace bytes mxfp4_gemm_a4w4 and mxfp4_gemm_a4w4_mxfp4_out need for
  * this shape: 0 where the GEMM runs on whole output tiles (every M <= 64
  * call, and most larger ones), else the split schedule's (see
- * mxfp4_gemm_a4w4), sized for up to 256 compute units: one fp32 output
- * tile per workgroup (256 KiB, or 128 KiB with 128-wide tiles; up to 64 MiB)
- * plus 4 bytes per split tile and per workgroup.
- * Depends on the mxfp4_debug_set_gemm_path setting.  0 on invalid shapes. */
+ * mxfp4_gemm_a4w4), sized for up to 256 compute units: a give-up word, 4
+ * bytes per split tile and per workgroup (these rounded up to 256 bytes),
+ * then one fp32 output tile per workgroup (256 KiB, or 128 KiB with
+ * 128-wide tiles; up to 64 MiB).
+ * (A test build may force another plan for the calling thread:
+ * mxfp4_testing.h.)  0 on invalid shapes. */
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -156,8 +160,11 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
  *   workspace mxfp4_gemm_workspace_bytes(M, N, K) bytes, 16-byte aligned
  *             (NULL when that is 0); scratch owned by the call until it
  *             completes on `stream`: its contents need no initialisation
- *             and are not kept.  Calls that overlap in time (other streams)
- *             need workspaces of their own.
+ *             and are not kept, except that after a call that used it (a
+ *             nonzero size) its first 32-bit word is nonzero if a bounded
+ *             wait of the split schedule gave up (never expected; the sum of
+ *             that tile is then not to be trusted).  Calls that overlap in
+ *             time (other streams) need workspaces of their own.
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
  * For M > 64 the output is cut into 256 x 256 tiles, or 256 x 128 where the
  * wider ones would leave most compute units idle (measured rule).  Where
@@ -275,27 +282,16 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
  *   w_pre  preshuffled weights of `B` matrices N x K, ws_pre their scales
  *   out    element (b, m, n) at out[b*sob + m*som + n] (ELEMENTS; sob, som
  *          even, pointer 4-byte aligned).  [B, M, N]: sob = M*N, som = N;
- *          batch-major [M, B, N]: sob = N, som = B*N.
+ *          batch-major [M, B, N]: sob = N, som = B*N.  Rows must not
+ *          overlap: either som >= N and sob >= (M-1)*som + N, or sob >= N
+ *          and som >= (B-1)*sob + N (a stride of a size-1 dimension is
+ *          free); otherwise MXFP4_ERR_SHAPE.
  *   B >= 1, M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
  */
 int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm,
                 const void* w_pre, const void* ws_pre,
                 void* out, int64_t sob, int64_t som, int out_dtype,
                 int64_t B, int64_t M, int64_t N, int64_t K, void* stream);
-
-/*
- * Test hook, not part of the method: force the GEMM kernel used by
- * mxfp4_gemm_a4w4 -- 1 = the small-M streaming kernel (M <= 64 only; larger
- * M still uses the tiled kernel), 2 = the LDS-tiled kernel, 0 = choose by M
- * (the default); 3 = the tiled kernel on whole 256-wide tiles only, 4 = the
- * tiled kernel with the split schedule wherever the tiles leave a round of
- * compute units part-empty and a tile has more than 512 of K; 5 and 6 = the
- * same with 128-wide tiles (3-6 also for the tiled kernel's share of
- * mxfp4_linear and mxfp4_linear_prequantized).  Process-wide and not synchronised with calls
- * in flight on other threads; query workspace sizes after setting it.
- * Returns MXFP4_ERR_ARG for other values.
- */
-int mxfp4_debug_set_gemm_path(int path);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,9 @@ Entry points (same names as the C ABI):
 * :func:`mxfp4_preshuffle_weight` -- quantised weights -> preshuffled layout
 * :func:`mxfp4_gemm_a4w4` -- W4A4 GEMM with optional bias, bf16/fp32 out
 * :func:`mxfp4_linear` -- bf16 activations -> quant + GEMM (+ bias) in one call,
-  the quantisation fused into the GEMM kernel for M <= 16
+  the quantisation fused into the GEMM kernel (one launch) at M = 1 and at
+  M <= 4 where N < 16384 and K <= 8192; otherwise quantised into a workspace
+  first (two launches)
 * :func:`mxfp4_gemm_a4w4_mxfp4_out` -- the GEMM writing MXFP4 (row-major FP4 +
   E8M0) for the next layer
 * :func:`mxfp4_shuffle_scales` -- row-major E8M0 scales -> the GEMM scale layout
@@ -73,7 +75,7 @@ _SIGNATURES = {
                                            _c_vp, _c_size, _c_vp]),
     "a16wfp4_bmm": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int,
                              _c_i64, _c_i64, _c_i64, _c_i64, _c_vp]),
-    "mxfp4_debug_set_gemm_path": (_c_int, [_c_int]),
+    "mxfp4_testing_set_gemm_path": (_c_int, [_c_int]),
 }
 
 _lib_handle = None
@@ -123,6 +125,38 @@ def _require_cuda(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a device (cuda/HIP) tensor")
 
 
+def _require_bytes(t: Optional[torch.Tensor], name: str, nbytes: int, device: torch.device) -> None:
+    """t is a uint8 tensor on `device`, contiguous, of at least nbytes bytes."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.uint8 or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor on {device}")
+    if t.numel() < nbytes:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {nbytes} needed")
+
+
+def _require_out(out: torch.Tensor, shape, dtype: torch.dtype, device: torch.device) -> None:
+    """A caller's output: this shape and dtype on `device`, unit stride along
+    its last dimension (the kernels write whole rows from there)."""
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype or out.device != device:
+        raise ValueError(f"out must be {tuple(shape)} {dtype} on {device}, "
+                         f"got {tuple(out.shape)} {out.dtype} on {out.device}")
+    if out.numel() and out.stride(-1) != 1:
+        raise ValueError("out must have unit stride along its last dimension")
+
+
+def _require_bias(bias: Optional[torch.Tensor], N: int, device: torch.device) -> None:
+    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N
+                             or bias.device != device or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous bf16 [N = {N}] tensor on {device}")
+
+
+def _require_weight(w_pre: torch.Tensor, ws_pre: torch.Tensor, N: int, K: int,
+                    device: torch.device, batch: int = 1) -> None:
+    _require_bytes(w_pre, "w_pre", weight_bytes(batch, N, K), device)
+    _require_bytes(ws_pre, "ws_pre", weight_scale_bytes(batch, N, K), device)
+
+
 def data_bytes(rows: int, K: int, layout: int) -> int:
     return int(lib().mxfp4_data_bytes(rows, K, layout))
 
@@ -140,10 +174,11 @@ def weight_scale_bytes(batch: int, N: int, K: int) -> int:
 
 
 def set_gemm_path(path: int) -> None:
-    """Test hook: 1 forces the small-M kernel (M <= 64), 2 the tiled kernel, 0 = by M;
-    3 the tiled kernel on whole 256-wide tiles only, 4 with the split (split-K)
+    """Test hook (include/mxfp4_testing.h), for the calling thread only: 1
+    forces the small-M kernel (M <= 64), 2 the tiled kernel, 0 = by M; 3 the
+    tiled kernel on whole 256-wide tiles only, 4 with the split (split-K)
     schedule; 5 and 6 the same with 128-wide tiles."""
-    _check("mxfp4_debug_set_gemm_path", lib().mxfp4_debug_set_gemm_path(path))
+    _check("mxfp4_testing_set_gemm_path", lib().mxfp4_testing_set_gemm_path(path))
 
 
 def mxfp4_quant_1x32(x: torch.Tensor, layout: int = MXFP4_LAYOUT_GEMM,
@@ -163,8 +198,15 @@ def mxfp4_quant_1x32(x: torch.Tensor, layout: int = MXFP4_LAYOUT_GEMM,
             q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
         else:
             q = torch.empty(data_bytes(M, K, layout), dtype=torch.uint8, device=x.device)
+    elif layout == MXFP4_LAYOUT_ROWMAJOR and q.dim() == 2:
+        if q.dtype != torch.uint8 or q.device != x.device or q.shape != (M, K // 2) or q.stride(1) != 1:
+            raise ValueError(f"q must be uint8 [{M}, {K // 2}] with unit stride along K on {x.device}")
+    else:
+        _require_bytes(q, "q", data_bytes(M, K, layout), x.device)
     if scales is None:
         scales = torch.empty(scale_bytes(M, K, layout), dtype=torch.uint8, device=x.device)
+    else:
+        _require_bytes(scales, "scales", scale_bytes(M, K, layout), x.device)
     ldq = q.stride(0) if (layout == MXFP4_LAYOUT_ROWMAJOR and q.dim() == 2) else K // 2
     _check("mxfp4_quant_1x32", lib().mxfp4_quant_1x32(
         _ptr(x), M, K, x.stride(0), _ptr(q), ldq, _ptr(scales), layout, _stream(x.device)))
@@ -186,19 +228,45 @@ def mxfp4_preshuffle_weight(w_fp4: torch.Tensor, w_scales: torch.Tensor, N: int,
     return w_pre, ws_pre
 
 
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().mxfp4_gemm_workspace_bytes(M, N, K))
+
+
+def _gemm_operands(a_fp4, a_scales, w_pre, ws_pre, M, N, K, bias):
+    _require_cuda(a_fp4, "a_fp4")
+    dev = a_fp4.device
+    _require_bytes(a_fp4, "a_fp4", data_bytes(M, K, MXFP4_LAYOUT_GEMM), dev)
+    _require_bytes(a_scales, "a_scales", scale_bytes(M, K, MXFP4_LAYOUT_GEMM), dev)
+    _require_weight(w_pre, ws_pre, N, K, dev)
+    _require_bias(bias, N, dev)
+    return dev
+
+
+def _gemm_workspace(M, N, K, workspace, dev):
+    need = gemm_workspace_bytes(M, N, K)
+    if workspace is None:
+        return (torch.empty(need, dtype=torch.uint8, device=dev) if need else None), need
+    _require_bytes(workspace, "workspace", need, dev)
+    return workspace, workspace.numel()
+
+
 def mxfp4_gemm_a4w4(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre: torch.Tensor,
                     ws_pre: torch.Tensor, M: int, N: int, K: int,
                     bias: Optional[torch.Tensor] = None,
-                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None):
-    """out[M, N] = dq(A) dq(W)^T (+ bias), bf16 or fp32; A and W in the GEMM layouts."""
-    _require_cuda(a_fp4, "a_fp4")
-    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
-        raise ValueError("bias must be bf16 [N]")
+                    out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """out[M, N] = dq(A) dq(W)^T (+ bias), bf16 or fp32; A and W in the GEMM layouts.
+
+    ``workspace`` (uint8, >= :func:`gemm_workspace_bytes`) is allocated here
+    when needed and not given; after a call that used one, its first 32-bit
+    word is nonzero if the split schedule's bounded wait gave up."""
+    dev = _gemm_operands(a_fp4, a_scales, w_pre, ws_pre, M, N, K, bias)
     code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a_fp4.device)
-    ws_bytes = int(lib().mxfp4_gemm_workspace_bytes(M, N, K))
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_fp4.device) if ws_bytes else None
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        _require_out(out, (M, N), out_dtype, dev)
+    workspace, ws_bytes = _gemm_workspace(M, N, K, workspace, dev)
     _check("mxfp4_gemm_a4w4", lib().mxfp4_gemm_a4w4(
         _ptr(a_fp4), _ptr(a_scales), _ptr(w_pre), _ptr(ws_pre), _ptr(bias),
         _ptr(out), out.stride(0), code, M, N, K, _ptr(workspace), ws_bytes, _stream(a_fp4.device)))
@@ -215,20 +283,25 @@ def mxfp4_linear(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: 
     """out[M, N] = round(dq(Q(x)) dq(W)^T (+ bias)) from bf16 x [M, K] (unit stride along K).
 
     ``workspace`` (uint8, >= :func:`linear_workspace_bytes` bytes) is
-    allocated here when needed and not given; M <= 16 needs none.
+    allocated here when needed and not given; the fused shapes (M = 1, and
+    M <= 4 where N < 16384 and K <= 8192) need none.
     """
     _require_cuda(x, "x")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bf16 tensor with unit stride along K")
-    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
-        raise ValueError("bias must be bf16 [N]")
     M, K = x.shape
+    _require_weight(w_pre, ws_pre, N, K, x.device)
+    _require_bias(bias, N, x.device)
     code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _require_out(out, (M, N), out_dtype, x.device)
     need = linear_workspace_bytes(M, N, K)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    elif workspace is not None:
+        _require_bytes(workspace, "workspace", need, x.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check("mxfp4_linear", lib().mxfp4_linear(
         _ptr(x), x.stride(0), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0),
@@ -240,21 +313,20 @@ def mxfp4_gemm_a4w4_mxfp4_out(a_fp4: torch.Tensor, a_scales: torch.Tensor, w_pre
                               ws_pre: torch.Tensor, M: int, N: int, K: int,
                               bias: Optional[torch.Tensor] = None,
                               out_fp4: Optional[torch.Tensor] = None,
-                              out_scales: Optional[torch.Tensor] = None):
+                              out_scales: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None):
     """(q [M, N/2], scales [M, N/32]) uint8: the GEMM's rows quantised per 1x32
     along N (bitwise mxfp4_quant_1x32 of the bf16 output, ROWMAJOR)."""
-    _require_cuda(a_fp4, "a_fp4")
-    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
-        raise ValueError("bias must be bf16 [N]")
+    dev = _gemm_operands(a_fp4, a_scales, w_pre, ws_pre, M, N, K, bias)
     if out_fp4 is None:
-        out_fp4 = torch.empty((M, N // 2), dtype=torch.uint8, device=a_fp4.device)
+        out_fp4 = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    else:
+        _require_out(out_fp4, (M, N // 2), torch.uint8, dev)
     if out_scales is None:
-        out_scales = torch.empty((M, N // 32), dtype=torch.uint8, device=a_fp4.device)
-    for t, name in ((out_fp4, "out_fp4"), (out_scales, "out_scales")):
-        if t.dtype != torch.uint8 or t.dim() != 2 or t.stride(1) != 1:
-            raise ValueError(f"{name} must be 2-D uint8 with unit stride along N")
-    ws_bytes = int(lib().mxfp4_gemm_workspace_bytes(M, N, K))
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_fp4.device) if ws_bytes else None
+        out_scales = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    else:
+        _require_out(out_scales, (M, N // 32), torch.uint8, dev)
+    workspace, ws_bytes = _gemm_workspace(M, N, K, workspace, dev)
     _check("mxfp4_gemm_a4w4_mxfp4_out", lib().mxfp4_gemm_a4w4_mxfp4_out(
         _ptr(a_fp4), _ptr(a_scales), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out_fp4),
         out_fp4.stride(0), _ptr(out_scales), out_scales.stride(0), M, N, K, _ptr(workspace),
@@ -273,6 +345,8 @@ def mxfp4_shuffle_scales(scales: torch.Tensor, rows: int, K: int,
     if out is None:
         out = torch.empty(scale_bytes(rows, K, MXFP4_LAYOUT_GEMM), dtype=torch.uint8,
                           device=scales.device)
+    else:
+        _require_bytes(out, "out", scale_bytes(rows, K, MXFP4_LAYOUT_GEMM), scales.device)
     _check("mxfp4_shuffle_scales", lib().mxfp4_shuffle_scales(
         _ptr(s2), s2.stride(0), rows, K, _ptr(out), _stream(scales.device)))
     return out
@@ -296,14 +370,21 @@ def mxfp4_linear_prequantized(x_fp4: torch.Tensor, x_scales: torch.Tensor, w_pre
     if (x_scales.dtype != torch.uint8 or x_scales.dim() != 2 or x_scales.shape != (M, K // 32)
             or x_scales.stride(1) != 1):
         raise ValueError("x_scales must be uint8 [M, K/32] with unit stride along the blocks")
-    if bias is not None and (bias.dtype != torch.bfloat16 or bias.numel() != N):
-        raise ValueError("bias must be bf16 [N]")
+    dev = x_fp4.device
+    if x_scales.device != dev:
+        raise ValueError("x_scales must be on the device of x_fp4")
+    _require_weight(w_pre, ws_pre, N, K, dev)
+    _require_bias(bias, N, dev)
     code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x_fp4.device)
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        _require_out(out, (M, N), out_dtype, dev)
     need = linear_prequantized_workspace_bytes(M, N, K)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x_fp4.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace is not None:
+        _require_bytes(workspace, "workspace", need, dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check("mxfp4_linear_prequantized", lib().mxfp4_linear_prequantized(
         _ptr(x_fp4), x_fp4.stride(0), _ptr(x_scales), x_scales.stride(0), _ptr(w_pre),
@@ -324,18 +405,17 @@ def a16wfp4_bmm(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: i
     if x.dtype != torch.bfloat16 or x.dim() != 3 or x.stride(2) != 1:
         raise ValueError("x must be a 3-D bf16 tensor with unit stride along K")
     B, M, K = x.shape
+    _require_weight(w_pre, ws_pre, N, K, x.device, batch=B)
     code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
+    shape = (M, B, N) if batch_major else (B, M, N)
     if out is None:
-        if batch_major:
-            out = torch.empty((M, B, N), dtype=out_dtype, device=x.device)
-        else:
-            out = torch.empty((B, M, N), dtype=out_dtype, device=x.device)
+        out = torch.empty(shape, dtype=out_dtype, device=x.device)
+    else:
+        _require_out(out, shape, out_dtype, x.device)
     if batch_major:
         sob, som = out.stride(1), out.stride(0)
     else:
         sob, som = out.stride(0), out.stride(1)
-    if out.stride(-1) != 1:
-        raise ValueError("out must have unit stride along N")
     _check("a16wfp4_bmm", lib().a16wfp4_bmm(
         _ptr(x), x.stride(0), x.stride(1), _ptr(w_pre), _ptr(ws_pre), _ptr(out), sob, som, code,
         B, M, N, K, _stream(x.device)))

@@ -9,13 +9,16 @@
 #include <atomic>
 
 #include "../../include/mxfp4.h"
+#include "../../include/mxfp4_testing.h"
 #include "mxfp4_launch.h"
 
 namespace mxfp4 {
 
-static std::atomic<int> g_gemm_path{0};
-void set_gemm_path_override(int path) { g_gemm_path.store(path); }
-int get_gemm_path_override() { return g_gemm_path.load(); }
+// The test hook's forced kernel choice: per thread, so a call on one thread
+// never sees another thread's setting between its size query and its GEMM.
+static thread_local int t_gemm_path = 0;
+void set_gemm_path_override(int path) { t_gemm_path = path; }
+int get_gemm_path_override() { return t_gemm_path; }
 
 namespace {
 
@@ -83,7 +86,7 @@ const char* mxfp4_status_str(int status) {
   }
 }
 
-int mxfp4_abi_version(void) { return 102; }
+int mxfp4_abi_version(void) { return 103; }
 
 size_t mxfp4_data_bytes(int64_t rows, int64_t K, int layout) {
   if (rows < 0 || K <= 0 || K % 32) return 0;
@@ -444,6 +447,13 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, cons
       M > kMaxBuf || N > kMaxBuf)
     return MXFP4_ERR_SHAPE;
   if (sxm < K || sxb < 0 || sob < 0 || som < 0) return MXFP4_ERR_SHAPE;
+  // output rows must not overlap: heads outside rows ([B, M, N]-like) or
+  // rows outside heads (batch-major [M, B, N]-like)
+  {
+    const bool heads_outer = (M <= 1 || som >= N) && (B <= 1 || sob >= (M - 1) * som + N);
+    const bool rows_outer = (B <= 1 || sob >= N) && (M <= 1 || som >= (B - 1) * sob + N);
+    if (M > 0 && !heads_outer && !rows_outer) return MXFP4_ERR_SHAPE;
+  }
   if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
       (64 * sxm + K) * 2 > kMaxBuf)
     return MXFP4_ERR_SHAPE;
@@ -459,9 +469,8 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, cons
                                    out_dtype == MXFP4_OUT_F32, B, M, N, K, (hipStream_t)stream, cus));
 }
 
-// Test hook: force the decode (1) or prefill (2) GEMM kernel, 0 = by M; 3
-// and 4: the prefill kernel with whole tiles only / the split schedule.
-int mxfp4_debug_set_gemm_path(int path) {
+// Test hook (include/mxfp4_testing.h): force a GEMM kernel on this thread.
+int mxfp4_testing_set_gemm_path(int path) {
   if (path < 0 || path > 6) return MXFP4_ERR_ARG;
   set_gemm_path_override(path);
   return MXFP4_OK;

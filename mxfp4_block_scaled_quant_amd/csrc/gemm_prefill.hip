@@ -113,9 +113,9 @@ constexpr int kLprShift = kWN == 4 ? 3 : 2;
 
 // Split schedule of one launch (PrefillSplit): tiles [0, r) of the tile
 // order are cut into s slices each (r = 0: whole tiles only).  Workspace:
-// one fp32 part slot of a tile per slice (slot = the slice's workgroup),
-// then an arrival counter per split tile and a ready flag per slot, zeroed
-// before every launch.
+// a give-up word, an arrival counter per split tile and a ready flag per
+// slot, all zeroed before every launch, then one fp32 part slot of a tile per
+// slice (slot = the slice's workgroup).
 using SkArgs = PrefillSplit;
 constexpr uint32_t kPartBytes = kBM * kBN * 4;  // 256 (128) KiB: one tile's fp32 accumulators
 // Cache policy of the part stores and loads: device scope (sc1), as the
@@ -823,15 +823,22 @@ __device__ bool sk_combine(const SkArgs& sk, const Share& s, Pipe& P, int wv) {
       return false;
     }
   }
+  bool waited_out = false;
   for (int k = 0; k < S; ++k) {
     if (k == kme) continue;
     const int id = k * sk.r + t;
-    for (int it = 0; it < kSpinLimit; ++it) {
+    bool seen = false;
+    for (int it = 0; it < kSpinLimit && !seen; ++it) {
       const uint32_t f = __hip_atomic_load(sk.flags + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_amdgcn_readfirstlane(f) != 0) break;
-      __builtin_amdgcn_s_sleep(2);
+      seen = __builtin_amdgcn_readfirstlane(f) != 0;
+      if (!seen) __builtin_amdgcn_s_sleep(2);
     }
+    waited_out = waited_out || !seen;
   }
+  // a wait that gave up (never expected: every slice waited for already
+  // holds its ticket, so it is running) is made visible in the workspace
+  if (waited_out && wv == 0 && lane == 0)
+    __hip_atomic_fetch_or(sk.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (S == 2) {
     add_part<true>(P.acc, rp, (uint32_t)((1 - kme) * sk.r + t) * kPartBytes + lofs);
   } else {
@@ -941,7 +948,7 @@ __global__ __launch_bounds__(512, 1) void MXFP4_PREFILL_KERNEL(GemmArgs p, int t
 hipError_t MXFP4_PREFILL_TILES(const GemmArgs& p, int grid, const PrefillSplit& sk, hipStream_t stream) {
   const int tiles_m = (p.M + kBM - 1) / kBM;
   const int tiles_n = (p.Ns * 16 + kBN - 1) / kBN;
-  if (sk.r) sk_clear_kernel<<<1, 256, 0, stream>>>(sk.ctrl, sk.r + grid);
+  if (sk.r) sk_clear_kernel<<<1, 256, 0, stream>>>(sk.err, 1 + sk.r + grid);
   const bool a16 = ((uintptr_t)p.out & 15) == 0;
   const int mode = p.out_fp4 ? 4
                  : p.out_f32 ? ((p.N % 4 == 0 && p.ldo % 4 == 0 && a16) ? 2 : 3)
@@ -961,6 +968,10 @@ hipError_t MXFP4_PREFILL_TILES(const GemmArgs& p, int grid, const PrefillSplit& 
 namespace {
 
 constexpr int kMaxSkGrid = 256;  // the split schedule's workgroups (and workspace) at most
+
+// Bytes of the split schedule's words (give-up word, counters, flags),
+// rounded up to 256 so the parts after them stay aligned.
+size_t sk_words_bytes(int r, int grid) { return ((size_t)(1 + r + grid) * 4 + 255) / 256 * 256; }
 
 struct PrefillPlan {
   int bn, grid, r, s;
@@ -997,8 +1008,7 @@ PrefillPlan plan_width(int bn, int M, int N, int K, int cus, int split) {
   pl.r = r;
   pl.s = s;
   pl.grid = T >= C ? C : r * s;
-  const size_t words = (size_t)r + (size_t)pl.grid;
-  pl.bytes = ((size_t)pl.grid * kBM * bn * 4 + words * 4 + 255) / 256 * 256;
+  pl.bytes = sk_words_bytes(r, pl.grid) + (size_t)pl.grid * kBM * bn * 4;
   return pl;
 }
 
@@ -1038,13 +1048,14 @@ size_t gemm_prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream) {
   PrefillPlan pl = plan_prefill(p.M, p.N, p.K, p.cus);
   if (pl.r && (!p.work || p.work_bytes < pl.bytes)) pl = plan_width(pl.bn, p.M, p.N, p.K, p.cus, 1);
-  PrefillSplit sk = {0, 1, nullptr, nullptr, nullptr};
+  PrefillSplit sk = {0, 1, nullptr, nullptr, nullptr, nullptr};
   if (pl.r) {
     sk.r = pl.r;
     sk.s = pl.s;
-    sk.part = p.work;
-    sk.ctrl = reinterpret_cast<uint32_t*>(p.work + (size_t)pl.grid * kBM * pl.bn * 4);
+    sk.err = reinterpret_cast<uint32_t*>(p.work);
+    sk.ctrl = sk.err + 1;
     sk.flags = sk.ctrl + pl.r;
+    sk.part = p.work + sk_words_bytes(pl.r, pl.grid);
   }
   return pl.bn == 128 ? launch_prefill_tiles_128(p, pl.grid, sk, stream)
                       : launch_prefill_tiles_256(p, pl.grid, sk, stream);

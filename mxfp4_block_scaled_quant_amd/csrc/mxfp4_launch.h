@@ -44,11 +44,15 @@ struct GemmArgs {
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream);
 // The large-M kernel's split (split-K) schedule of one launch: tiles [0, r)
-// cut into s K slices (r = 0: whole tiles), parts, counters and flags in the
-// workspace.
+// cut into s K slices (r = 0: whole tiles); in the workspace, in this order:
+// the give-up word (raised when a slice's bounded wait for another slice's
+// flag expired -- the tile's sum is then not to be trusted), the tiles'
+// arrival counters, the slices' ready flags, then (256-byte aligned) the
+// parts.
 struct PrefillSplit {
   int r, s;
   uint8_t* part;
+  uint32_t* err;
   uint32_t* ctrl;
   uint32_t* flags;
 };
@@ -78,8 +82,9 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
                             const void* ws, void* out, int64_t sob, int64_t som, int out_f32,
                             int64_t B, int64_t M, int64_t N, int64_t K, hipStream_t stream, int cus);
 
-// Kernel-selection overrides used only by the tests and the benchmark to
-// exercise each GEMM path on every shape: 0 = automatic by M, 1 = decode
+// Kernel-selection override of the calling thread, set only through the
+// test hook (include/mxfp4_testing.h) to exercise each GEMM path on every
+// shape: 0 = automatic by M, 1 = decode
 // kernel, 2 = prefill kernel (schedule by estimate), 3 = prefill kernel with
 // whole tiles only, 4 = prefill kernel with the split schedule wherever a
 // tile has more than one group of 4 K-steps; 5 and 6: the same as 3 and 4

@@ -66,8 +66,18 @@ def check_bf16_cast(y_bits: np.ndarray, y_ref: np.ndarray, bound: np.ndarray) ->
     hi = ordered(to_bf16(y_ref + bound))
     o = ordered(y_bits)
     in_band = (o >= lo) & (o <= hi)
-    bad = ~(within_ulp | in_band)
+    # the band reading only where the strict bar is out of reach: the rounded
+    # band spans more than one bf16 ulp there
+    wide = (hi - lo) >= 2
+    bad = ~(within_ulp | (in_band & wide))
     assert not bad.any(), (f"{int(bad.sum())} bf16 outputs neither within 1 ulp nor inside "
-                           f"the rounded tolerance band; worst ulp distance "
+                           f"a rounded tolerance band wider than 1 ulp; worst ulp distance "
                            f"{int(ulp_distance(y_bits, ref_bits)[bad].max())}")
-    return float((~within_ulp).mean()) if y_bits.size else 0.0
+    frac = float((~within_ulp).mean()) if y_bits.size else 0.0
+    BAND_FRACTIONS.append(frac)
+    return frac
+
+
+# fraction of outputs that needed the band reading, one entry per check
+# (reported by tests/test_zz_band_report.py)
+BAND_FRACTIONS: list = []

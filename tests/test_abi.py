@@ -12,13 +12,13 @@ import torch
 from oracle import layout as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("mxfp4.h", "mxfp4_testing.h")]
 
 import mxfp4_block_scaled_quant_amd as mx  # noqa: E402
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_0-9]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.mxfp4_abi_version() == 102
+    assert lib.mxfp4_abi_version() == 103
     for s in range(8):
         assert lib.mxfp4_status_str(s)
     assert lib.mxfp4_status_str(99) == b"unknown status"
@@ -202,8 +202,16 @@ def test_bmm_validation(lib):
     assert call(sxm=100) == 2
     assert call(x=None) == 1
     assert call(sxm=196) == 3
-    assert call(som=511) == 3
+    assert call(som=513, sob=64 * 514) == 3                    # odd row stride
     assert call(M=0, x=None) == 0
+    # output rows that would overlap are rejected before any other check
+    assert call(som=510) == 2                                  # rows closer than N
+    assert call(sob=512, som=512) == 2                         # heads on top of each other
+    assert call(sob=63 * 512 + 510) == 2                       # head b's rows reach head b+1
+    assert call(M=1, som=0, x=None) == 1                       # one row: its stride is moot
+    assert call(B=1, sob=0, x=None) == 1                       # one head: its stride is moot
+    assert call(sob=512, som=16 * 512, x=None) == 1            # batch-major [M, B, N]
+    assert call(sob=64 * 520, som=520, x=None) == 1            # padded rows
 
 
 def test_valid_call_without_gpu_reports_device(lib):
@@ -215,11 +223,31 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.mxfp4_linear(P, 64, P, P, None, P, 16, 0, 4, 16, 64, None, 0, None) == 5
 
 
-def test_debug_path_hook(lib):
-    assert lib.mxfp4_debug_set_gemm_path(7) == 7
-    assert lib.mxfp4_debug_set_gemm_path(-1) == 7
+def test_testing_path_hook(lib):
+    assert lib.mxfp4_testing_set_gemm_path(7) == 7
+    assert lib.mxfp4_testing_set_gemm_path(-1) == 7
     for path in (6, 5, 4, 3, 2, 1, 0):
-        assert lib.mxfp4_debug_set_gemm_path(path) == 0
+        assert lib.mxfp4_testing_set_gemm_path(path) == 0
+
+
+def test_testing_path_hook_is_per_thread(lib):
+    # a path forced on another thread changes neither this thread's plan
+    # nor its workspace size
+    import threading
+    base = lib.mxfp4_gemm_workspace_bytes(2048, 34816, 5120)
+    seen = {}
+
+    def other():
+        lib.mxfp4_testing_set_gemm_path(4)
+        seen["other"] = lib.mxfp4_gemm_workspace_bytes(2048, 34816, 5120)
+        lib.mxfp4_testing_set_gemm_path(0)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["other"] == _split_bytes(256, 64) != base == 0
+    assert lib.mxfp4_gemm_workspace_bytes(2048, 34816, 5120) == base
+    assert "mxfp4_testing_set_gemm_path" not in open(HEADERS[0]).read()
 
 
 # The large-M kernel's plan (256 compute units): 128-wide output tiles where
@@ -227,10 +255,10 @@ def test_debug_path_hook(lib):
 # the split schedule: the r tiles short of whole rounds are cut along K into
 # s = 256 / r slices, one per workgroup, where the slices stay long enough to
 # pay for their parts' traffic; its workspace is one fp32 256 x bn part per
-# workgroup, then a counter per split tile and a flag per workgroup, rounded
-# up to 256 bytes.
+# workgroup, after a give-up word, a counter per split tile and a flag per
+# workgroup (those words rounded up to 256 bytes).
 def _split_bytes(grid, r, bn=256):
-    return (grid * 256 * bn * 4 + 4 * (r + grid) + 255) // 256 * 256
+    return grid * 256 * bn * 4 + (4 * (1 + r + grid) + 255) // 256 * 256
 
 
 @pytest.mark.parametrize("M,N,K,grid,r,bn", [
@@ -256,9 +284,9 @@ def test_split_schedule_workspace(lib, M, N, K, grid, r, bn):
 
 def test_split_schedule_forced_and_whole(lib):
     try:
-        assert lib.mxfp4_debug_set_gemm_path(3) == 0
+        assert lib.mxfp4_testing_set_gemm_path(3) == 0
         assert lib.mxfp4_gemm_workspace_bytes(8192, 5120, 14336) == 0
-        assert lib.mxfp4_debug_set_gemm_path(4) == 0
+        assert lib.mxfp4_testing_set_gemm_path(4) == 0
         # forced: wherever a round is left part-empty and a tile has 2+ groups
         assert lib.mxfp4_gemm_workspace_bytes(2048, 34816, 5120) == _split_bytes(256, 64)
         assert lib.mxfp4_gemm_workspace_bytes(300, 520, 1056) == _split_bytes(18, 6)
@@ -266,12 +294,12 @@ def test_split_schedule_forced_and_whole(lib):
         assert lib.mxfp4_gemm_workspace_bytes(300, 128, 256) == 0        # one group: nothing to split
         assert lib.mxfp4_gemm_workspace_bytes(8192, 14336, 5120) == 0    # whole rounds
         assert lib.mxfp4_gemm_workspace_bytes(2048, 5120, 14336) == 0    # 256 / 160: one slice
-        assert lib.mxfp4_debug_set_gemm_path(6) == 0                      # 128 wide, split forced
+        assert lib.mxfp4_testing_set_gemm_path(6) == 0                      # 128 wide, split forced
         assert lib.mxfp4_gemm_workspace_bytes(2048, 5120, 14336) == _split_bytes(256, 64, 128)
-        assert lib.mxfp4_debug_set_gemm_path(5) == 0                      # 128 wide, whole tiles
+        assert lib.mxfp4_testing_set_gemm_path(5) == 0                      # 128 wide, whole tiles
         assert lib.mxfp4_gemm_workspace_bytes(512, 5120, 14336) == 0
     finally:
-        lib.mxfp4_debug_set_gemm_path(0)
+        lib.mxfp4_testing_set_gemm_path(0)
 
 
 def test_split_schedule_workspace_validation(lib):

@@ -35,12 +35,23 @@ def _run(prob, path, weight=None):
     mx.set_gemm_path(path)
     try:
         q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
-        y32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
-        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16)
+        need = mx.gemm_workspace_bytes(M, N, K)
+        ws = [torch.empty(need, dtype=torch.uint8, device="cuda") if need else None for _ in range(2)]
+        y32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32, workspace=ws[0])
+        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16, workspace=ws[1])
     finally:
         mx.set_gemm_path(0)
     torch.cuda.synchronize()
+    assert_no_giveup(*ws)
     return y32.cpu().numpy(), host_bf16_bits(y16)
+
+
+def assert_no_giveup(*workspaces):
+    """After a split-schedule call, the first word of its workspace is
+    nonzero only if a bounded wait for another slice gave up."""
+    for ws in workspaces:
+        if ws is not None:
+            assert int(ws[:4].view(torch.int32).item()) == 0, "split schedule: a bounded wait gave up"
 
 
 def _check(prob, y32, y16, rows=None, cols=None):

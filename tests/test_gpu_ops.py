@@ -1,7 +1,7 @@
 """GPU checks of the torch custom ops: torch.library.opcheck (schema, fake vs
 real, dispatch), torch.compile through the fake implementations with
 dynamic sizes, and capture in a CUDA (HIP) graph -- each bitwise equal to
-the direct binding calls, which the other GPU tests hold to the oracle."""
+the direct binding calls -- and the ops' own outputs held to the oracle."""
 
 import numpy as np
 import pytest
@@ -92,3 +92,41 @@ def test_graph_capture_replays():
             assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
             _ = torch.ops.mxfp4.linear(x, W.w_pre, W.ws_pre, W.N, None, torch.bfloat16)  # eager work
             torch.cuda.synchronize()
+
+
+def test_ops_meet_the_oracle():
+    # The ops' own outputs held to the oracle directly (not only through the
+    # binding calls they equal): quantisation bytes exactly, the GEMM and the
+    # linear within the GEMM bar, the BMM within its bar.
+    need_gpu()
+    from oracle import linalg as G
+    from oracle import quant as Q
+    from tests.helpers import check_f32_tolerance, host_u8
+    from tests.test_gpu_gemm import _check
+
+    M, N, K = 37, 96, 4128
+    p = inputs.linear_problem(M, N, K, 5, edge=True, with_bias=True)
+    x, b = dev_bf16(p["x"]), dev_bf16(p["bias"])
+    W = mx.quantize_weight(dev_bf16(p["w"]))
+    qr, sr = torch.ops.mxfp4.quant_1x32(x, mx.MXFP4_LAYOUT_ROWMAJOR)
+    q_ref, s_ref = Q.quant_1x32(p["x"])
+    assert np.array_equal(host_u8(qr), q_ref)
+    assert np.array_equal(host_u8(sr).reshape(M, K // 32), s_ref)
+    q, s = torch.ops.mxfp4.quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
+    y32 = torch.ops.mxfp4.gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
+    y16 = torch.ops.mxfp4.gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16)
+    torch.cuda.synchronize()
+    _check(p, y32.cpu().numpy(), y16.cpu().view(torch.int16).numpy().view(np.uint16))
+    for rows in (1, 16, M):
+        pr = dict(p, x=p["x"][:rows])
+        z32 = torch.ops.mxfp4.linear(x[:rows], W.w_pre, W.ws_pre, N, b, torch.float32)
+        z16 = torch.ops.mxfp4.linear(x[:rows], W.w_pre, W.ws_pre, N, b, torch.bfloat16)
+        torch.cuda.synchronize()
+        _check(pr, z32.cpu().numpy(), z16.cpu().view(torch.int16).numpy().view(np.uint16))
+    pb = inputs.bmm_problem(4, 9, 64, 192, 4)
+    Wb = mx.quantize_weight(dev_bf16(pb["w"]))
+    o = torch.ops.mxfp4.a16wfp4_bmm(dev_bf16(pb["x"]), Wb.w_pre, Wb.ws_pre, 64, True, torch.float32)
+    torch.cuda.synchronize()
+    qw, sw = Q.quant_1x32(pb["w"].reshape(4 * 64, 192))
+    o_ref, S = G.bmm_a16wfp4(pb["x"], qw.reshape(4, 64, 96), sw.reshape(4, 64, 6))
+    check_f32_tolerance(o.cpu().numpy().transpose(1, 0, 2), o_ref, S)

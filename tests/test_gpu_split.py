@@ -21,7 +21,7 @@ import mxfp4_block_scaled_quant_amd as mx
 from mxfp4_block_scaled_quant_amd import inputs
 from oracle import quant as Q
 from tests.helpers import dev_bf16, host_bf16_bits, host_u8, need_gpu
-from tests.test_gpu_gemm import _check, _run
+from tests.test_gpu_gemm import _check, _run, assert_no_giveup
 
 pytestmark = pytest.mark.gpu
 
@@ -82,11 +82,15 @@ def test_split_mxfp4_out_is_the_quantised_bf16_output():
     q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
     mx.set_gemm_path(SPLIT)
     try:
-        oq, os_ = mx.mxfp4_gemm_a4w4_mxfp4_out(q, s, W.w_pre, W.ws_pre, M, N, K, b)
-        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16)
+        need = mx.gemm_workspace_bytes(M, N, K)
+        assert need > 0
+        ws = [torch.empty(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        oq, os_ = mx.mxfp4_gemm_a4w4_mxfp4_out(q, s, W.w_pre, W.ws_pre, M, N, K, b, workspace=ws[0])
+        y16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16, workspace=ws[1])
     finally:
         mx.set_gemm_path(0)
     torch.cuda.synchronize()
+    assert_no_giveup(*ws)
     q_ref, s_ref = Q.quant_1x32(host_bf16_bits(y16))
     assert np.array_equal(host_u8(oq), q_ref)
     assert np.array_equal(host_u8(os_), s_ref)
@@ -133,17 +137,19 @@ def test_split_graph_replays(split):
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
     mx.set_gemm_path(split)
     try:
+        gws = torch.empty(mx.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+        assert gws.numel() > 0
         eager = [mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32) for q, s in qs]
         q_in.copy_(qs[0][0])
         s_in.copy_(qs[0][1])
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            mx.mxfp4_gemm_a4w4(q_in, s_in, W.w_pre, W.ws_pre, M, N, K, b, torch.float32, out=out)
+            mx.mxfp4_gemm_a4w4(q_in, s_in, W.w_pre, W.ws_pre, M, N, K, b, torch.float32, out=out, workspace=gws)
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            mx.mxfp4_gemm_a4w4(q_in, s_in, W.w_pre, W.ws_pre, M, N, K, b, torch.float32, out=out)
+            mx.mxfp4_gemm_a4w4(q_in, s_in, W.w_pre, W.ws_pre, M, N, K, b, torch.float32, out=out, workspace=gws)
         for rep in range(6):
             i = rep % 3
             q_in.copy_(qs[i][0])
@@ -152,6 +158,7 @@ def test_split_graph_replays(split):
             graph.replay()
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int32), eager[i].view(torch.int32)), rep
+            assert_no_giveup(gws)
             # eager work between replays, through a workspace of its own
             e = mx.mxfp4_gemm_a4w4(qs[2 - i][0], qs[2 - i][1], W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
             torch.cuda.synchronize()

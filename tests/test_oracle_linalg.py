@@ -119,3 +119,42 @@ def test_zero_blocks_with_unit_scale_change_nothing():
 def test_bf16_output_single_rounding():
     y = np.array([[1.0 + 2.0 ** -8 + 2.0 ** -40, -3.0]])
     assert list(G.to_bf16(y)[0]) == [0x3F81, 0xC040]
+
+
+@pytest.mark.parametrize("B,M,N,K", [(1, 1, 1, 32), (2, 3, 2, 64), (3, 2, 4, 96)])
+def test_bmm_matches_fraction_brute_force(B, M, N, K):
+    # Both outputs of the BMM oracle -- the product and the sum of |x_k w_k|
+    # that sets every BMM parity bar -- against exact rational sums, per
+    # head, with x taken exactly from its bf16 bits and the weight from the
+    # closed-form E2M1 x 2^(s-127) dequantisation.  Negative activations and
+    # weights make a dropped |.| (or a sign or index slip) show.
+    p = inputs.bmm_problem(B, M, N, K, 13)
+    x, w = p["x"], p["w"]                       # uint16 [B, M, K], [B, N, K]
+    qw, sw = Q.quant_1x32(w.reshape(B * N, K))
+    qw, sw = qw.reshape(B, N, K // 2), sw.reshape(B, N, K // 32)
+    o, s = G.bmm_a16wfp4(x, qw, sw)
+    assert (F.bf16_to_f64(x) < 0).any() and (F.bf16_to_f64(x) > 0).any()
+    for b in range(B):
+        W = _frac_dq(qw[b], sw[b])
+        X = [[Fraction(float(v)) for v in row] for row in F.bf16_to_f64(x[b])]
+        for m in range(M):
+            for n in range(N):
+                exact = sum(X[m][k] * W[n][k] for k in range(K))
+                exact_abs = sum(abs(X[m][k] * W[n][k]) for k in range(K))
+                bound = (K + 2) * 2.0 ** -52 * float(exact_abs)
+                assert abs(Fraction(o[b, m, n]) - exact) <= Fraction(bound)
+                assert abs(Fraction(s[b, m, n]) - exact_abs) <= Fraction(bound)
+                # not vacuous: the signed sum and the absolute sum differ
+                if K >= 64:
+                    assert exact_abs > abs(exact)
+
+
+def test_bmm_abs_sum_pins_a_planted_mistake():
+    # A plausible slip -- the abs taken of the product's sum instead of the
+    # sum of |products| -- is caught by the rational pin above: show that the
+    # two differ on the pinned inputs (so the pin can tell them apart).
+    p = inputs.bmm_problem(2, 3, 2, 64, 13)
+    qw, sw = Q.quant_1x32(p["w"].reshape(4, 64))
+    qw, sw = qw.reshape(2, 2, 32), sw.reshape(2, 2, 2)
+    o, s = G.bmm_a16wfp4(p["x"], qw, sw)
+    assert not np.allclose(np.abs(o), s)
