@@ -210,6 +210,25 @@ int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_p
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mxfp4_linear for callers that cannot allocate device memory or pass a
+ * workspace (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments without the workspace, the same
+ * result as mxfp4_linear (bitwise, wherever mxfp4_linear does not take the
+ * large-M kernel's split schedule; this entry point always runs whole tiles).
+ * The quantised activations go to the library's own scratch array, a fixed
+ * 32 MiB of device memory per GPU that the library runs on, held until the
+ * process ends: this call allocates nothing.  Shapes whose quantised
+ * activations exceed it (ceil(M/16) * (ceil(K/128) * 1024 + ceil(K/512) * 256)
+ * bytes: M above 4400 at K = 14336, above 12336 at K = 5120) return
+ * MXFP4_ERR_WORKSPACE, before anything is enqueued.  Every call on a
+ * GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ * (other streams) race, and must not be made.
+ */
+int mxfp4_linear_noalloc(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre,
+                         const void* bias, void* out, int64_t ldo, int out_dtype,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * W4A4 GEMM with MXFP4 output for the next layer (the producer side of the
  * prequantised input of P2 §2: the next layer's activations leave this
  * GEMM already quantised, instead of as bf16 that a separate quantisation

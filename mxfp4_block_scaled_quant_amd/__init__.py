@@ -66,6 +66,8 @@ _SIGNATURES = {
     "mxfp4_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "mxfp4_linear": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
                               _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
+    "mxfp4_linear_noalloc": (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_int,
+                                      _c_i64, _c_i64, _c_i64, _c_vp]),
     "mxfp4_gemm_a4w4_mxfp4_out": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp,
                                            _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_size, _c_vp]),
     "mxfp4_shuffle_scales": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
@@ -306,6 +308,30 @@ def mxfp4_linear(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: 
     _check("mxfp4_linear", lib().mxfp4_linear(
         _ptr(x), x.stride(0), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0),
         code, M, N, K, _ptr(workspace), ws_bytes, _stream(x.device)))
+    return out
+
+
+def mxfp4_linear_noalloc(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: int,
+                         bias: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.bfloat16,
+                         out: Optional[torch.Tensor] = None):
+    """:func:`mxfp4_linear` through the entry point that allocates nothing and
+    takes no workspace (the library's own per-GPU scratch holds the quantised
+    activations; calls that overlap on one GPU race).  Only ``out`` is
+    allocated here, and only when not given."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bf16 tensor with unit stride along K")
+    M, K = x.shape
+    _require_weight(w_pre, ws_pre, N, K, x.device)
+    _require_bias(bias, N, x.device)
+    code = {torch.bfloat16: MXFP4_OUT_BF16, torch.float32: MXFP4_OUT_F32}[out_dtype]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    else:
+        _require_out(out, (M, N), out_dtype, x.device)
+    _check("mxfp4_linear_noalloc", lib().mxfp4_linear_noalloc(
+        _ptr(x), x.stride(0), _ptr(w_pre), _ptr(ws_pre), _ptr(bias), _ptr(out), out.stride(0),
+        code, M, N, K, _stream(x.device)))
     return out
 
 

@@ -66,6 +66,80 @@ bool linear_fused(int64_t M, int64_t N, int64_t K) {
 }
 
 }  // namespace
+
+int device_cus(int* cus) { return check_device(cus); }
+
+// Quantised activations in the GEMM layouts, then the GEMM's workspace, in
+// one workspace: byte offsets of the scales and of the GEMM's part.
+size_t act_scales_offset(int64_t M, int64_t K) { return (size_t)cdiv(gemm_data_bytes(M, K), 256) * 256; }
+size_t act_gemm_offset(int64_t M, int64_t K) {
+  return (act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K) + 255) / 256 * 256;
+}
+
+size_t linear_act_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 || linear_fused(M, N, K)) return 0;
+  return act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K);
+}
+
+int linear_check(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre, const void* bias,
+                 const void* out, int64_t ldo, int out_dtype, int64_t M, int64_t N, int64_t K) {
+  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
+  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  if (ldo < N || ldx < K) return MXFP4_ERR_SHAPE;
+  if (ldo > kMaxBuf / 256 / (out_dtype == MXFP4_OUT_F32 ? 4 : 2)) return MXFP4_ERR_SHAPE;
+  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
+      gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
+    return MXFP4_ERR_SHAPE;
+  // the fused kernel addresses x through one 32-bit buffer range
+  if (M > 0 && linear_fused(M, N, K) && ((M - 1) * ldx + K) * 2 > kMaxBuf) return MXFP4_ERR_SHAPE;
+  if (M == 0) return MXFP4_OK;
+  if (!x || !w_pre || !ws_pre || !out) return MXFP4_ERR_NULL;
+  if (!aligned(x, 16) || ldx % 8 || !aligned(w_pre, 16) || !aligned(ws_pre, 4) || !aligned(out, 4) ||
+      (bias && !aligned(bias, 2)))
+    return MXFP4_ERR_ALIGN;
+  return MXFP4_OK;
+}
+
+int linear_run(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre, const void* bias,
+               void* out, int64_t ldo, int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+               size_t workspace_bytes, bool split, int cus, hipStream_t s) {
+  GemmArgs p{};
+  p.cus = cus;
+  p.w = (const uint8_t*)w_pre;
+  p.ws = (const uint8_t*)ws_pre;
+  p.bias = (const uint16_t*)bias;
+  p.out = out;
+  p.ldo = ldo;
+  p.out_f32 = out_dtype == MXFP4_OUT_F32;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.Kt = (int)cdiv(K, 128);
+  p.G = (int)cdiv(p.Kt, 4);
+  p.Ns = (int)cdiv(N, 16);
+  if (linear_fused(M, N, K)) {
+    p.x = (const uint16_t*)x;
+    p.ldx = (int)ldx;
+    p.x_bytes = (uint32_t)(((M - 1) * ldx + K) * 2);
+    return launched(launch_linear_decode(p, s));
+  }
+  // Larger M: quantise into the workspace, then the GEMM kernel for that M
+  // (the large-M kernel's split schedule in the rest of the workspace, when
+  // allowed and the workspace holds it; else whole tiles).
+  uint8_t* q = (uint8_t*)workspace;
+  uint8_t* sc = q + act_scales_offset(M, K);
+  const int st = launched(launch_quant_1x32(x, M, K, ldx, q, 0, sc, MXFP4_LAYOUT_GEMM, s));
+  if (st) return st;
+  p.a = q;
+  p.as = sc;
+  if (split && workspace_bytes > act_gemm_offset(M, K)) {
+    p.work = q + act_gemm_offset(M, K);
+    p.work_bytes = workspace_bytes - act_gemm_offset(M, K);
+  }
+  return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+}
+
 }  // namespace mxfp4
 
 using namespace mxfp4;
@@ -125,12 +199,6 @@ size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return gemm_path(M) == 2 ? gemm_prefill_workspace_bytes(M, N, K) : 0;
 }
 
-// Quantised activations in the GEMM layouts, then the GEMM's workspace, in
-// one workspace: byte offsets of the scales and of the GEMM's part.
-static size_t act_scales_offset(int64_t M, int64_t K) { return (size_t)cdiv(gemm_data_bytes(M, K), 256) * 256; }
-static size_t act_gemm_offset(int64_t M, int64_t K) {
-  return (act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K) + 255) / 256 * 256;
-}
 
 int mxfp4_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, int64_t ldq,
                      void* scales, int layout, void* stream) {
@@ -229,69 +297,18 @@ size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int mxfp4_linear(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre,
                  const void* bias, void* out, int64_t ldo, int out_dtype, int64_t M, int64_t N,
                  int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
-  if (out_dtype != MXFP4_OUT_BF16 && out_dtype != MXFP4_OUT_F32) return MXFP4_ERR_ARG;
-  if (M < 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf)
-    return MXFP4_ERR_SHAPE;
-  if (ldo < N || ldx < K) return MXFP4_ERR_SHAPE;
-  if (ldo > kMaxBuf / 256 / (out_dtype == MXFP4_OUT_F32 ? 4 : 2)) return MXFP4_ERR_SHAPE;
-  if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
-      gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
-    return MXFP4_ERR_SHAPE;
-  const bool fused = M > 0 && linear_fused(M, N, K);
-  // the fused kernel addresses x through one 32-bit buffer range
-  if (fused && M > 0 && ((M - 1) * ldx + K) * 2 > kMaxBuf) return MXFP4_ERR_SHAPE;
+  int st = linear_check(x, ldx, w_pre, ws_pre, bias, out, ldo, out_dtype, M, N, K);
+  if (st) return st;
   const size_t need = mxfp4_linear_workspace_bytes(M, N, K);
   if (workspace_bytes < need) return MXFP4_ERR_WORKSPACE;
   if (M == 0) return MXFP4_OK;
-  if (!x || !w_pre || !ws_pre || !out || (need && !workspace)) return MXFP4_ERR_NULL;
-  if (!aligned(x, 16) || ldx % 8 || !aligned(w_pre, 16) || !aligned(ws_pre, 4) ||
-      !aligned(out, 4) || (bias && !aligned(bias, 2)) || (need && !aligned(workspace, 16)))
-    return MXFP4_ERR_ALIGN;
+  if (need && !workspace) return MXFP4_ERR_NULL;
+  if (need && !aligned(workspace, 16)) return MXFP4_ERR_ALIGN;
   int cus = 0;
-  int st = check_device(&cus);
+  st = check_device(&cus);
   if (st) return st;
-  hipStream_t s = (hipStream_t)stream;
-  GemmArgs p{};
-  p.cus = cus;
-  p.w = (const uint8_t*)w_pre;
-  p.ws = (const uint8_t*)ws_pre;
-  p.bias = (const uint16_t*)bias;
-  p.out = out;
-  p.ldo = ldo;
-  p.out_f32 = out_dtype == MXFP4_OUT_F32;
-  p.M = (int)M;
-  p.N = (int)N;
-  p.K = (int)K;
-  p.Kt = (int)cdiv(K, 128);
-  p.G = (int)cdiv(p.Kt, 4);
-  p.Ns = (int)cdiv(N, 16);
-  p.a_rowmajor = 0;
-  p.lda = p.lds = 0;
-  p.scales_vec = 0;
-  p.out_fp4 = 0;
-  p.out_scales = nullptr;
-  p.ldos = 0;
-  if (fused) {
-    p.a = nullptr;
-    p.as = nullptr;
-    p.x = (const uint16_t*)x;
-    p.ldx = (int)ldx;
-    p.x_bytes = (uint32_t)(((M - 1) * ldx + K) * 2);
-    return launched(launch_linear_decode(p, s));
-  }
-  // Larger M: quantise into the workspace, then the GEMM kernel for that M.
-  uint8_t* q = (uint8_t*)workspace;
-  uint8_t* sc = q + act_scales_offset(M, K);
-  st = launched(launch_quant_1x32(x, M, K, ldx, q, 0, sc, MXFP4_LAYOUT_GEMM, s));
-  if (st) return st;
-  p.a = q;
-  p.as = sc;
-  p.x = nullptr;
-  p.ldx = 0;
-  p.x_bytes = 0;
-  p.work = q + act_gemm_offset(M, K);
-  p.work_bytes = workspace_bytes > act_gemm_offset(M, K) ? workspace_bytes - act_gemm_offset(M, K) : 0;
-  return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+  return linear_run(x, ldx, w_pre, ws_pre, bias, out, ldo, out_dtype, M, N, K, workspace, workspace_bytes,
+                    true, cus, (hipStream_t)stream);
 }
 
 int mxfp4_gemm_a4w4_mxfp4_out(const void* a_fp4, const void* a_scales, const void* w_pre,

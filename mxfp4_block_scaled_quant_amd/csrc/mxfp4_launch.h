@@ -78,6 +78,20 @@ hipError_t launch_preshuffle_strided(const void* w_fp4, int64_t ldw, const void*
                                      int64_t lds, int64_t batch, int64_t N, int64_t K,
                                      void* w_out, void* ws_out, hipStream_t stream);
 
+// mxfp4_linear's steps behind its C entry points (csrc/api.hip): the host
+// argument checks (everything but the workspace), the activation workspace
+// bytes without the large-M GEMM's split part (0 where the quantisation is
+// fused), and the launches on a given workspace -- the split schedule only
+// when `split` and the workspace holds it, else whole tiles.
+int linear_check(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre, const void* bias,
+                 const void* out, int64_t ldo, int out_dtype, int64_t M, int64_t N, int64_t K);
+size_t linear_act_bytes(int64_t M, int64_t N, int64_t K);
+int linear_run(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre, const void* bias,
+               void* out, int64_t ldo, int out_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+               size_t workspace_bytes, bool split, int cus, hipStream_t s);
+// The current device's compute units if it is a gfx950 (MXFP4_OK), else MXFP4_ERR_DEVICE.
+int device_cus(int* cus);
+
 hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void* w,
                             const void* ws, void* out, int64_t sob, int64_t som, int out_f32,
                             int64_t B, int64_t M, int64_t N, int64_t K, hipStream_t stream, int cus);
