@@ -32,7 +32,17 @@ apart, the call on row-major prequantised activations, and the GEMM writing
 MXFP4 for the next layer), the
 prefill sweep (M in {512, 2048, 8192}: TFLOP/s and fraction of the 10.1
 PFLOP/s dense FP4 peak), the A16WFP4 BMM sweep (MLA K-up / V-up on 16 heads),
-and the CPU oracle timed on a bounded sample of the headline workload.
+and the CPU oracle timed on bounded samples of the headline workload, one
+prefill shape and one BMM.
+
+Timing: every row's value is the mean over its timed replays (each replay a
+graph of >= 32 back-to-back launches, so graph-launch overhead is amortised);
+each replay is also timed on its own (an event between replays), and the
+rows carry the spread of the per-launch time over the replays (p10 / p50 /
+p90, `*_spread_us`); the headline likewise per step (`step_spread_us`).  The
+shader clock is sampled from sysfs (pp_dpm_sclk, current level) by a host
+thread during the headline, the roofline loop and the prefill sweep
+(`sclk`, `prefill.sclk`).
 """
 
 from __future__ import annotations
@@ -89,6 +99,69 @@ def copies_for(nbytes):
     return max(2, -(-ROTATE_BYTES // int(nbytes)))
 
 
+def _stats(values):
+    """mean, median, p10 and p90 of a list of per-launch (or per-step) times."""
+    v = np.asarray(values, dtype=np.float64)
+    return {"mean": float(v.mean()), "p10": float(np.percentile(v, 10)),
+            "p50": float(np.percentile(v, 50)), "p90": float(np.percentile(v, 90)), "n": int(v.size)}
+
+
+def _us(st):
+    """A stats dict in seconds -> the same in microseconds, rounded, for the JSON line."""
+    return {k: (round(v * 1e6, 3) if k != "n" else v) for k, v in st.items()}
+
+
+class ClockSampler:
+    """Samples the GPU's shader clock (the current level of the sysfs
+    pp_dpm_sclk table, the line marked '*') from a host thread while a timed
+    region runs; reports the median and p10 / p90 of the samples in MHz, or
+    None where the file is not readable."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+
+    def _read(self):
+        try:
+            with open(self.path) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self._read() if self.path else None
+                if v is not None:
+                    self.samples.append(v)
+                time.sleep(self.period)
+
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.asarray(self.samples)
+        return {"median_mhz": float(np.median(v)), "p10_mhz": float(np.percentile(v, 10)),
+                "p90_mhz": float(np.percentile(v, 90)), "samples": int(v.size),
+                "source": self.path}
+
+
 class Timer:
     """HIP-event timing of graph replays on the current stream."""
 
@@ -102,10 +175,13 @@ class Timer:
         return g
 
     def time_graphs(self, graphs, reps, warmup_s=0.025):
+        """Seconds per replay: an event before every replay and one after the
+        last, so each replay is timed on its own (mean over all, and the
+        spread: p10 / p50 / p90 over the replays)."""
         # Untimed replays of the same sequence for at least warmup_s first:
         # after a pause the GPU takes a few milliseconds of load to reach its
-        # steady clocks (measured: a timed run right after two warm-up replays
-        # came out 10-15% slower than the runs after it).
+        # steady clocks (measured: a timed run right after two warm-up
+        # replays came out 10-15% slower than the runs after it).
         t0 = time.perf_counter()
         i = 0
         while True:
@@ -115,14 +191,16 @@ class Timer:
                 torch.cuda.synchronize()
                 if time.perf_counter() - t0 >= warmup_s:
                     break
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
         for i in range(reps):
             graphs[i % len(graphs)].replay()
-        b.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e-3      # seconds per replay
+        per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)]
+        st = _stats(per)
+        st["mean"] = ev[0].elapsed_time(ev[reps]) * 1e-3 / reps
+        return st
 
 
 TRAFFIC_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -629,13 +707,15 @@ def main():
     for i in range(args.warmup):
         step_graphs[i % cycle].replay()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(args.steps):
-        step_graphs[i % cycle].replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    step_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    with ClockSampler() as clk_head:
+        evs[0].record()
+        for i in range(args.steps):
+            step_graphs[i % cycle].replay()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+    step_s = evs[0].elapsed_time(evs[args.steps]) * 1e-3 / args.steps
+    step_stats = _stats([evs[i].elapsed_time(evs[i + 1]) * 1e-3 for i in range(args.steps)])
     step_bytes = sum(pipeline_bytes(c["M"], c["N"], c["K"], True) for c in cases)
     value_gbs = step_bytes / step_s / 1e9
 
@@ -652,8 +732,9 @@ def main():
                 launch(i % nvariants)
 
         g = T.capture(body)
-        reps = max(2, reps_target // n)
-        return T.time_graphs([g], reps) / n
+        reps = max(8, reps_target // n)
+        st = T.time_graphs([g], reps)
+        return {k: (v / n if k != "n" else v) for k, v in st.items()}
 
     def gemm_only_time(M, N, K, x_q, x_s, bias, out, copies, reps_target=400):
         def launch(i):
@@ -678,17 +759,18 @@ def main():
     # shapes, each shape inside a marker range so a kernel trace of this run
     # can select exactly these launches.
     roof_t = {}
-    for (N, K) in DECODE_NK:
-        b = dev_bf16(inputs.bias(N, 2))
-        for M in HEADLINE_M:
-            x = dev_bf16(inputs.activations(M, K, 2))
-            q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
-            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            torch.cuda.synchronize()
-            torch.cuda.nvtx.range_push(f"roofline M={M} N={N} K={K}")
-            roof_t[(M, N, K)] = gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
-            torch.cuda.synchronize()
-            torch.cuda.nvtx.range_pop()
+    with ClockSampler() as clk_roof:
+        for (N, K) in DECODE_NK:
+            b = dev_bf16(inputs.bias(N, 2))
+            for M in HEADLINE_M:
+                x = dev_bf16(inputs.activations(M, K, 2))
+                q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
+                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                torch.cuda.synchronize()
+                torch.cuda.nvtx.range_push(f"roofline M={M} N={N} K={K}")
+                roof_t[(M, N, K)] = gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
+                torch.cuda.synchronize()
+                torch.cuda.nvtx.range_pop()
 
     decode_rows = []
     for (N, K) in DECODE_NK:
@@ -697,10 +779,10 @@ def main():
             x = dev_bf16(inputs.activations(M, K, 2))
             q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
             out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            t = roof_t.get((M, N, K)) or gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
+            ts = roof_t.get((M, N, K)) or gemm_only_time(M, N, K, q, s, b, out, weights[(N, K)])
             gb = gemm_bytes(M, N, K, True)
             tq = quant_time(x, q, s)
-            tl = linear_time(M, N, K, x, b, out, weights[(N, K)])
+            tls = linear_time(M, N, K, x, b, out, weights[(N, K)])
             qr, sr = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_ROWMAJOR)
             sr = sr.reshape(M, K // 32)
             cps = weights[(N, K)]
@@ -711,59 +793,71 @@ def main():
             tf4 = per_launch_time(lambda i: mx.mxfp4_gemm_a4w4_mxfp4_out(
                 q, s, cps[i].w_pre, cps[i].ws_pre, M, N, K, b, out_fp4=oq, out_scales=osc), len(cps), 400)
             pb = pipeline_bytes(M, N, K, True)
+            t, tl = ts["mean"], tls["mean"]
             decode_rows.append(dict(M=M, N=N, K=K,
                                     linear_us=round(tl * 1e6, 3),
                                     linear_GBps=round(pb / tl / 1e9, 1),
                                     linear_hbm_frac=round(pb / tl / PEAK_HBM, 4),
+                                    linear_spread_us=_us(tls),
                                     gemm_us=round(t * 1e6, 3),
                                     gemm_GBps=round(gb / t / 1e9, 1),
                                     hbm_frac=round(gb / t / PEAK_HBM, 4),
-                                    quant_us=round(tq * 1e6, 3),
-                                    prequantized_us=round(tp * 1e6, 3),
-                                    mxfp4_out_us=round(tf4 * 1e6, 3),
+                                    gemm_spread_us=_us(ts),
+                                    quant_us=round(tq["mean"] * 1e6, 3),
+                                    prequantized_us=round(tp["mean"] * 1e6, 3),
+                                    mxfp4_out_us=round(tf4["mean"] * 1e6, 3),
                                     tflops=round(2 * M * N * K / tl / 1e12, 2)))
     head_rows = [r for r in decode_rows if r["M"] in HEADLINE_M]
     dom_bytes = sum(gemm_bytes(r["M"], r["N"], r["K"], True) for r in head_rows)
     dom_time = sum(r["gemm_us"] for r in head_rows) * 1e-6
     achieved = dom_bytes / len(head_rows) / (dom_time / len(head_rows))
+    # the spread of the roofline kernel's per-launch rate over the shapes'
+    # replays: each shape's p10 / p50 / p90 launch time, averaged over shapes
+    roof_spread = {q: round(dom_bytes / sum(roof_t[(r["M"], r["N"], r["K"])][q] for r in head_rows) / 1e9, 1)
+                   for q in ("p10", "p50", "p90")}
 
     log("decode sweep done")
     # ---------------- prefill sweep (GEMM, TFLOP/s vs the FP4 peak)
     prefill_rows = []
+    clk_prefill = None
     if not args.no_prefill:
-        for (N, K) in DECODE_NK:
-            for M in PREFILL_M:
-                x = dev_bf16(inputs.activations(M, K, 3, outliers=True))
-                q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
-                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-                cps = weights[(N, K)][:4]
-                t = gemm_only_time(M, N, K, q, s, None, out, cps, reps_target=40)
-                oq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
-                osc = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
-                tf4 = per_launch_time(lambda i: mx.mxfp4_gemm_a4w4_mxfp4_out(
-                    q, s, cps[i].w_pre, cps[i].ws_pre, M, N, K, None, out_fp4=oq, out_scales=osc),
-                    len(cps), 40)
-                tq = quant_time(x, q, s, reps_target=64)
-                fl = 2 * M * N * K
-                prefill_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 2),
-                                         # split-K of the leftover tiles (it needs a workspace)
-                                         schedule="split" if mx.lib().mxfp4_gemm_workspace_bytes(M, N, K)
-                                         else "whole",
-                                         tflops=round(fl / t / 1e12, 1),
-                                         fp4_peak_frac=round(fl / t / PEAK_FP4, 4),
-                                         quant_us=round(tq * 1e6, 2),
-                                         mxfp4_out_us=round(tf4 * 1e6, 2),
-                                         mxfp4_out_tflops=round(fl / tf4 / 1e12, 1),
-                                         quant_GBps=round(quant_bytes(M, K) / tq / 1e9, 1)))
-                del x, q, s, out, oq, osc
-        torch.cuda.empty_cache()
+        with ClockSampler() as clk:
+            for (N, K) in DECODE_NK:
+                for M in PREFILL_M:
+                    x = dev_bf16(inputs.activations(M, K, 3, outliers=True))
+                    q, s = mx.mxfp4_quant_1x32(x, mx.MXFP4_LAYOUT_GEMM)
+                    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                    cps = weights[(N, K)][:4]
+                    ts = gemm_only_time(M, N, K, q, s, None, out, cps, reps_target=40)
+                    oq = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+                    osc = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+                    tf4 = per_launch_time(lambda i: mx.mxfp4_gemm_a4w4_mxfp4_out(
+                        q, s, cps[i].w_pre, cps[i].ws_pre, M, N, K, None, out_fp4=oq, out_scales=osc),
+                        len(cps), 40)["mean"]
+                    tq = quant_time(x, q, s, reps_target=64)["mean"]
+                    fl = 2 * M * N * K
+                    t = ts["mean"]
+                    prefill_rows.append(dict(M=M, N=N, K=K, gemm_us=round(t * 1e6, 2),
+                                             gemm_spread_us=_us(ts),
+                                             # split-K of the leftover tiles (it needs a workspace)
+                                             schedule="split" if mx.gemm_workspace_bytes(M, N, K) else "whole",
+                                             tflops=round(fl / t / 1e12, 1),
+                                             fp4_peak_frac=round(fl / t / PEAK_FP4, 4),
+                                             quant_us=round(tq * 1e6, 2),
+                                             mxfp4_out_us=round(tf4 * 1e6, 2),
+                                             mxfp4_out_tflops=round(fl / tf4 / 1e12, 1),
+                                             quant_GBps=round(quant_bytes(M, K) / tq / 1e9, 1)))
+                    del x, q, s, out, oq, osc
+            torch.cuda.empty_cache()
+        clk_prefill = clk.summary()
     big = [r for r in prefill_rows if r["M"] >= 2048]
     prefill_summary = None
     if big:
         fl = sum(2 * r["M"] * r["N"] * r["K"] for r in big)
         tt = sum(r["gemm_us"] for r in big) * 1e-6
         prefill_summary = dict(tflops_M_ge_2048=round(fl / tt / 1e12, 1),
-                               fp4_peak_frac=round(fl / tt / PEAK_FP4, 4), shapes=prefill_rows)
+                               fp4_peak_frac=round(fl / tt / PEAK_FP4, 4), sclk=clk_prefill,
+                               shapes=prefill_rows)
 
     log("prefill sweep done")
     # ---------------- A16WFP4 BMM sweep (MLA absorbed K-up / V-up, 16 heads)
@@ -780,11 +874,12 @@ def main():
                 out = (torch.empty((M, BMM_HEADS, N), dtype=torch.bfloat16, device=dev) if bm
                        else torch.empty((BMM_HEADS, M, N), dtype=torch.bfloat16, device=dev))
 
-                t = per_launch_time(lambda i: mx.a16wfp4_bmm(xs[i], W.w_pre, W.ws_pre, N, out=out,
-                                                             batch_major=bm), R, 400)
+                ts = per_launch_time(lambda i: mx.a16wfp4_bmm(xs[i], W.w_pre, W.ws_pre, N, out=out,
+                                                              batch_major=bm), R, 400)
+                t = ts["mean"]
                 by = bmm_bytes(BMM_HEADS, M, N, K)
                 fl = 2 * BMM_HEADS * M * N * K
-                bmm_rows.append(dict(op=name, M=M, N=N, K=K, us=round(t * 1e6, 3),
+                bmm_rows.append(dict(op=name, M=M, N=N, K=K, us=round(t * 1e6, 3), spread_us=_us(ts),
                                      GBps=round(by / t / 1e9, 1), hbm_frac=round(by / t / PEAK_HBM, 4),
                                      tflops=round(fl / t / 1e12, 2)))
                 del xs, x, out
@@ -814,10 +909,12 @@ def main():
             "workload": "decode-sweep W4A4 MXFP4 linear at M<=16: per-1x32 quant of bf16 "
                         "activations + block-scaled FP4 GEMM + bf16 bias, bf16 out",
             "M": HEADLINE_M, "NK": DECODE_NK,
-            "step": "9 shapes x mxfp4_linear (M<=4: quant fused into the GEMM; M=16: "
-                    "quant then GEMM), weights preshuffled at load, rotated copies",
+            "step": "9 shapes x mxfp4_linear (M=1, and M=4 at N=14336: quant fused into the "
+                    "GEMM; else quant then GEMM), weights preshuffled at load, rotated copies",
             "hbm_frac": round(value_gbs * 1e9 / PEAK_HBM, 4),
         },
+        "step_spread_us": _us(step_stats),
+        "sclk": {"headline": clk_head.summary(), "roofline": clk_roof.summary()},
         "roofline": {
             "kernel": "gemm_decode_kernel (W4A4 GEMM, M<=16, mean over the 9 headline shapes)",
             "bound": "hbm",
@@ -828,6 +925,7 @@ def main():
             "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
             "launch_us": round(dom_time / len(head_rows) * 1e6, 3),
             "bytes_per_launch": round(dom_bytes / len(head_rows)),
+            "achieved_at_p10_p50_p90_launch": roof_spread,
         },
         "cpu_baseline": cpu,
         "decode_sweep": decode_rows,
@@ -839,12 +937,27 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def _oracle_time(fn, budget_s):
+    """Seconds per call of fn, repeated for about budget_s."""
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        fn()
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    return (time.perf_counter() - t0) / reps
+
+
 def cpu_baseline(inputs):
-    """The oracle, as it stands, on a bounded sample: each headline shape with
-    the first 256 output columns, repeated for about 1.5 s (about 14 s of
-    CPU work in all).  Weight quantisation is load time (untimed), as on the
-    GPU; the timed work per shape is quant(x) + dequantise + fp64 matmul +
-    bias."""
+    """The oracle, as it stands, on bounded samples (about 20 s of CPU work in
+    all).  Headline (the reported value, in the metric's GB/s): each headline
+    shape with the first 256 output columns, repeated for about 1.5 s; weight
+    quantisation is load time (untimed), as on the GPU; the timed work per
+    shape is quant(x) + dequantise + fp64 matmul + bias.  Beside it, in their
+    own units: one prefill shape (M = 2048, N = 14336, K = 5120) restricted to
+    256 output columns (TFLOP/s over the sample's 2MNK) and one A16WFP4 BMM
+    (MLA V-up, M = 256, 16 heads: GB/s over its algorithmic bytes)."""
     from oracle import linalg as OL
     from oracle import quant as OQ
     try:
@@ -861,22 +974,44 @@ def cpu_baseline(inputs):
         b = inputs.bias(N, 2)[:NS]
         for M in HEADLINE_M:
             x = inputs.activations(M, K, 2)
-            t0 = time.perf_counter()
-            reps = 0
-            while True:
+
+            def step():
                 qa, sa = OQ.quant_1x32(x)
                 y, _ = OL.gemm_a4w4_from_quant(qa, sa, qw, sw, b)
                 OL.to_bf16(y)
-                reps += 1
-                if time.perf_counter() - t0 > 1.5:
-                    break
-            total_s += (time.perf_counter() - t0) / reps
+            total_s += _oracle_time(step, 1.5)
             total_bytes += pipeline_bytes(M, NS, K, True)
+    # prefill sample
+    Mp, Np, Kp = 2048, 14336, 5120
+    xp = inputs.activations(Mp, Kp, 3, outliers=True)
+    qwp, swp = OQ.quant_1x32(inputs.weights(Np, Kp, 2)[:NS])
+
+    def pre():
+        qa, sa = OQ.quant_1x32(xp)
+        y, _ = OL.gemm_a4w4_from_quant(qa, sa, qwp, swp)
+        OL.to_bf16(y)
+    tp = _oracle_time(pre, 2.0)
+    # BMM sample
+    B, Mb, Nb, Kb = BMM_HEADS, 256, 256, 512
+    pbm = inputs.bmm_problem(B, Mb, Nb, Kb, 4)
+    qb, sb = OQ.quant_1x32(pbm["w"].reshape(B * Nb, Kb))
+    qb, sb = qb.reshape(B, Nb, Kb // 2), sb.reshape(B, Nb, Kb // 32)
+
+    def bmm():
+        o, _ = OL.bmm_a16wfp4(pbm["x"], qb, sb)
+        OL.to_bf16(o)
+    tb = _oracle_time(bmm, 1.5)
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"headline shapes (M in {HEADLINE_M}, (N,K) in {DECODE_NK}) restricted to the "
                       f"first {NS} output columns; numpy fp64, BLAS threads {threads}; "
-                      f"weight quantisation untimed (load time)"}
+                      f"weight quantisation untimed (load time)",
+            "prefill": {"value": round(2 * Mp * NS * Kp / tp / 1e12, 5), "unit": "TFLOP/s",
+                        "sample": f"M={Mp}, N={Np} (first {NS} columns), K={Kp}: quant(x) + fp64 GEMM",
+                        "seconds": round(tp, 3)},
+            "bmm": {"value": round(bmm_bytes(B, Mb, Nb, Kb) / tb / 1e9, 4), "unit": "GB/s",
+                    "sample": f"A16WFP4 V-up, {B} heads, M={Mb}, N={Nb}, K={Kb}: fp64 batched product",
+                    "seconds": round(tb, 4)}}
 
 
 if __name__ == "__main__":
