@@ -10,6 +10,7 @@
     python bench.py --traffic-summary FETCH.csv WRITE.csv CMD...   (CPU only)
     python bench.py --trace-summary STATS.csv TRACE.csv MARKER.csv BENCH.log CMD...  (CPU only)
     python bench.py --prefill-summary TRACE.csv COUNTERS.csv CMD...  (CPU only)
+    python bench.py --prefill-stall-summary PASS_A.csv PASS_B.csv PASS_C.csv CMD...  (CPU only)
 
 Headline (the metric's M <= 16 decode regime): one step is one pass over the
 decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
@@ -606,7 +607,106 @@ def prefill_counter_summary(trace_csv, pmc_csv, command):
         print(r)
 
 
+PREFILL_STALL_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                "gemm_prefill_kernel__M8192_stall_counters.md")
+# the three counter passes of the stall summary (each well within one
+# pass's limits: at most 8 SQ and 2 GRBM counters)
+STALL_PASSES = [
+    ["GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+     "SQ_VALU_MFMA_BUSY_CYCLES"],
+    ["GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+     "SQ_ACTIVE_INST_VMEM"],
+    ["GRBM_GUI_ACTIVE", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_DATA_FIFO_FULL",
+     "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_MFMA"],
+]
+
+
+def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command):
+    """Where the prefill kernel's waves spend their time (PREFILL_STALL_MD):
+    three counter passes of prefill_pass (STALL_PASSES), per (N, K) averaged over the measured
+    launches (each shape's warm-up launch dropped).  SQ_WAVE_CYCLES and the
+    SQ_WAIT_* counters count quad-cycles summed over waves; the SQ_ACTIVE_INST_*
+    counters count cycles summed over waves; per-SE counters are summed over
+    the 32 SEs (8 XCDs x 4)."""
+    import csv
+
+    def load(path):
+        d = {}
+        for r in csv.DictReader(open(path)):
+            if "gemm_prefill_kernel" not in r["Kernel_Name"]:
+                continue
+            e = d.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [d[k] for k in sorted(d)]
+
+    A, B, C = load(pmc_a), load(pmc_b), load(pmc_c)
+    per = 1 + PREFILL_PASS_REPS
+    assert len(A) == len(B) == len(C) == per * len(DECODE_NK), (len(A), len(B), len(C))
+    M = PREFILL_PASS_M
+    rows = []
+    for si, (N, K) in enumerate(DECODE_NK):
+        ia = [A[si * per + k] for k in range(1, per)]
+        ib = [B[si * per + k] for k in range(1, per)]
+        ic = [C[si * per + k] for k in range(1, per)]
+
+        def mean(lst, key):
+            return float(np.mean([e[key] for e in lst]))
+        cyc = mean(ia, "GRBM_GUI_ACTIVE") / 8                     # per XCD: the kernel's cycles
+        wave_cyc = 4 * mean(ia, "SQ_WAVE_CYCLES")                  # summed over waves
+        wave_cyc_b = 4 * mean(ib, "SQ_WAVE_CYCLES")
+        pf = 2.0 * M * N * K / (mean(ia, "us") * 1e-6) / 1e15
+        rows.append(dict(
+            N=N, K=K, counter_run_us=round(mean(ia, "us"), 1), clock_ghz=round(cyc / (mean(ia, "us") * 1e3), 3),
+            pflops_counter_run=round(pf, 3),
+            mfma_busy=round(mean(ia, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * cyc), 3),
+            wave_wait_any=round(4 * mean(ia, "SQ_WAIT_ANY") / wave_cyc, 3),
+            wave_wait_inst_any=round(4 * mean(ia, "SQ_WAIT_INST_ANY") / wave_cyc, 3),
+            wave_wait_inst_lds=round(4 * mean(ia, "SQ_WAIT_INST_LDS") / wave_cyc, 3),
+            wave_active_any=round(mean(ib, "SQ_ACTIVE_INST_ANY") / wave_cyc_b, 3),
+            wave_active_valu=round(mean(ib, "SQ_ACTIVE_INST_VALU") / wave_cyc_b, 3),
+            wave_active_lds=round(mean(ib, "SQ_ACTIVE_INST_LDS") / wave_cyc_b, 3),
+            wave_active_vmem=round(mean(ib, "SQ_ACTIVE_INST_VMEM") / wave_cyc_b, 3),
+            lds_insts_per_kstep_per_wave=round(mean(ic, "SQ_INSTS_LDS") / (M / 256 * -(-N // 256) * (K / 128) * 8), 2),
+            mfma_insts_per_kstep_per_wave=round(mean(ic, "SQ_INSTS_MFMA") / (M / 256 * -(-N // 256) * (K / 128) * 8), 2),
+            lds_active_per_cu=round(mean(ic, "SQ_LDS_IDX_ACTIVE") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 3),
+            lds_bank_conflict_per_cu=round(mean(ic, "SQ_LDS_BANK_CONFLICT") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 4),
+            lds_addr_conflict_per_cu=round(mean(ic, "SQ_LDS_ADDR_CONFLICT") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 4),
+            lds_data_fifo_full_per_cu=round(mean(ic, "SQ_LDS_DATA_FIFO_FULL") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 4)))
+    lines = ["# gemm_prefill_kernel — where the waves spend their time at M = 8192", "",
+             "Workload `python bench.py --prefill-pass` (the prefill GEMM at M = 8192 for each",
+             f"(N, K), a warm-up launch then {PREFILL_PASS_REPS} launches, sweep inputs). Three counter passes:", "",
+             "```", *command, "```", "",
+             "Per shape, the mean over the measured launches of:",
+             "- clock = GRBM_GUI_ACTIVE / 8 XCDs / the launch's duration in the counter run;",
+             "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x those cycles);",
+             "- wave shares: each counter over the waves' total cycles (4 x SQ_WAVE_CYCLES):",
+             "  waiting for anything (`s_waitcnt`, barrier: SQ_WAIT_ANY), waiting to issue",
+             "  (SQ_WAIT_INST_ANY; its LDS part SQ_WAIT_INST_LDS), and executing any / VALU",
+             "  (MFMA included) / LDS / VMEM instructions (SQ_ACTIVE_INST_*);",
+             "- LDS and MFMA instructions per K-step per wave (SQ_INSTS_* over tiles x K-steps x 8",
+             "  waves; the loop itself issues 12 fragment reads, 32 MFMAs and one scale read per 4",
+             "  steps per wave);",
+             "- per-CU LDS shares: SQ_LDS_IDX_ACTIVE (LDS busy with indexed reads and writes), bank",
+             "  and address conflict stalls, data-FIFO-full cycles, over 256 CUs x the cycles.", "",
+             "| N | K | us | GHz | PF | MFMA busy | wait any | wait issue | wait issue LDS | active any | active VALU | active LDS | active VMEM | LDS/step/wave | MFMA/step/wave | LDS busy/CU | bank confl/CU | addr confl/CU | LDS data FIFO full/CU |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| " + " | ".join(str(r[k]) for k in (
+            "N", "K", "counter_run_us", "clock_ghz", "pflops_counter_run", "mfma_busy", "wave_wait_any",
+            "wave_wait_inst_any", "wave_wait_inst_lds", "wave_active_any", "wave_active_valu", "wave_active_lds",
+            "wave_active_vmem", "lds_insts_per_kstep_per_wave", "mfma_insts_per_kstep_per_wave", "lds_active_per_cu",
+            "lds_bank_conflict_per_cu", "lds_addr_conflict_per_cu", "lds_data_fifo_full_per_cu")) + " |")
+    lines += ["", "```json", json.dumps(dict(kernel="gemm_prefill_kernel", M=M, shapes=rows)), "```", ""]
+    with open(PREFILL_STALL_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {PREFILL_STALL_MD}")
+    for r in rows:
+        print(r)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--prefill-stall-summary":
+        return prefill_stall_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     if len(sys.argv) > 1 and sys.argv[1] == "--hbm-pass":
         return hbm_pass()
     if len(sys.argv) > 1 and sys.argv[1] == "--hbm-summary":
