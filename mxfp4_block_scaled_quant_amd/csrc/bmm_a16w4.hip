@@ -21,7 +21,7 @@
 // lane order), one barrier per m-tile, so activations are read from HBM
 // once, weights once per workgroup, and output written once.  Waves 0-3 issue all activation loads
 // and waves 4-7 all output stores (through a double-buffered LDS staging
-// area, as whole 16-byte pieces of rows): a wave's memory counter retires
+// area, as whole rows of the workgroup's columns, non-temporal): a wave's memory counter retires
 // loads and stores in issue order, so a wave that both stores and waits
 // for its loads would wait for its stores too.  The general kernel (any K):
 // a 256-thread workgroup owns one head and a 64 (m) x 128 (n) output tile;
@@ -159,8 +159,9 @@ constexpr int kWavesS = 8;
 // LDS of one instance (KF K-fragments, NT column tiles, output element
 // size ESZ, NS stages): NS stages of KF KiB (fragment c of a stage at c
 // KiB), a 1 KiB target for padding loads, then two output staging buffers,
-// each with a 16-row block per wave (rows of NT*16 elements plus 16 bytes to
-// spread banks).  A shallow ring: measured on MI355X with activations read
+// each holding the m-tile's 16 output rows over the workgroup's 8*NT*16
+// columns (wave w's columns at w*NT*16; rows padded by 16 bytes to spread
+// banks), so that stores go out as whole rows.  A shallow ring: measured on MI355X with activations read
 // from HBM, a three-stage ring beats deeper ones (K-up / V-up, M = 4096:
 // 23.2 / 24.1 us with three stages, 23.3 / 24.9 with four, 24.5 / 28.1 with
 // eight: the larger start-up burst of every workgroup delays its first
@@ -169,10 +170,9 @@ constexpr int kWavesS = 8;
 // 6.0).
 template <int KF, int NT, int ESZ, int NS>
 struct BmmLds {
-  static constexpr int kRowB = NT * 16 * ESZ;
-  static constexpr int kRowStride = kRowB + 16;
-  static constexpr int kBlock = 16 * kRowStride;         // one wave's staged block
-  static constexpr int kStgBuf = kWavesS * kBlock;       // one staging buffer
+  static constexpr int kRowB = NT * 16 * ESZ;                 // one wave's part of a row
+  static constexpr int kRowStride = kWavesS * kRowB + 16;
+  static constexpr int kStgBuf = 16 * kRowStride;             // one staging buffer
   static constexpr int kStage = KF * 1024;
   static constexpr int kStages = NS;
   static constexpr int kTrash = kStages * kStage;
@@ -306,18 +306,25 @@ __device__ __forceinline__ void stage_write(const v4f (&acc)[NT], uint32_t slot,
   }
 }
 
-// Store of a staged 16 x (NT*16) block (m-tile mt, first 16-column strip
-// s0) from LDS `slot`: piece k of the block is row k / CPR, 16-byte piece
-// k % CPR, so consecutive lanes write consecutive bytes of a row.  VEC:
-// whole pieces (N a multiple of the piece, aligned rows); otherwise each
-// element on its own.  Out-of-range elements get an out-of-range offset.
+// Store of rows 4*quarter..+3 of a staged m-tile (m-tile mt, the
+// workgroup's columns from 16-column strip c0) from staging buffer `stg`:
+// piece k is row 4*quarter + k / CPR, 16-byte piece k % CPR of it, so
+// consecutive lanes write consecutive bytes of a row and every store covers
+// whole rows of the workgroup's columns.  VEC: whole pieces (N a multiple of
+// the piece, aligned rows), written non-temporal (the output is not read
+// again here); otherwise each element on its own.  Out-of-range elements get
+// an out-of-range offset.  Measured on MI355X against the earlier staging of
+// one wave's 16 x NT*16 block per store (V-up rows then 64 bytes: half
+// lines), back-to-back launches at M = 4096: V-up 26.4 -> 22.5 us, K-up
+// (128-byte rows before) unchanged at 20.2-20.9 us.
 template <int NT, bool F32, bool VEC, int ROWSTRIDE>
-__device__ __forceinline__ void stage_store(const BmmArgs& p, int b, int mt, int s0, uint32_t slot, uint32_t lane) {
+__device__ __forceinline__ void stage_store(const BmmArgs& p, int b, int mt, int c0, uint32_t stg, int quarter,
+                                            uint32_t lane) {
   constexpr int esz = F32 ? 4 : 2;
   constexpr int EPP = 16 / esz;              // elements per piece
-  constexpr int CPR = NT * esz;              // pieces per staged row
-  constexpr int CH = 16 * CPR;               // pieces in the block
-  constexpr int PER = (CH + 63) / 64;        // pieces per lane
+  constexpr int CPR = kWavesS * NT * esz;    // pieces per staged row
+  constexpr int PER = 4 * CPR / 64;          // pieces per lane
+  static_assert(4 * CPR % 64 == 0, "whole pieces per lane");
   const int m0 = mt * 16;
   const int rows = max(0, min(16, p.M - m0));
   const __amdgpu_buffer_rsrc_t ro =
@@ -330,23 +337,18 @@ __device__ __forceinline__ void stage_store(const BmmArgs& p, int b, int mt, int
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const uint32_t k = lane + 64u * e;
-    const uint32_t row = k / CPR, piece = k % CPR;
-    n[e] = s0 * 16 + (int)piece * EPP;
-    ok[e] = k < CH && (int)row < rows;
+    const uint32_t row = (uint32_t)quarter * 4u + k / CPR, piece = k % CPR;
+    n[e] = c0 * 16 + (int)piece * EPP;
+    ok[e] = (int)row < rows;
     base[e] = (uint32_t)(row * p.som + n[e]) * esz;
-    ds_read16<0>(v[e], slot + (k < CH ? row : 0u) * ROWSTRIDE + piece * 16);
+    ds_read16<0>(v[e], stg + row * ROWSTRIDE + piece * 16);
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     asm volatile("" : "+v"(v[e]));
     if (VEC) {
-      // Staged rows of whole 128-byte lines go out non-temporal (the output
-      // is not read again here): measured K-up (128 bytes per row) M = 1024
-      // 9.0 -> 7.7 us, M = 4096 22.4 -> 22.0 us; half-line rows (V-up) were
-      // slower that way (M = 4096 23.4 -> 24.9 us), so they keep the default.
-      constexpr int kAux = CPR * 16 >= 128 ? 2 : 0;
-      __builtin_amdgcn_raw_buffer_store_b128(v[e], ro, ok[e] && n[e] < p.N ? base[e] : kOOB, 0, kAux);
+      __builtin_amdgcn_raw_buffer_store_b128(v[e], ro, ok[e] && n[e] < p.N ? base[e] : kOOB, 0, 2);
     } else {
 #pragma unroll
       for (int x = 0; x < EPP; ++x) {
@@ -459,7 +461,8 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
       __builtin_amdgcn_sched_barrier(0);
     }
 
-  const uint32_t slot = lds0 + L::kStg + (uint32_t)wv * L::kBlock;  // this wave's staging block (buffer 0)
+  const uint32_t stg = lds0 + L::kStg;                           // staging buffer 0
+  const uint32_t slot = stg + (uint32_t)wv * L::kRowB;               // this wave's columns in it
   for (int i = 0; i < cnt; ++i) {
     const int stage = i % kStages;
     // Loading waves: their loads of m-tile i were issued kStages-1
@@ -472,10 +475,9 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
       issue_xtile<KD, KF, L::kStage, L::kTrash>(p, b, mt0 + i + kStages - 1, i + kStages - 1 < cnt ? nmt : 0,
                                                 (i + kStages - 1) % kStages, kf, wv, lane);
     } else if (i > 0) {
-      // Storing waves: m-tile i-1 of source waves wv-4 and wv.
+      // Storing waves: rows 4*(wv-4)..+3 of m-tile i-1.
       const uint32_t buf = (uint32_t)((i - 1) & 1) * L::kStgBuf;
-      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, cb + (wv - 4) * NT, slot + buf - 4 * L::kBlock, lane);
-      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, cb + wv * NT, slot + buf, lane);
+      stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + i - 1, cb, stg + buf, wv - 4, lane);
     }
     // PA partial sums per column tile (fragment c adds into part c % PA), so
     // several independent accumulation chains keep the MFMA pipe busy; the
@@ -524,8 +526,7 @@ __global__ __launch_bounds__(512, 1) void bmm_stream_kernel(BmmArgs p, int S, in
   barrier_nofence();
   if (!loader && cnt > 0) {
     const uint32_t buf = (uint32_t)((cnt - 1) & 1) * L::kStgBuf;
-    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, cb + (wv - 4) * NT, slot + buf - 4 * L::kBlock, lane);
-    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, cb + wv * NT, slot + buf, lane);
+    stage_store<NT, F32, VEC, L::kRowStride>(p, b, mt0 + cnt - 1, cb, stg + buf, wv - 4, lane);
   }
   // Loads issued past the last m-tile (empty descriptors) still write LDS:
   // let them finish before the workgroup ends.
