@@ -4,13 +4,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-prefill] [--no-bmm]
     python bench.py --traffic-pass          (workload of the counter runs)
-    python bench.py --prefill-pass          (workload of the prefill counter runs)
+    python bench.py --prefill-pass [M]      (workload of the prefill counter runs; M = 8192 by default)
     python bench.py --hbm-pass              (workload of the quantisation / BMM counter runs)
     python bench.py --hbm-summary FETCH.csv WRITE.csv CMD...  (CPU only)
     python bench.py --traffic-summary FETCH.csv WRITE.csv CMD...   (CPU only)
     python bench.py --trace-summary STATS.csv TRACE.csv MARKER.csv BENCH.log CMD...  (CPU only)
     python bench.py --prefill-summary TRACE.csv COUNTERS.csv CMD...  (CPU only)
-    python bench.py --prefill-stall-summary PASS_A.csv PASS_B.csv PASS_C.csv CMD...  (CPU only)
+    python bench.py --prefill-stall-summary [--m M] PASS_A.csv PASS_B.csv PASS_C.csv CMD...  (CPU only)
 
 Headline (the metric's M <= 16 decode regime): one step is one pass over the
 decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
@@ -37,10 +37,12 @@ and the CPU oracle timed on bounded samples of the headline workload, one
 prefill shape and one BMM.
 
 Timing: every row's value is the mean over its timed replays (each replay a
-graph of >= 32 back-to-back launches, so graph-launch overhead is amortised);
-each replay is also timed on its own (an event between replays), and the
-rows carry the spread of the per-launch time over the replays (p10 / p50 /
-p90, `*_spread_us`); the headline likewise per step (`step_spread_us`).  The
+graph of >= 32 back-to-back launches, so graph-launch overhead is amortised),
+with nothing recorded between the replays; a second pass of as many replays,
+each between its own pair of events, gives the spread of the per-launch time
+(p10 / p50 / p90, `*_spread_us`).  The headline's K steps run between two
+events; a second pass of K steps timed in chunks of 10 steps gives its spread
+(`step_spread_us`, per step; its mean is the headline's).  The
 shader clock is sampled from sysfs (pp_dpm_sclk, current level) by a host
 thread during the headline, the roofline loop and the prefill sweep
 (`sclk`, `prefill.sclk`).
@@ -176,9 +178,10 @@ class Timer:
         return g
 
     def time_graphs(self, graphs, reps, warmup_s=0.025):
-        """Seconds per replay: an event before every replay and one after the
-        last, so each replay is timed on its own (mean over all, and the
-        spread: p10 / p50 / p90 over the replays)."""
+        """Seconds per replay: the mean from `reps` replays between two
+        events, then the spread (p10 / p50 / p90) from `reps` more, each
+        between its own pair of events.  An event recorded between replays
+        costs a few microseconds of its own, so it stays out of the mean."""
         # Untimed replays of the same sequence for at least warmup_s first:
         # after a pause the GPU takes a few milliseconds of load to reach its
         # steady clocks (measured: a timed run right after two warm-up
@@ -192,15 +195,21 @@ class Timer:
                 torch.cuda.synchronize()
                 if time.perf_counter() - t0 >= warmup_s:
                     break
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        b.record()
+        torch.cuda.synchronize()
+        mean = a.elapsed_time(b) * 1e-3 / reps
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record()
         for i in range(reps):
             graphs[i % len(graphs)].replay()
             ev[i + 1].record()
         torch.cuda.synchronize()
-        per = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)]
-        st = _stats(per)
-        st["mean"] = ev[0].elapsed_time(ev[reps]) * 1e-3 / reps
+        st = _stats([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps)])
+        st["mean"] = mean
         return st
 
 
@@ -390,9 +399,9 @@ PREFILL_PASS_M = 8192
 PREFILL_PASS_REPS = 4   # launches per shape the summary reads, after one warm-up launch
 
 
-def prefill_pass():
+def prefill_pass(M=PREFILL_PASS_M):
     """The workload of the prefill counter runs (run under rocprofv3): the
-    prefill GEMM at M = 8192 for each (N, K) of the sweep, one warm-up launch
+    prefill GEMM at M (8192 unless given) for each (N, K) of the sweep, one warm-up launch
     (its counters also catch the activity before it) then PREFILL_PASS_REPS
     launches, on the sweep's inputs (activations seed 3 with outliers,
     weights seed 2, no bias, bf16 out)."""
@@ -401,7 +410,6 @@ def prefill_pass():
     mx.lib()
     dev = torch.device("cuda:0")
     plan = []
-    M = PREFILL_PASS_M
     for (N, K) in DECODE_NK:
         W = mx.quantize_weight(inputs.bits_to_torch_bf16(inputs.weights(N, K, 2)).to(dev))
         x = inputs.bits_to_torch_bf16(inputs.activations(M, K, 3, outliers=True)).to(dev)
@@ -607,8 +615,9 @@ def prefill_counter_summary(trace_csv, pmc_csv, command):
         print(r)
 
 
-PREFILL_STALL_MD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                                "gemm_prefill_kernel__M8192_stall_counters.md")
+def prefill_stall_md(M):
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"gemm_prefill_kernel__M{M}_stall_counters.md")
 # the three counter passes of the stall summary (each well within one
 # pass's limits: at most 8 SQ and 2 GRBM counters)
 STALL_PASSES = [
@@ -621,9 +630,9 @@ STALL_PASSES = [
 ]
 
 
-def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command):
-    """Where the prefill kernel's waves spend their time (PREFILL_STALL_MD):
-    three counter passes of prefill_pass (STALL_PASSES), per (N, K) averaged over the measured
+def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command, M=PREFILL_PASS_M):
+    """Where the prefill kernel's waves spend their time (prefill_stall_md(M)):
+    three counter passes of prefill_pass(M) (STALL_PASSES), per (N, K) averaged over the measured
     launches (each shape's warm-up launch dropped).  SQ_WAVE_CYCLES and the
     SQ_WAIT_* counters count quad-cycles summed over waves; the SQ_ACTIVE_INST_*
     counters count cycles summed over waves; per-SE counters are summed over
@@ -633,16 +642,17 @@ def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command):
     def load(path):
         d = {}
         for r in csv.DictReader(open(path)):
-            if "gemm_prefill_kernel" not in r["Kernel_Name"]:
+            name = r["Kernel_Name"]
+            if "gemm_prefill_kernel" not in name and "gemm_prefill_n128_kernel" not in name:
                 continue
-            e = d.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3})
+            e = d.setdefault(int(r["Dispatch_Id"]), {"us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
+                                                       "bn": 128 if "n128" in name else 256})
             e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         return [d[k] for k in sorted(d)]
 
     A, B, C = load(pmc_a), load(pmc_b), load(pmc_c)
     per = 1 + PREFILL_PASS_REPS
     assert len(A) == len(B) == len(C) == per * len(DECODE_NK), (len(A), len(B), len(C))
-    M = PREFILL_PASS_M
     rows = []
     for si, (N, K) in enumerate(DECODE_NK):
         ia = [A[si * per + k] for k in range(1, per)]
@@ -655,8 +665,11 @@ def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command):
         wave_cyc = 4 * mean(ia, "SQ_WAVE_CYCLES")                  # summed over waves
         wave_cyc_b = 4 * mean(ib, "SQ_WAVE_CYCLES")
         pf = 2.0 * M * N * K / (mean(ia, "us") * 1e-6) / 1e15
+        bn = ia[0]["bn"]
+        tiles = -(-M // 256) * -(-N // bn)
         rows.append(dict(
-            N=N, K=K, counter_run_us=round(mean(ia, "us"), 1), clock_ghz=round(cyc / (mean(ia, "us") * 1e3), 3),
+            N=N, K=K, tile=f"256x{bn}", tiles=tiles,
+            counter_run_us=round(mean(ia, "us"), 1), clock_ghz=round(cyc / (mean(ia, "us") * 1e3), 3),
             pflops_counter_run=round(pf, 3),
             mfma_busy=round(mean(ia, "SQ_VALU_MFMA_BUSY_CYCLES") / (1024 * cyc), 3),
             wave_wait_any=round(4 * mean(ia, "SQ_WAIT_ANY") / wave_cyc, 3),
@@ -666,15 +679,18 @@ def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command):
             wave_active_valu=round(mean(ib, "SQ_ACTIVE_INST_VALU") / wave_cyc_b, 3),
             wave_active_lds=round(mean(ib, "SQ_ACTIVE_INST_LDS") / wave_cyc_b, 3),
             wave_active_vmem=round(mean(ib, "SQ_ACTIVE_INST_VMEM") / wave_cyc_b, 3),
-            lds_insts_per_kstep_per_wave=round(mean(ic, "SQ_INSTS_LDS") / (M / 256 * -(-N // 256) * (K / 128) * 8), 2),
-            mfma_insts_per_kstep_per_wave=round(mean(ic, "SQ_INSTS_MFMA") / (M / 256 * -(-N // 256) * (K / 128) * 8), 2),
+            lds_insts_per_kstep_per_wave=round(mean(ic, "SQ_INSTS_LDS") / (tiles * (K / 128) * 8), 2),
+            mfma_insts_per_kstep_per_wave=round(mean(ic, "SQ_INSTS_MFMA") / (tiles * (K / 128) * 8), 2),
             lds_active_per_cu=round(mean(ic, "SQ_LDS_IDX_ACTIVE") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 3),
             lds_bank_conflict_per_cu=round(mean(ic, "SQ_LDS_BANK_CONFLICT") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 4),
             lds_addr_conflict_per_cu=round(mean(ic, "SQ_LDS_ADDR_CONFLICT") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 4),
             lds_data_fifo_full_per_cu=round(mean(ic, "SQ_LDS_DATA_FIFO_FULL") / (256 * mean(ic, "GRBM_GUI_ACTIVE") / 8), 4)))
-    lines = ["# gemm_prefill_kernel — where the waves spend their time at M = 8192", "",
-             "Workload `python bench.py --prefill-pass` (the prefill GEMM at M = 8192 for each",
-             f"(N, K), a warm-up launch then {PREFILL_PASS_REPS} launches, sweep inputs). Three counter passes:", "",
+    arg = "" if M == PREFILL_PASS_M else f" {M}"
+    lines = [f"# gemm_prefill_kernel — where the waves spend their time at M = {M}", "",
+             f"Workload `python bench.py --prefill-pass{arg}` (the prefill GEMM at M = {M} for each",
+             f"(N, K), whole tiles, a warm-up launch then {PREFILL_PASS_REPS} launches, sweep inputs;",
+             "the tile width is the one the launcher picks, 256 x 128 where 256-wide tiles would fill",
+             "at most half a round of compute units). Three counter passes:", "",
              "```", *command, "```", "",
              "Per shape, the mean over the measured launches of:",
              "- clock = GRBM_GUI_ACTIVE / 8 XCDs / the launch's duration in the counter run;",
@@ -684,28 +700,30 @@ def prefill_stall_summary(pmc_a, pmc_b, pmc_c, command):
              "  (SQ_WAIT_INST_ANY; its LDS part SQ_WAIT_INST_LDS), and executing any / VALU",
              "  (MFMA included) / LDS / VMEM instructions (SQ_ACTIVE_INST_*);",
              "- LDS and MFMA instructions per K-step per wave (SQ_INSTS_* over tiles x K-steps x 8",
-             "  waves; the loop itself issues 12 fragment reads, 32 MFMAs and one scale read per 4",
-             "  steps per wave);",
+             "  waves; per K-step and wave the 256-wide loop issues 12 fragment reads and 32 MFMAs,",
+             "  the 128-wide one 10 and 16, each one scale read per 4 steps);",
              "- per-CU LDS shares: SQ_LDS_IDX_ACTIVE (LDS busy with indexed reads and writes), bank",
              "  and address conflict stalls, data-FIFO-full cycles, over 256 CUs x the cycles.", "",
-             "| N | K | us | GHz | PF | MFMA busy | wait any | wait issue | wait issue LDS | active any | active VALU | active LDS | active VMEM | LDS/step/wave | MFMA/step/wave | LDS busy/CU | bank confl/CU | addr confl/CU | LDS data FIFO full/CU |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "| N | K | tile | tiles | us | GHz | PF | MFMA busy | wait any | wait issue | wait issue LDS | active any | active VALU | active LDS | active VMEM | LDS/step/wave | MFMA/step/wave | LDS busy/CU | bank confl/CU | addr confl/CU | LDS data FIFO full/CU |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         lines.append("| " + " | ".join(str(r[k]) for k in (
-            "N", "K", "counter_run_us", "clock_ghz", "pflops_counter_run", "mfma_busy", "wave_wait_any",
+            "N", "K", "tile", "tiles", "counter_run_us", "clock_ghz", "pflops_counter_run", "mfma_busy", "wave_wait_any",
             "wave_wait_inst_any", "wave_wait_inst_lds", "wave_active_any", "wave_active_valu", "wave_active_lds",
             "wave_active_vmem", "lds_insts_per_kstep_per_wave", "mfma_insts_per_kstep_per_wave", "lds_active_per_cu",
             "lds_bank_conflict_per_cu", "lds_addr_conflict_per_cu", "lds_data_fifo_full_per_cu")) + " |")
     lines += ["", "```json", json.dumps(dict(kernel="gemm_prefill_kernel", M=M, shapes=rows)), "```", ""]
-    with open(PREFILL_STALL_MD, "w") as fh:
+    with open(prefill_stall_md(M), "w") as fh:
         fh.write("\n".join(lines))
-    print(f"wrote {PREFILL_STALL_MD}")
+    print(f"wrote {prefill_stall_md(M)}")
     for r in rows:
         print(r)
 
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--prefill-stall-summary":
+        if sys.argv[2] == "--m":
+            return prefill_stall_summary(sys.argv[4], sys.argv[5], sys.argv[6], sys.argv[7:], int(sys.argv[3]))
         return prefill_stall_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     if len(sys.argv) > 1 and sys.argv[1] == "--hbm-pass":
         return hbm_pass()
@@ -718,7 +736,7 @@ def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-pass":
         return traffic_pass()
     if len(sys.argv) > 1 and sys.argv[1] == "--prefill-pass":
-        return prefill_pass()
+        return prefill_pass(int(sys.argv[2]) if len(sys.argv) > 2 else PREFILL_PASS_M)
     if len(sys.argv) > 1 and sys.argv[1] == "--traffic-summary":
         return traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4:])
     ap = argparse.ArgumentParser()
@@ -807,15 +825,28 @@ def main():
     for i in range(args.warmup):
         step_graphs[i % cycle].replay()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with ClockSampler() as clk_head:
-        evs[0].record()
+        e0.record()
         for i in range(args.steps):
             step_graphs[i % cycle].replay()
-            evs[i + 1].record()
+        e1.record()
         torch.cuda.synchronize()
-    step_s = evs[0].elapsed_time(evs[args.steps]) * 1e-3 / args.steps
-    step_stats = _stats([evs[i].elapsed_time(evs[i + 1]) * 1e-3 for i in range(args.steps)])
+    step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    # The spread: the same number of steps again, timed in chunks of up to 10
+    # steps between events (an event between replays costs a few
+    # microseconds of its own: measured, one after every step lengthened the
+    # step by ~4 us), so it stays out of the figure above.
+    chunk = min(10, args.steps)
+    nch = max(1, args.steps // chunk)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nch + 1)]
+    evs[0].record()
+    for j in range(nch):
+        for i in range(chunk):
+            step_graphs[(j * chunk + i) % cycle].replay()
+        evs[j + 1].record()
+    torch.cuda.synchronize()
+    step_stats = _stats([evs[j].elapsed_time(evs[j + 1]) * 1e-3 / chunk for j in range(nch)])
     step_bytes = sum(pipeline_bytes(c["M"], c["N"], c["K"], True) for c in cases)
     value_gbs = step_bytes / step_s / 1e9
 
@@ -1013,7 +1044,7 @@ def main():
                     "GEMM; else quant then GEMM), weights preshuffled at load, rotated copies",
             "hbm_frac": round(value_gbs * 1e9 / PEAK_HBM, 4),
         },
-        "step_spread_us": _us(step_stats),
+        "step_spread_us": dict(_us(dict(step_stats, mean=step_s)), steps_per_sample=chunk),
         "sclk": {"headline": clk_head.summary(), "roofline": clk_roof.summary()},
         "roofline": {
             "kernel": "gemm_decode_kernel (W4A4 GEMM, M<=16, mean over the 9 headline shapes)",
