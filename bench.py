@@ -68,7 +68,7 @@ HEADLINE_M = [1, 4, 16]
 DECODE_M = [1, 4, 16, 32, 64]
 PREFILL_M = [512, 2048, 8192]
 BMM_CASES = [("K-up", 512, 192, False), ("V-up", 256, 512, True)]   # (name, N, K, batch_major)
-BMM_M = [1, 64, 256, 4096]
+BMM_M = [1, 64, 128, 256, 4096]
 BMM_HEADS = 16
 ROTATE_BYTES = 1 << 30
 MIN_LAUNCHES = 32          # launches per timed graph (amortises graph-launch overhead)

@@ -575,9 +575,26 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
     else if (nt <= 2 && kf <= 16) cfg = 2;
     else if (nt <= 1 && kf <= 32) cfg = 3;
   }
+  // A few m-tiles per workgroup (5 to 32 m-tiles per head at K = 192, 5 to
+  // 15 at K = 512, with 16 heads on 256 compute units): the head's columns
+  // over two workgroups, each loading and dequantising half the weights and
+  // reading the activations itself.  Measured on MI355X, back-to-back
+  // launches (us, whole head / two column halves): K-up M = 80 4.60 / 3.65,
+  // M = 128 4.67 / 3.76, M = 256 5.06 / 4.53, M = 512 6.28 / 6.18, M = 1024
+  // 8.00 / 8.76; V-up M = 128 5.13 / 4.18, M = 192 5.22 / 5.09, M = 256
+  // 5.34 / 5.93.
+  const int s_full = (int)((cus + B - 1) / B);
+  if (cfg == 4 && nt > 2 && nmt <= 2 * s_full) {
+    cfg = 8;
+    NB = 2;
+  } else if (cfg == 2 && kf == 16 && nt == 2 && nmt < s_full) {
+    cfg = 9;
+    NB = 2;
+  }
   if (cfg) {
-    // Workgroups per head: enough to fill the device, each with whole m-tiles.
-    int S = (int)((cus + B - 1) / B);
+    // Workgroups per head and column block: enough to fill the device (the
+    // small-M blocks keep those of a whole head), each with whole m-tiles.
+    int S = small ? s_full : (int)((cus + B * NB - 1) / (B * NB));
     if (S > nmt) S = nmt;
     if (S < 1) S = 1;
     const int T = (nmt + S - 1) / S;
@@ -599,6 +616,8 @@ hipError_t launch_bmm_a16w4(const void* x, int64_t sxb, int64_t sxm, const void*
     else MXFP4_BMM_LAUNCH_NS(KF_, NT_, 3);           \
   } while (0)
     if (cfg == 4) MXFP4_BMM_LAUNCH(6, 4);
+    else if (cfg == 8) MXFP4_BMM_LAUNCH(6, 2);
+    else if (cfg == 9) MXFP4_BMM_LAUNCH(16, 1);
     else if (cfg == 1) MXFP4_BMM_LAUNCH(8, 4);
     else if (cfg == 2) MXFP4_BMM_LAUNCH(16, 2);
     else if (cfg == 5) MXFP4_BMM_LAUNCH_NS(6, 1, 2);

@@ -56,6 +56,11 @@ CASES = [
     # three-stage ring), the last workgroup with three, the last tile 7 rows
     ("kup_M1287", 16, 1287, 512, 192, False),
     ("vup_M1287", 16, 1287, 256, 512, True),
+    # the head's columns over two workgroups (a few m-tiles per head): K-up
+    # with 32 m-tiles (four per workgroup, the last 4 rows), V-up with 10
+    # (the last 6 rows)
+    ("kup_M500_colsplit", 16, 500, 512, 192, False),
+    ("vup_M150_colsplit", 16, 150, 256, 512, True),
 ]
 
 
