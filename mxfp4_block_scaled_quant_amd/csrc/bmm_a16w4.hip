@@ -13,17 +13,19 @@
 //
 // Two kernels.  The streaming kernel (shapes whose weight slice fits in
 // registers, which covers the MLA K-up 512 x 192 and V-up 256 x 512 heads):
-// a 512-thread workgroup owns one head (for M <= 64 one 128-column block of
-// it) and a run of 16-row m-tiles; each of its 8 waves dequantises its 1/8
-// of the workgroup's output columns once into registers (bf16 MFMA
-// fragments), and the activation m-tiles stream through
-// a ring of two or three LDS stages by buffer->LDS loads (in the MFMA's
-// lane order), one barrier per m-tile, so activations are read from HBM
-// once, weights once per workgroup, and output written once.  Waves 0-3 issue all activation loads
-// and waves 4-7 all output stores (through a double-buffered LDS staging
-// area, as whole rows of the workgroup's columns, non-temporal): a wave's memory counter retires
-// loads and stores in issue order, so a wave that both stores and waits
-// for its loads would wait for its stores too.  The general kernel (any K):
+// a 512-thread workgroup owns one head (with few m-tiles per head, one
+// column block of it: 128 columns for M <= 64, half the head a little
+// above) and a run of 16-row m-tiles; each of its 8 waves dequantises its
+// 1/8 of the workgroup's output columns once into registers (bf16 MFMA
+// fragments), and the activation m-tiles stream through a ring of two or
+// three LDS stages by buffer->LDS loads (in the MFMA's lane order), one
+// barrier per m-tile, so activations are read from HBM once, weights once
+// per workgroup, and output written once.  Waves 0-3 issue all activation
+// loads and waves 4-7 all output stores (through a double-buffered LDS
+// staging area, as whole rows of the workgroup's columns, non-temporal): a
+// wave's memory counter retires loads and stores in issue order, so a wave
+// that both stores and waits for its loads would wait for its stores too.
+// The general kernel (any K):
 // a 256-thread workgroup owns one head and a 64 (m) x 128 (n) output tile;
 // wave w takes 32 columns (2 MFMA tiles) over all 64 rows (4 MFMA tiles).  The weight acts as the MFMA's A operand (16 output columns
 // n per tile) and the activations as its B operand (16 rows m), so each lane
