@@ -41,8 +41,12 @@ graph of >= 32 back-to-back launches, so graph-launch overhead is amortised),
 with nothing recorded between the replays; a second pass of as many replays,
 each between its own pair of events, gives the spread of the per-launch time
 (p10 / p50 / p90, `*_spread_us`).  The headline's K steps run between two
-events; a second pass of K steps timed in chunks of 10 steps gives its spread
-(`step_spread_us`, per step; its mean is the headline's).  The
+events, replayed as graphs of 10 steps each (90 linear calls per graph, as a
+captured decode pass over a model's layers; single-step graphs for a
+remainder); a second pass of as many steps, an event after each 10-step
+graph, gives its spread (`step_spread_us`, per step; its mean is the
+headline's), and a third with one graph per step is reported beside it
+(`one_step_per_graph`: each graph launch costs a few microseconds).  The
 shader clock is sampled from sysfs (pp_dpm_sclk, current level) by a host
 thread during the headline, the roofline loop and the prefill sweep
 (`sclk`, `prefill.sclk`).
@@ -72,6 +76,7 @@ BMM_M = [1, 64, 128, 256, 4096]
 BMM_HEADS = 16
 ROTATE_BYTES = 1 << 30
 MIN_LAUNCHES = 32          # launches per timed graph (amortises graph-launch overhead)
+HEADLINE_GRAPH_STEPS = 10  # headline steps per captured graph
 
 METRIC = "W4A4 MXFP4 GEMM TFLOPS & % FP4 peak (M≥2048); GB/s & % HBM at M≤16"
 
@@ -801,52 +806,89 @@ def main():
         mx.mxfp4_linear(c["x"], copy.w_pre, copy.ws_pre, c["N"], c["bias"], torch.bfloat16,
                         out=c["out"], workspace=c["work"])
 
-    # One graph per step position of the rotation cycle: launch i of shape (N,K)
-    # uses copy (i mod R); the cycle repeats after lcm over shapes of R/3 steps.
+    # Rotation: at position p of the cycle, the j-th launch of shape (N,K) in
+    # the step uses copy (p * per_step + j) mod R; the cycle repeats after
+    # lcm over shapes of R / gcd(R, per_step) steps.
     per_step = {nk: sum(1 for c in cases if (c["N"], c["K"]) == nk) for nk in DECODE_NK}
     cycle = 1
     for nk in DECODE_NK:
         R = len(weights[nk])
         k = R // np.gcd(R, per_step[nk])
         cycle = int(np.lcm(cycle, k))
-    counters = {nk: 0 for nk in DECODE_NK}
-    step_graphs = []
 
-    def one_step():
-        for c in cases:
-            nk = (c["N"], c["K"])
-            copy = weights[nk][counters[nk] % len(weights[nk])]
-            counters[nk] += 1
-            launch_case(c, copy)
+    def capture_steps(pos, n):
+        """A graph of n consecutive steps from rotation position pos."""
+        counters = {nk: (pos * per_step[nk]) % len(weights[nk]) for nk in DECODE_NK}
 
-    for _ in range(cycle):
-        step_graphs.append(T.capture(one_step))
+        def body():
+            for _ in range(n):
+                for c in cases:
+                    nk = (c["N"], c["K"])
+                    launch_case(c, weights[nk][counters[nk] % len(weights[nk])])
+                    counters[nk] += 1
+        return T.capture(body)
 
+    # Steps are replayed as graphs of HEADLINE_GRAPH_STEPS steps (each graph
+    # holds 9 x that many linear calls, as a captured decode pass over a
+    # model's layers would), single-step graphs for any remainder: each graph
+    # launch costs ~4 us of its own before its first kernel (measured: 127.5
+    # us per step with one step per graph, 123.2 with ten).
+    step_graphs = [capture_steps(p, 1) for p in range(cycle)]
+    multi = {}
+
+    def run_steps(pos, n, events=None):
+        """Replay n steps from position pos; returns the next position.  With
+        `events`, one event after every full multi-step graph."""
+        G = HEADLINE_GRAPH_STEPS
+        for _ in range(n // G):
+            if pos not in multi:
+                multi[pos] = capture_steps(pos, G)
+            multi[pos].replay()
+            if events is not None:
+                events.append(torch.cuda.Event(enable_timing=True))
+                events[-1].record()
+            pos = (pos + G) % cycle
+        for _ in range(n % G):
+            step_graphs[pos].replay()
+            pos = (pos + 1) % cycle
+        return pos
+
+    # capture every multi-step graph the runs below replay, before any timing
+    pos = args.warmup % cycle
+    for _ in range(2 * (args.steps // HEADLINE_GRAPH_STEPS) + 1):
+        if pos not in multi:
+            multi[pos] = capture_steps(pos, HEADLINE_GRAPH_STEPS)
+        pos = (pos + HEADLINE_GRAPH_STEPS) % cycle
     for i in range(args.warmup):
         step_graphs[i % cycle].replay()
     torch.cuda.synchronize()
+    pos = args.warmup % cycle
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with ClockSampler() as clk_head:
         e0.record()
-        for i in range(args.steps):
-            step_graphs[i % cycle].replay()
+        pos = run_steps(pos, args.steps)
         e1.record()
         torch.cuda.synchronize()
     step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
-    # The spread: the same number of steps again, timed in chunks of up to 10
-    # steps between events (an event between replays costs a few
-    # microseconds of its own: measured, one after every step lengthened the
-    # step by ~4 us), so it stays out of the figure above.
-    chunk = min(10, args.steps)
-    nch = max(1, args.steps // chunk)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nch + 1)]
+    # The spread: as many steps again, an event after every multi-step graph
+    # (per step: the graph's time over its steps); an event between replays
+    # costs a few microseconds of its own, so it stays out of the figure above.
+    evs = [torch.cuda.Event(enable_timing=True)]
     evs[0].record()
-    for j in range(nch):
-        for i in range(chunk):
-            step_graphs[(j * chunk + i) % cycle].replay()
-        evs[j + 1].record()
+    pos = run_steps(pos, args.steps - args.steps % HEADLINE_GRAPH_STEPS, evs)
     torch.cuda.synchronize()
-    step_stats = _stats([evs[j].elapsed_time(evs[j + 1]) * 1e-3 / chunk for j in range(nch)])
+    chunk = HEADLINE_GRAPH_STEPS
+    step_stats = (_stats([evs[j].elapsed_time(evs[j + 1]) * 1e-3 / chunk for j in range(len(evs) - 1)])
+                  if len(evs) > 1 else _stats([step_s]))
+    # The same steps with one graph per step, for comparison with that form.
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record()
+    for i in range(args.steps):
+        step_graphs[(pos + i) % cycle].replay()
+    e3.record()
+    torch.cuda.synchronize()
+    step_s_single = e2.elapsed_time(e3) * 1e-3 / args.steps
     step_bytes = sum(pipeline_bytes(c["M"], c["N"], c["K"], True) for c in cases)
     value_gbs = step_bytes / step_s / 1e9
 
@@ -1045,6 +1087,9 @@ def main():
             "hbm_frac": round(value_gbs * 1e9 / PEAK_HBM, 4),
         },
         "step_spread_us": dict(_us(dict(step_stats, mean=step_s)), steps_per_sample=chunk),
+        "graph_steps": HEADLINE_GRAPH_STEPS,
+        "one_step_per_graph": {"ms_per_step": round(step_s_single * 1e3, 5),
+                               "value": round(step_bytes / step_s_single / 1e9, 1)},
         "sclk": {"headline": clk_head.summary(), "roofline": clk_roof.summary()},
         "roofline": {
             "kernel": "gemm_decode_kernel (W4A4 GEMM, M<=16, mean over the 9 headline shapes)",
