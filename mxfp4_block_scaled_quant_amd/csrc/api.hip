@@ -189,8 +189,8 @@ size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K) {
 // Which GEMM kernel a call of M rows takes: 1 = small-M, 2 = large-M.
 static int gemm_path(int64_t M) {
   const int path = get_gemm_path_override();
-  if (path == 1 && M <= 64) return 1;
-  if (path >= 2) return 2;
+  if ((path == 1 || path == 7 || path == 8) && M <= 64) return 1;
+  if (path >= 2 && path <= 6) return 2;
   return M <= 64 ? 1 : 2;
 }
 
@@ -488,7 +488,7 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, cons
 
 // Test hook (include/mxfp4_testing.h): force a GEMM kernel on this thread.
 int mxfp4_testing_set_gemm_path(int path) {
-  if (path < 0 || path > 6) return MXFP4_ERR_ARG;
+  if (path < 0 || path > 8) return MXFP4_ERR_ARG;
   set_gemm_path_override(path);
   return MXFP4_OK;
 }

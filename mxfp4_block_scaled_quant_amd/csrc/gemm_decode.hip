@@ -260,6 +260,93 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
   reduce_store<MT, NS, MAXW>(reinterpret_cast<float*>(red), acc, p, s0);
 }
 
+// Persistent form, for more rows (each workgroup of the form above re-reads
+// all M activation rows of its K-run, bytes that grow with M while the
+// weights do not): one workgroup per compute unit walks the strips
+// s = blockIdx.x + k * gridDim.x, one scale group (4 K-steps) per wave; a
+// wave loads its group's activation operands and scales once, and they stay
+// in registers; the weights of the next D strips are in flight in a ring of
+// registers while the current strip's MFMAs and reduction run.  Per strip a
+// wave's partial tile is the one gemm_decode_kernel forms with one group per
+// wave, and reduce_store sums them in the same order: bitwise the same
+// output.  The reduction areas alternate between strips, so the one barrier
+// inside reduce_store also orders a strip's LDS reads before the writes two
+// strips later.
+template <int MT, int MAXW, int D>
+__global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
+  extern __shared__ v4f red[];
+  constexpr size_t kRedFloats = reduce_lds_bytes<MT, 1, MAXW>() / sizeof(float);
+  const int lane = threadIdx.x & 63;
+  const int g = threadIdx.x >> 6;  // this wave's scale group
+  const bool gv = g < p.G;
+  const auto ra = make_rsrc(p.a, (uint32_t)MT * p.Kt * 1024u);
+  const auto rw = make_rsrc(p.w, (uint32_t)p.Ns * p.Kt * 1024u);
+  const auto ras = make_rsrc(p.as, (uint32_t)MT * p.G * 256u);
+  const auto rws = make_rsrc(p.ws, (uint32_t)p.Ns * p.G * 256u);
+
+  int4 af[4][MT];
+  uint32_t sa[MT];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = g * 4 + u;
+    const bool tv = gv && t < p.Kt;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      // rows past M are zero padding: skip their bytes
+      const int row = i * 16 + (lane & 15);
+      af[u][i] = buf_load16(ra, (tv && row < p.M) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i) sa[i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+
+  const int nk = (int)blockIdx.x < p.Ns ? (p.Ns - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  int4 bf[D][4];
+  uint32_t sb[D];
+  // Weights and scale of this wave's group of the k-th strip into ring slot
+  // `slot` (strips past the end load zeros).
+  auto issue = [&](int k, int4 (&b)[4], uint32_t& sc) {
+    const int s = (int)blockIdx.x + k * (int)gridDim.x;
+    const bool sv = k < nk && gv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = g * 4 + u;
+      const uint32_t off = (sv && t < p.Kt) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
+      b[u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+    }
+    sc = buf_load4(rws, sv ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, bf[d], sb[d]);
+
+  for (int k0 = 0; k0 < nk; k0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int k = k0 + d;
+      if (k >= nk) break;  // the same for every wave of the workgroup
+      v4f acc[MT][1];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i][0] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          switch (u) {
+            case 0: acc[i][0] = mfma_sel<0>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
+            case 1: acc[i][0] = mfma_sel<1>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
+            case 2: acc[i][0] = mfma_sel<2>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
+            default: acc[i][0] = mfma_sel<3>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
+          }
+        }
+      issue(k + D, bf[d], sb[d]);
+      reduce_store<MT, 1, MAXW>(reinterpret_cast<float*>(red) + (size_t)(k & 1) * kRedFloats, acc, p,
+                                (int)blockIdx.x + k * (int)gridDim.x);
+    }
+  }
+  // the ring's last loads (past the end: zeros) land before the waves end
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // The same product with the activation quantisation fused in, for M <= 4:
 // the A operand is encoded from bf16 x in registers instead of being read
 // from a quantised copy.  Per scale group (4 K-steps x 4 blocks = 16 blocks
@@ -402,11 +489,42 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // of a few waves, which beat fewer workgroups of more waves with fewer
 // load rounds each); 12 with four (a compute unit holds 12 of those waves
 // either way, and fewer load rounds per wave win).
+// Where the persistent form pays: many strips per compute unit, at least ten
+// waves (groups) per workgroup, and many activation rows.  Measured on
+// MI355X with rotated weight copies (us, one workgroup per strip /
+// persistent): M = 64, K = 5120: N = 14336 14.14 / 13.39, N = 24576 21.01 /
+// 17.71, N = 34816 31.55 / 23.98; M = 16, N = 34816 18.78 / 18.03.  It loses
+// with fewer rows (M <= 8: 9-25% slower, the streaming form keeps more loads
+// in flight per compute unit), fewer strips (M = 16, N = 14336: 9.16 /
+// 10.09) or fewer waves (K = 4096, M = 64, N = 16384: 12.50 / 12.85).
+static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
+  if (kw < 10) return false;
+  if (M > 48) return Ns >= 3 * cus;
+  return M >= 16 && Ns >= 8 * cus;
+}
+
+template <int MT, int MAXW>
+static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t stream) {
+  // strips in flight per wave, as registers allow at 12 waves (six at one
+  // row tile measured no faster than four)
+  constexpr int D = MT == 4 ? 3 : 4;
+  const int grid = p.Ns < p.cus ? p.Ns : p.cus;
+  gemm_decode_persist_kernel<MT, MAXW, D><<<grid, 64 * kw, 2 * reduce_lds_bytes<MT, 1, MAXW>(), stream>>>(p);
+  return hipGetLastError();
+}
+
 template <int MT>
 static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   constexpr int MAXW = MT == 1 ? 16 : MT == 4 ? 12 : 8;
   const int gpw = (p.G + MAXW - 1) / MAXW;
   const int kw = (p.G + gpw - 1) / gpw;
+  // persistent form: one group per wave, bf16 / fp32 output from the GEMM
+  // layout (path 7 of the test hook forces it where it applies, 8 keeps the
+  // form above)
+  const bool persist_ok = gpw == 1 && kw <= 12 && !p.out_fp4 && !p.a_rowmajor;
+  const int ov = get_gemm_path_override();
+  const bool persist = persist_ok && (ov == 7 || (ov != 8 && decode_persist_pays(p.M, p.Ns, p.cus, kw)));
+  if (persist) return launch_decode_persist<MT, 12>(p, kw, stream);
   const bool one_strip = p.Ns >= 1024 && p.M <= 8 && !p.out_fp4;  // MXFP4 output: 32 columns per workgroup
   if constexpr (MT == 1) {
     if (gpw >= 2)

@@ -224,9 +224,9 @@ def test_valid_call_without_gpu_reports_device(lib):
 
 
 def test_testing_path_hook(lib):
-    assert lib.mxfp4_testing_set_gemm_path(7) == 7
+    assert lib.mxfp4_testing_set_gemm_path(9) == 7
     assert lib.mxfp4_testing_set_gemm_path(-1) == 7
-    for path in (6, 5, 4, 3, 2, 1, 0):
+    for path in (8, 7, 6, 5, 4, 3, 2, 1, 0):
         assert lib.mxfp4_testing_set_gemm_path(path) == 0
 
 
