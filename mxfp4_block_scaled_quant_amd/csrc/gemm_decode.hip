@@ -489,18 +489,21 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // of a few waves, which beat fewer workgroups of more waves with fewer
 // load rounds each); 12 with four (a compute unit holds 12 of those waves
 // either way, and fewer load rounds per wave win).
-// Where the persistent form pays: many strips per compute unit, at least ten
-// waves (groups) per workgroup, and many activation rows.  Measured on
-// MI355X with rotated weight copies (us, one workgroup per strip /
-// persistent): M = 64, K = 5120: N = 14336 14.14 / 13.39, N = 24576 21.01 /
-// 17.71, N = 34816 31.55 / 23.98; M = 16, N = 34816 18.78 / 18.03.  It loses
-// with fewer rows (M <= 8: 9-25% slower, the streaming form keeps more loads
-// in flight per compute unit), fewer strips (M = 16, N = 14336: 9.16 /
-// 10.09) or fewer waves (K = 4096, M = 64, N = 16384: 12.50 / 12.85).
+// Where the persistent form pays: many strips per compute unit, the more
+// the fewer activation rows, and at least ten waves (groups) per workgroup.
+// Measured on MI355X with rotated weight copies (us, streaming /
+// persistent), K = 5120: N = 34816 (8.5 strips per CU): M = 17 20.6 / 18.6,
+// M = 32 21.8 / 19.3, M = 48 25.2 / 21.2, M = 64 31.6 / 24.1; N = 24576 (6
+// per CU): M = 32 14.7 / 14.5, M = 33 18.8 / 15.6, M = 64 21.0 / 17.9;
+// N = 14336 (3.5 per CU): M = 32 10.3 / 10.9, M = 64 14.1 / 13.4; N = 8192:
+// 7-11% slower at every M.  With M <= 8 it is 9-25% slower everywhere (the
+// streaming form keeps more loads in flight per compute unit); with fewer
+// waves too (K = 4096, M = 64, N = 16384: 12.50 / 12.85).
 static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
-  if (kw < 10) return false;
+  if (kw < 10 || M < 16) return false;
   if (M > 48) return Ns >= 3 * cus;
-  return M >= 16 && Ns >= 8 * cus;
+  if (M > 32) return Ns >= 6 * cus;
+  return Ns >= 8 * cus;
 }
 
 template <int MT, int MAXW>
@@ -521,10 +524,14 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   // persistent form: one group per wave, bf16 / fp32 output from the GEMM
   // layout (path 7 of the test hook forces it where it applies, 8 keeps the
   // form above)
-  const bool persist_ok = gpw == 1 && kw <= 12 && !p.out_fp4 && !p.a_rowmajor;
+  // (one group per wave there: the same K split as above wherever that has
+  // one group per wave too, so the same bits; two or three row tiles above
+  // 4096 of K split K in two groups per wave above, so their sums differ in
+  // order)
+  const bool persist_ok = p.G <= 12 && !p.out_fp4 && !p.a_rowmajor;
   const int ov = get_gemm_path_override();
-  const bool persist = persist_ok && (ov == 7 || (ov != 8 && decode_persist_pays(p.M, p.Ns, p.cus, kw)));
-  if (persist) return launch_decode_persist<MT, 12>(p, kw, stream);
+  const bool persist = persist_ok && (ov == 7 || (ov != 8 && decode_persist_pays(p.M, p.Ns, p.cus, p.G)));
+  if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
   const bool one_strip = p.Ns >= 1024 && p.M <= 8 && !p.out_fp4;  // MXFP4 output: 32 columns per workgroup
   if constexpr (MT == 1) {
     if (gpw >= 2)
