@@ -430,6 +430,11 @@ def prefill_pass(M=PREFILL_PASS_M):
     print(json.dumps({"prefill_pass": plan}), flush=True)
 
 
+def _is_decode_gemm(kernel_name):
+    """The decode GEMM's kernels: the streaming form and the persistent one."""
+    return "gemm_decode_kernel" in kernel_name or "gemm_decode_persist_kernel" in kernel_name
+
+
 def _counter_rows(csv_path):
     import csv
     rows = []
@@ -447,7 +452,7 @@ def traffic_summary(fetch_csv, write_csv, command):
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in _counter_rows(path) if r[2] == name]
         calib = [v for _, k, _, v in rows if "bitwise_not" in k]
-        gemm = [v for _, k, _, v in rows if "gemm_decode_kernel" in k]
+        gemm = [v for _, k, _, v in rows if _is_decode_gemm(k)]
         per[name] = (calib, gemm)
     f_cal, f_gemm = per["FETCH_SIZE"]
     w_cal, w_gemm = per["WRITE_SIZE"]
@@ -468,7 +473,7 @@ def traffic_summary(fetch_csv, write_csv, command):
                                ratio=round(tr / alg, 4)))
     assert i == len(f_gemm) == len(w_gemm), (i, len(f_gemm), len(w_gemm))
     traffic = float(np.mean([r["hbm_bytes"] for r in shapes]))
-    summary = dict(kernel="gemm_decode_kernel", traffic_bytes_per_launch=round(traffic),
+    summary = dict(kernel="gemm_decode_kernel / gemm_decode_persist_kernel", traffic_bytes_per_launch=round(traffic),
                    algorithmic_bytes_per_launch=round(float(np.mean([r["algorithmic_bytes"] for r in shapes]))),
                    fetch_scale=round(ff, 4), write_scale=round(wf, 4),
                    calibration=f"int32 bitwise_not (torch elementwise kernel) over {CALIB_BYTES} bytes: FETCH_SIZE "
@@ -482,7 +487,9 @@ def traffic_summary(fetch_csv, write_csv, command):
              "bytes read and written), then averaged per shape over its launches;",
              "`traffic_bytes_per_launch` is the mean over the 9 shapes, as `achieved`",
              "in the benchmark's roofline.  bench.py reports it only while",
-             "`source_sha256` matches the decode kernel's sources.", "",
+             "`source_sha256` matches the decode kernel's sources.  The decode GEMM is",
+             "`gemm_decode_kernel`, or its persistent form `gemm_decode_persist_kernel` where",
+             "that is chosen (at these shapes: M = 16, N = 34816).", "",
              "| M | N | K | launches | FETCH KiB | WRITE KiB | HBM bytes | algorithmic | ratio |",
              "|---|---|---|---|---|---|---|---|---|"]
     for r in shapes:
@@ -515,7 +522,7 @@ def trace_summary(stats_csv, trace_csv, marker_csv, bench_log, command):
         label = next(v for v in mk.values() if isinstance(v, str) and v.startswith("roofline"))
         t0, t1 = int(mk["Start_Timestamp"]), int(mk["End_Timestamp"])
         d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-             if "gemm_decode_kernel" in r["Kernel_Name"] and t0 <= int(r["Start_Timestamp"]) <= t1]
+             if _is_decode_gemm(r["Kernel_Name"]) and t0 <= int(r["Start_Timestamp"]) <= t1]
         if d:
             per_shape.append((label, len(d), float(np.mean(d))))
     trace_us = float(np.mean([a for _, _, a in per_shape])) / 1e3 if per_shape else float("nan")
@@ -533,7 +540,8 @@ def trace_summary(stats_csv, trace_csv, marker_csv, bench_log, command):
                      f"{int(float(r['AverageNs']))} | {float(r['Percentage']):.2f} | {r['MinNs']} | "
                      f"{r['MaxNs']} |")
     lines += ["", "## Roofline kernel: the decode GEMM at the 9 headline shapes", "",
-              "Launches of `gemm_decode_kernel` inside the run's `roofline M=.. N=.. K=..` marker",
+              "Launches of the decode GEMM (`gemm_decode_kernel`, or `gemm_decode_persist_kernel`",
+              "where that form is chosen) inside the run's `roofline M=.. N=.. K=..` marker",
               "ranges (kernel duration from the trace), averaged per shape, then over the shapes",
               "-- the same averaging as the benchmark's `roofline.launch_us`, which times the",
               "same graph replays with HIP events (dispatch gaps included).", "",
@@ -1092,7 +1100,8 @@ def main():
                                "value": round(step_bytes / step_s_single / 1e9, 1)},
         "sclk": {"headline": clk_head.summary(), "roofline": clk_roof.summary()},
         "roofline": {
-            "kernel": "gemm_decode_kernel (W4A4 GEMM, M<=16, mean over the 9 headline shapes)",
+            "kernel": "decode W4A4 GEMM (gemm_decode_kernel; gemm_decode_persist_kernel at M=16, N=34816), "
+                      "M<=16, mean over the 9 headline shapes",
             "bound": "hbm",
             "achieved": round(achieved / 1e9, 1),
             "peak": PEAK_HBM / 1e9,
