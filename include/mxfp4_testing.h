@@ -25,8 +25,9 @@ extern "C" {
  * tiles leave a round of compute units part-empty and a tile has more than
  * 512 of K; 5 and 6 = as 3 and 4 with 128-wide tiles; 7 and 8 = the
  * small-M kernel (M <= 64) in its persistent form wherever that form
- * applies (one scale group per wave, bf16 or fp32 output from GEMM-layout
- * activations), and in its one-workgroup-per-strip form only.
+ * applies (one scale group per wave, bf16 or fp32 output, activations in
+ * the GEMM layout or row-major), and in its one-workgroup-per-strip form
+ * only.
  * Returns MXFP4_OK, or MXFP4_ERR_ARG for other values.
  */
 int mxfp4_testing_set_gemm_path(int path);

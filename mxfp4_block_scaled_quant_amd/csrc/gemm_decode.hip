@@ -264,26 +264,31 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
 // all M activation rows of its K-run, bytes that grow with M while the
 // weights do not): one workgroup per compute unit walks the strips
 // s = blockIdx.x + k * gridDim.x, one scale group (4 K-steps) per wave; a
-// wave loads its group's activation operands and scales once, and they stay
-// in registers; the weights of the next D strips are in flight in a ring of
+// wave loads its group's activation operands and scales once (from either
+// activation layout, AROW as above), and they stay in registers; the weights of the next D strips are in flight in a ring of
 // registers while the current strip's MFMAs and reduction run.  Per strip a
 // wave's partial tile is the one gemm_decode_kernel forms with one group per
 // wave, and reduce_store sums them in the same order: bitwise the same
 // output.  The reduction areas alternate between strips, so the one barrier
 // inside reduce_store also orders a strip's LDS reads before the writes two
 // strips later.
-template <int MT, int MAXW, int D>
+template <int MT, int MAXW, int D, bool AROW>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
   extern __shared__ v4f red[];
   constexpr size_t kRedFloats = reduce_lds_bytes<MT, 1, MAXW>() / sizeof(float);
   const int lane = threadIdx.x & 63;
   const int g = threadIdx.x >> 6;  // this wave's scale group
   const bool gv = g < p.G;
-  const auto ra = make_rsrc(p.a, (uint32_t)MT * p.Kt * 1024u);
+  const int nblk = p.K >> 5;
+  const auto ra = make_rsrc(p.a, AROW ? (uint32_t)(p.M - 1) * p.lda + (uint32_t)(p.K >> 1)
+                                      : (uint32_t)MT * p.Kt * 1024u);
   const auto rw = make_rsrc(p.w, (uint32_t)p.Ns * p.Kt * 1024u);
-  const auto ras = make_rsrc(p.as, (uint32_t)MT * p.G * 256u);
+  const auto ras = make_rsrc(p.as, AROW ? (uint32_t)(p.M - 1) * p.lds + (uint32_t)nblk
+                                        : (uint32_t)MT * p.G * 256u);
   const auto rws = make_rsrc(p.ws, (uint32_t)p.Ns * p.G * 256u);
 
+  // This wave's activation operands and scales, as gemm_decode_kernel reads
+  // them (from the GEMM layout, or gathered from the row-major form).
   int4 af[4][MT];
   uint32_t sa[MT];
 #pragma unroll
@@ -294,11 +299,40 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
     for (int i = 0; i < MT; ++i) {
       // rows past M are zero padding: skip their bytes
       const int row = i * 16 + (lane & 15);
-      af[u][i] = buf_load16(ra, (tv && row < p.M) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+      const bool rv = row < p.M;
+      if constexpr (AROW) {
+        const bool cv = t * 4 + (lane >> 4) < nblk;
+        af[u][i] = buf_load16(ra, (tv && rv && cv) ? (uint32_t)row * p.lda + (uint32_t)(t * 64 + (lane >> 4) * 16)
+                                                     : kOOB);
+      } else {
+        af[u][i] = buf_load16(ra, (tv && rv) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+      }
     }
   }
 #pragma unroll
-  for (int i = 0; i < MT; ++i) sa[i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+  for (int i = 0; i < MT; ++i) {
+    if constexpr (AROW) {
+      const int row = i * 16 + (lane & 15);
+      const bool ok = gv && row < p.M;
+      uint32_t word = 0;
+      if (p.scales_vec) {
+        const int4 v = buf_load16(ras, ok ? (uint32_t)row * p.lds + (uint32_t)(g * 16) : kOOB);
+        const uint32_t sh = (uint32_t)(lane >> 4) * 8u;
+        word = ((uint32_t)v.x >> sh & 0xFFu) | ((uint32_t)v.y >> sh & 0xFFu) << 8 |
+               ((uint32_t)v.z >> sh & 0xFFu) << 16 | ((uint32_t)v.w >> sh & 0xFFu) << 24;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = (g * 4 + j) * 4 + (lane >> 4);
+          const uint32_t off = (ok && c < nblk) ? (uint32_t)row * p.lds + (uint32_t)c : kOOB;
+          word |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, off, 0, 0) << (8 * j);
+        }
+      }
+      sa[i] = word;
+    } else {
+      sa[i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+    }
+  }
 
   const int nk = (int)blockIdx.x < p.Ns ? (p.Ns - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   int4 bf[D][4];
@@ -506,13 +540,31 @@ static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
   return Ns >= 8 * cus;
 }
 
+// Row-major (prequantised) activations: every workgroup of the streaming form
+// gathers its rows' 16-byte pieces afresh, so loading them once per wave pays
+// sooner than from the GEMM layout.  Measured as above (us, streaming /
+// persistent), K = 5120: N = 24576 (6 strips per CU): M = 1 14.5 / 13.4,
+// M = 16 14.7 / 14.0, M = 64 31.2 / 21.4; N = 34816: M = 32 28.9 / 20.8,
+// M = 64 48.7 / 27.5; N = 14336 (3.5 per CU): M = 1 8.4 / 10.0, M = 32
+// 12.9 / 12.6, M = 33 16.8 / 13.8, M = 64 20.6 / 17.0; N = 8192 (two per
+// CU): M = 64 11.5 / 12.6.
+static bool decode_persist_pays_rowmajor(int M, int Ns, int cus, int kw) {
+  if (kw < 10) return false;
+  if (M > 32) return Ns >= 3 * cus;
+  return Ns >= 6 * cus;
+}
+
 template <int MT, int MAXW>
 static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t stream) {
   // strips in flight per wave, as registers allow at 12 waves (six at one
   // row tile measured no faster than four)
   constexpr int D = MT == 4 ? 3 : 4;
   const int grid = p.Ns < p.cus ? p.Ns : p.cus;
-  gemm_decode_persist_kernel<MT, MAXW, D><<<grid, 64 * kw, 2 * reduce_lds_bytes<MT, 1, MAXW>(), stream>>>(p);
+  const size_t lds = 2 * reduce_lds_bytes<MT, 1, MAXW>();
+  if (p.a_rowmajor)
+    gemm_decode_persist_kernel<MT, MAXW, D, true><<<grid, 64 * kw, lds, stream>>>(p);
+  else
+    gemm_decode_persist_kernel<MT, MAXW, D, false><<<grid, 64 * kw, lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -528,9 +580,11 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   // one group per wave too, so the same bits; two or three row tiles above
   // 4096 of K split K in two groups per wave above, so their sums differ in
   // order)
-  const bool persist_ok = p.G <= 12 && !p.out_fp4 && !p.a_rowmajor;
+  const bool persist_ok = p.G <= 12 && !p.out_fp4;
   const int ov = get_gemm_path_override();
-  const bool persist = persist_ok && (ov == 7 || (ov != 8 && decode_persist_pays(p.M, p.Ns, p.cus, p.G)));
+  const bool persist =
+      persist_ok && (ov == 7 || (ov != 8 && (p.a_rowmajor ? decode_persist_pays_rowmajor(p.M, p.Ns, p.cus, p.G)
+                                                          : decode_persist_pays(p.M, p.Ns, p.cus, p.G))));
   if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
   const bool one_strip = p.Ns >= 1024 && p.M <= 8 && !p.out_fp4;  // MXFP4 output: 32 columns per workgroup
   if constexpr (MT == 1) {

@@ -6,8 +6,8 @@ producer arrive as row-major packed FP4 + row-major E8M0 scales.
 * mxfp4_linear_prequantized: the oracle's GEMM tolerance, and bitwise the
   result of mxfp4_gemm_a4w4 on the same values in the GEMM layouts through
   the same kernel (small-M kernel reading the row-major operands directly
-  for M <= 64; permutation into the workspace, then the tiled kernel,
-  above)."""
+  for M <= 64, in either of its forms; permutation into the workspace, then
+  the tiled kernel, above)."""
 
 import numpy as np
 import pytest
@@ -80,3 +80,53 @@ def test_linear_prequantized(name, M, N, K, kw, pads):
     assert np.array_equal(y32n.view(np.uint32), r32n.view(np.uint32))
     assert torch.equal(y16.cpu().view(torch.int16), r16.cpu().view(torch.int16))
     _check(prob, y32n, y16.cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+PERSIST = [
+    # name, M, N, K, (ldq pad, lds pad)
+    ("m1_1040x4128", 1, 1040, 4128, (0, 0)),                  # ragged K tile, byte scale loads
+    ("m5_300x640_pad", 5, 300, 640, (16, 1)),
+    ("m16_5000x5120", 16, 5000, 5120, (0, 0)),                # 16-byte scale loads
+    ("m33_520x1056_pad", 33, 520, 1056, (32, 3)),
+    ("m48_4200x4096", 48, 4200, 4096, (16, 16)),
+    ("m64_2064x6144", 64, 2064, 6144, (0, 0)),
+    ("m16_24576x5120", 16, 24576, 5120, (0, 0)),              # chosen by default (six strips per CU)
+    ("m40_12288x5120_pad", 40, 12288, 5120, (16, 16)),        # chosen by default (three per CU)
+]
+
+
+@pytest.mark.parametrize("name,M,N,K,pads", PERSIST, ids=[c[0] for c in PERSIST])
+def test_linear_prequantized_persistent_form(name, M, N, K, pads):
+    # The small-M kernel's persistent form reading the row-major operands:
+    # bitwise what the same form computes from the GEMM layouts, and bitwise
+    # the one-workgroup-per-strip form where both split K the same way; the
+    # default choice is bitwise one of the two forms; the oracle bar on
+    # sampled columns at the wide shapes.
+    need_gpu()
+    from tests.test_gpu_gemm import _same_k_split, _sample
+    prob = inputs.linear_problem(M, N, K, 21, outliers=True, with_bias=True)
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    q_rm, s_rm = Q.quant_1x32(prob["x"])
+    xq, xs = _strided_u8(q_rm, pads[0]), _strided_u8(s_rm, pads[1])
+    b = dev_bf16(prob["bias"])
+    q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
+    res = {}
+    try:
+        for path in (0, 7, 8):
+            mx.set_gemm_path(path)
+            res[path] = (mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.float32),
+                         mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.bfloat16))
+        mx.set_gemm_path(7)
+        r32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
+    finally:
+        mx.set_gemm_path(0)
+    torch.cuda.synchronize()
+    y32 = res[7][0].cpu().numpy()
+    assert np.array_equal(y32.view(np.uint32), r32.cpu().numpy().view(np.uint32))
+    if _same_k_split(M, K):
+        assert np.array_equal(y32.view(np.uint32), res[8][0].cpu().numpy().view(np.uint32))
+        assert torch.equal(res[7][1].cpu().view(torch.int16), res[8][1].cpu().view(torch.int16))
+    d32 = res[0][0].cpu().numpy().view(np.uint32)
+    assert any(np.array_equal(d32, res[f][0].cpu().numpy().view(np.uint32)) for f in (7, 8))
+    _check(prob, y32, res[7][1].cpu().view(torch.int16).numpy().view(np.uint16),
+           cols=_sample(N, 96, N) if N > 4096 else None)
