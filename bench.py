@@ -16,8 +16,9 @@ Headline (the metric's M <= 16 decode regime): one step is one pass over the
 decode sweep W4A4 MXFP4 linear at M in {1, 4, 16} x (N, K) in {(14336, 5120),
 (5120, 14336), (34816, 5120)} -- for each shape, mxfp4_linear: per-1x32
 quantisation of the bf16 activations and the block-scaled FP4 GEMM with a
-bf16 bias and bf16 output (M <= 4: one launch, the quantisation fused into
-the GEMM kernel; M = 16: quantisation into a workspace, then the GEMM),
+bf16 bias and bf16 output (one launch with the quantisation fused into the
+GEMM kernel at M = 1, and at M = 4 for N = 14336 and N = 34816; elsewhere
+quantisation into a workspace, then the GEMM),
 against weights quantised and preshuffled once at load time.  value = sum of the pipeline's algorithmic
 bytes over the step / step time (GB/s).  Inputs are resident in HBM before the
 timed region.  Each launch reads a different copy of its weights (>= 1 GiB of
@@ -1090,8 +1091,8 @@ def main():
             "workload": "decode-sweep W4A4 MXFP4 linear at M<=16: per-1x32 quant of bf16 "
                         "activations + block-scaled FP4 GEMM + bf16 bias, bf16 out",
             "M": HEADLINE_M, "NK": DECODE_NK,
-            "step": "9 shapes x mxfp4_linear (M=1, and M=4 at N=14336: quant fused into the "
-                    "GEMM; else quant then GEMM), weights preshuffled at load, rotated copies",
+            "step": "9 shapes x mxfp4_linear (M=1, and M=4 at N=14336 and N=34816: quant fused "
+                    "into the GEMM; else quant then GEMM), weights preshuffled at load, rotated copies",
             "hbm_frac": round(value_gbs * 1e9 / PEAK_HBM, 4),
         },
         "step_spread_us": dict(_us(dict(step_stats, mean=step_s)), steps_per_sample=chunk),

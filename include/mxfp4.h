@@ -190,17 +190,20 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales,
  * the FP4 GEMM, bias added after).  Same result as mxfp4_quant_1x32 (GEMM
  * layout) followed by mxfp4_gemm_a4w4:
  *   out[m, n] = round(sum_k dq(Q(x))[m,k] dq(W)[n,k] + bias[n]).
- * Where it is faster (M = 1; M <= 4 for N < 16384 and K <= 8192) the
- * quantisation runs inside the GEMM kernel: one launch, no quantised copy of
- * x, bitwise the same output as the two-call form.  Otherwise x is quantised
- * into `workspace` and the GEMM kernel for that M then reads it.
+ * Where it is faster (M = 1; M <= 4 for N < 16384 and K <= 8192; 2 <= M
+ * <= 4 with 4608 < K <= 6144 and at least six 16-column weight strips per
+ * compute unit) the quantisation runs inside the GEMM kernel: one launch, no
+ * quantised copy of x, bitwise the same output as the two-call form.
+ * Otherwise x is quantised into `workspace` and the GEMM kernel for that M
+ * then reads it.
  *
  *   x       bf16 [M, K], row stride ldx ELEMENTS (ldx >= K, ldx % 8 == 0,
  *           16-byte aligned); for M <= 4, ((M-1)*ldx + K)*2 < 2^31
  *   w_pre, ws_pre, bias, out, ldo, out_dtype: as for mxfp4_gemm_a4w4
  *   workspace  mxfp4_linear_workspace_bytes(M, N, K) bytes (0 when the
- *           quantisation is fused: then it may be NULL), 16-byte aligned;
- *           overwritten, caller-owned
+ *           quantisation is fused: then it may be NULL; the last fused case
+ *           above, which depends on the device, still asks for it and leaves
+ *           it untouched), 16-byte aligned; overwritten, caller-owned
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
  */
 size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -118,6 +118,14 @@ int linear_run(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre
   p.Kt = (int)cdiv(K, 128);
   p.G = (int)cdiv(p.Kt, 4);
   p.Ns = (int)cdiv(N, 16);
+  const int64_t x_bytes = ((M - 1) * ldx + K) * 2;
+  if (linear_persist_applies((int)M, (int)K, x_bytes) && linear_persist_pays((int)M, (int)N, (int)K, cus)) {
+    // quantised inside the persistent form: the workspace stays untouched
+    p.x = (const uint16_t*)x;
+    p.ldx = (int)ldx;
+    p.x_bytes = (uint32_t)x_bytes;
+    return launched(launch_linear_persist(p, s));
+  }
   if (linear_fused(M, N, K)) {
     p.x = (const uint16_t*)x;
     p.ldx = (int)ldx;

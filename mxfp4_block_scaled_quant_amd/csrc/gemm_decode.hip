@@ -272,8 +272,15 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
 // output.  The reduction areas alternate between strips, so the one barrier
 // inside reduce_store also orders a strip's LDS reads before the writes two
 // strips later.
-template <int MT, int MAXW, int D, bool AROW>
+// Where the persistent form takes its activations from.
+constexpr int kASrcGemm = 0;  // quantised, GEMM layouts
+constexpr int kASrcRow = 1;   // quantised, row-major (AROW above)
+constexpr int kASrcBf16 = 2;  // bf16 rows, quantised here (one row tile)
+
+template <int MT, int MAXW, int D, int ASRC>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
+  constexpr bool AROW = ASRC == kASrcRow;
+  static_assert(ASRC != kASrcBf16 || MT == 1, "bf16 activations: one row tile");
   extern __shared__ v4f red[];
   constexpr size_t kRedFloats = reduce_lds_bytes<MT, 1, MAXW>() / sizeof(float);
   const int lane = threadIdx.x & 63;
@@ -288,11 +295,27 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
   const auto rws = make_rsrc(p.ws, (uint32_t)p.Ns * p.G * 256u);
 
   // This wave's activation operands and scales, as gemm_decode_kernel reads
-  // them (from the GEMM layout, or gathered from the row-major form).
+  // them (from the GEMM layout, or gathered from the row-major form); from
+  // bf16 rows, each lane loads the whole 1x32 block its operand of K-step u
+  // holds (row lane % 16, block (4g + u) * 4 + lane / 16: 64 bytes) and
+  // encodes it below, once the weight ring is in flight.
   int4 af[4][MT];
   uint32_t sa[MT];
+  int4 xv[ASRC == kASrcBf16 ? 4 : 1][4];
+  if constexpr (ASRC == kASrcBf16) {
+    const auto rx = make_rsrc(p.x, p.x_bytes);
+    const int row = lane & 15;
+    const bool rv = gv && row < p.M;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u) {
+      const int kb = (g * 4 + u) * 4 + (lane >> 4);
+      const uint32_t off = (uint32_t)row * (uint32_t)p.ldx * 2u + (uint32_t)kb * 64u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[u][c] = buf_load16(rx, (rv && kb < nblk) ? off + (uint32_t)c * 16u : kOOB);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4 && ASRC != kASrcBf16; ++u) {
     const int t = g * 4 + u;
     const bool tv = gv && t < p.Kt;
 #pragma unroll
@@ -310,7 +333,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
     }
   }
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+  for (int i = 0; i < MT && ASRC != kASrcBf16; ++i) {
     if constexpr (AROW) {
       const int row = i * 16 + (lane & 15);
       const bool ok = gv && row < p.M;
@@ -352,6 +375,17 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, bf[d], sb[d]);
+  if constexpr (ASRC == kASrcBf16) {
+    // the encoding waits for x only: the ring's loads stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    sa[0] = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t b;
+      af[u][0] = quant_block32(xv[u], b);
+      sa[0] |= b << (8 * u);
+    }
+  }
 
   for (int k0 = 0; k0 < nk; k0 += D) {
 #pragma unroll
@@ -562,9 +596,9 @@ static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t s
   const int grid = p.Ns < p.cus ? p.Ns : p.cus;
   const size_t lds = 2 * reduce_lds_bytes<MT, 1, MAXW>();
   if (p.a_rowmajor)
-    gemm_decode_persist_kernel<MT, MAXW, D, true><<<grid, 64 * kw, lds, stream>>>(p);
+    gemm_decode_persist_kernel<MT, MAXW, D, kASrcRow><<<grid, 64 * kw, lds, stream>>>(p);
   else
-    gemm_decode_persist_kernel<MT, MAXW, D, false><<<grid, 64 * kw, lds, stream>>>(p);
+    gemm_decode_persist_kernel<MT, MAXW, D, kASrcGemm><<<grid, 64 * kw, lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -638,4 +672,39 @@ hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
   const int kw = (p.G + gpw - 1) / gpw;
   return launch_linear_t<1, 2>(p, kw, gpw, stream);
 }
+// Fused quantisation in the persistent form (M <= 16, at most 12 scale
+// groups): each wave encodes its group's blocks of the 16 rows once.  The
+// same operands, K split and order as quantisation + the persistent GEMM,
+// so the same bits.
+bool linear_persist_applies(int M, int K, int64_t x_bytes) {
+  const int G = (K / 32 + 15) / 16;
+  return M >= 1 && M <= 16 && G <= 12 && x_bytes <= (int64_t)0x7FFFFFFF;  // 31-bit buffer offsets
+}
+
+// Every workgroup encodes the bf16 rows itself (4x the bytes of their FP4
+// form through each compute unit's L2 path before the first MFMA), so the
+// fusion beats quantisation + GEMM only while the rows are few and the
+// weight strips many.  Measured on MI355X (us, default two launches /
+// fused persistent; rotated weight copies, bf16 out), K = 5120: N = 24576
+// (6 strips per CU): M = 2 15.0 / 14.0, M = 4 15.0 / 14.3, M = 8 15.1 /
+// 15.2, M = 16 15.3 / 17.0; N = 34816: M = 2 18.6 / 18.3, M = 4 18.9 /
+// 18.7, M = 16 20.2 / 21.3; N = 14336 and 16384 (K = 6144): 5-22% slower
+// at every M; M = 1 stays with the streaming fused kernel (N = 34816: 16.4
+// against 18.2).
+bool linear_persist_pays(int M, int N, int K, int cus) {
+  const int ov = get_gemm_path_override();
+  if (ov == 7) return true;
+  if (ov == 8) return false;
+  const int Ns = (N + 15) / 16;
+  const int G = (K / 32 + 15) / 16;
+  return M >= 2 && M <= 4 && G >= 10 && Ns >= 6 * cus;
+}
+
+hipError_t launch_linear_persist(const GemmArgs& p, hipStream_t stream) {
+  if (p.M > 16 || p.G > 12) return hipErrorInvalidValue;
+  const int grid = p.Ns < p.cus ? p.Ns : p.cus;
+  gemm_decode_persist_kernel<1, 12, 4, kASrcBf16><<<grid, 64 * p.G, 2 * reduce_lds_bytes<1, 1, 12>(), stream>>>(p);
+  return hipGetLastError();
+}
+
 }  // namespace mxfp4

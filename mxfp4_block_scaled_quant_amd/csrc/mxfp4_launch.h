@@ -66,6 +66,12 @@ size_t gemm_prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // that beats quantisation + GEMM for a shape.
 hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream);
 bool linear_fused_pays(int M, int N, int K);
+// The fused quantisation in the small-M kernel's persistent form: whether the
+// shape fits it (x_bytes = ((M-1)*ldx + K)*2), whether it is chosen, and
+// its launch (p.x / ldx / x_bytes set).
+bool linear_persist_applies(int M, int K, int64_t x_bytes);
+bool linear_persist_pays(int M, int N, int K, int cus);
+hipError_t launch_linear_persist(const GemmArgs& p, hipStream_t stream);
 
 hipError_t launch_quant_1x32(const void* x, int64_t M, int64_t K, int64_t ldx, void* q,
                              int64_t ldq, void* scales, int layout, hipStream_t stream);
