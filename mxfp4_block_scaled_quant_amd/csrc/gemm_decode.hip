@@ -48,8 +48,28 @@ __device__ __forceinline__ v4f mfma_sel(const int4& a, const int4& b, uint32_t s
 // Measured on MI355X against per-output loops over the waves (one LDS round
 // trip per wave, 4-way bank conflicts): M = 64 decode shapes 8-12% faster,
 // M <= 16 within 1%.
+// The bias of a thread's output columns in reduce_store / reduce_store_fp4
+// (column (s0 + j) * 16 + lane % 16 of strip j) as raw bf16 bits, 0 past N
+// or without a bias: loaded with the weights, so the reduction does not
+// wait a memory round trip for them (measured on MI355X: +0.65 us per
+// launch at N = 34816 with the load in the reduction, against the same
+// launch without bias).  A buffer load, so that no branch guards it (a
+// guarded load gets its wait at the end of the branch, before the weight
+// loads are even issued).
+template <int NS>
+__device__ __forceinline__ void load_bias(const GemmArgs& p, int s0, uint32_t (&bb)[NS]) {
+  const int lane = threadIdx.x & 63;
+  const auto rb = make_rsrc(p.bias, p.bias ? (uint32_t)p.N * 2u : 0u);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const uint32_t n = (uint32_t)((s0 + j) * 16 + (lane & 15));
+    bb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, n < (uint32_t)p.N ? n * 2u : kOOB, 0, 0);
+  }
+}
+
 template <int MT, int NS, int MAXW>
-__device__ __forceinline__ void reduce_store(float* red, const v4f (&acc)[MT][NS], const GemmArgs& p, int s0) {
+__device__ __forceinline__ void reduce_store(float* red, const v4f (&acc)[MT][NS], const GemmArgs& p, int s0,
+                                             const uint32_t (&bb)[NS]) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int KW = blockDim.x >> 6;
@@ -74,7 +94,7 @@ __device__ __forceinline__ void reduce_store(float* red, const v4f (&acc)[MT][NS
     for (int w = 1; w < MAXW; ++w)
       if (w < KW) v += part[w];
     if (m < p.M && n < p.N) {
-      if (p.bias) v += bf16_to_f32(p.bias[n]);
+      if (p.bias) v += bf16_to_f32((uint16_t)bb[j]);
       if (p.out_f32)
         reinterpret_cast<float*>(p.out)[(int64_t)m * p.ldo + n] = v;
       else
@@ -89,11 +109,20 @@ constexpr size_t reduce_lds_bytes() {
   return (size_t)MT * NS * 4 * MAXW * 64 * sizeof(float);
 }
 
-// AROW: the activations come row-major as a producer hands them over
+// Where the activations come from.  Row-major: as a producer hands them over
 // (packed FP4 [M, K/2], row stride lda bytes; scales [M, K/32], row stride
-// lds bytes) and are gathered into the same MFMA operands: lane l's 16 bytes
-// of row r, block kb are one contiguous piece of the row, and its scale
-// dword is assembled from the 4 K-steps' bytes.  Same values, same MFMAs.
+// lds bytes), gathered into the same MFMA operands: lane l's 16 bytes of row
+// r, block kb are one contiguous piece of the row, and its scale dword is
+// assembled from the 4 K-steps' bytes (one 16-byte load of the group's
+// scales when the rows allow it, else four byte loads).  Same values, same
+// MFMAs.  The scale-load form is a template choice, not a branch: a load
+// inside a branch gets its wait at the branch's end, which held every load
+// issued before it (the weights) up before the activations were even
+// requested (measured: 2-3 us per launch at N = 34816).
+constexpr int kASrcGemm = 0;   // quantised, GEMM layouts
+constexpr int kASrcRow16 = 1;  // quantised, row-major; 16-byte scale loads
+constexpr int kASrcRow8 = 2;   // quantised, row-major; byte scale loads
+constexpr int kASrcBf16 = 3;   // bf16 rows, quantised in the kernel (persistent form, one row tile)
 // MXFP4 output (two strips = 32 columns per workgroup, one 1x32 block per
 // row): the summed rows are rounded to bf16 into an LDS staging area, then
 // 4 threads per row each take 8 of the block's values, combine the block's
@@ -101,7 +130,8 @@ constexpr size_t reduce_lds_bytes() {
 // amax's exponent, scaled conversion): 4 code bytes per thread, the scale
 // byte from the first.  Bitwise the bf16 output quantised afterwards.
 template <int MT>
-__device__ __forceinline__ void reduce_store_fp4(v4f* red, const v4f (&acc)[MT][2], const GemmArgs& p, int s0) {
+__device__ __forceinline__ void reduce_store_fp4(v4f* red, const v4f (&acc)[MT][2], const GemmArgs& p, int s0,
+                                                 const uint32_t (&bb)[2]) {
   constexpr int NS = 2;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -122,7 +152,7 @@ __device__ __forceinline__ void reduce_store_fp4(v4f* red, const v4f (&acc)[MT][
     for (int w = 0; w < KW; ++w) v += red[(w * MT * NS + tile) * 64 + l][reg];
     const int m = i * 16 + 4 * (l >> 4) + reg;
     const int n = (s0 + j) * 16 + (l & 15);
-    if (p.bias && n < p.N) v += bf16_to_f32(p.bias[n]);
+    if (p.bias && n < p.N) v += bf16_to_f32((uint16_t)bb[j]);
     stg[m * 32 + j * 16 + (l & 15)] = f32_to_bf16_rne(v);
   }
   __syncthreads();
@@ -138,8 +168,10 @@ __device__ __forceinline__ void reduce_store_fp4(v4f* red, const v4f (&acc)[MT][
   }
 }
 
-template <int MT, int NS, int GPR, int MAXW, bool AROW>
+template <int MT, int NS, int GPR, int MAXW, int ASRC>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int gpw) {
+  constexpr bool AROW = ASRC == kASrcRow16 || ASRC == kASrcRow8;
+  static_assert(ASRC != kASrcBf16, "bf16 activations: the persistent form only");
   extern __shared__ v4f red[];  // reduce_store's partials (or reduce_store_fp4's)
   constexpr int STEPS = 4 * GPR;
   const int lane = threadIdx.x & 63;
@@ -159,6 +191,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  uint32_t bb[NS];
 
   const int g_begin = wv * gpw;
   const int g_end = min(g_begin + gpw, p.G);
@@ -191,7 +224,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
           const int row = i * 16 + (lane & 15);
           const bool ok = gv && row < p.M;
           uint32_t word = 0;
-          if (p.scales_vec) {
+          if constexpr (ASRC == kASrcRow16) {
             // the group's 16 scale bytes of the row in one load (whole
             // groups: K % 512 == 0); this lane's block kb is byte kb of
             // each dword
@@ -213,6 +246,17 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         }
       }
     }
+    if constexpr (AROW && GPR == 1) {
+      // Row-major rows are a few KiB that every workgroup reads piece by
+      // piece; requested alongside the weights they slowed the stream
+      // (N = 14336, K = 5120, M = 1 / 4 / 16: 9.13 / 9.33 / 10.72 us),
+      // requested once the weights and scales are in they do not (8.47 /
+      // 8.67 / 9.93).  With two groups per round the concurrent form is the
+      // faster (K = 14336, N = 5120, M = 1: 9.58 against 9.75).
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
       const int t = gr * 4 + u;
@@ -231,6 +275,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         }
       }
     }
+    // the bias after the operands (every round: no branch), so that the
+    // MFMAs' waits do not include it; row-major operands leave no registers
+    // for it (two strips and two groups per round spill), so there it is
+    // loaded after the loop
+    if constexpr (!AROW) load_bias<NS>(p, s0, bb);
     // Keep every load of the round ahead of the first wait: without this the
     // scheduler interleaves loads and MFMAs to save registers, which turns one
     // memory round trip into several.
@@ -251,35 +300,33 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         }
   }
 
+  if constexpr (AROW) load_bias<NS>(p, s0, bb);
   if constexpr (NS == 2) {
     if (p.out_fp4) {
-      reduce_store_fp4<MT>(red, acc, p, s0);
+      reduce_store_fp4<MT>(red, acc, p, s0, bb);
       return;
     }
   }
-  reduce_store<MT, NS, MAXW>(reinterpret_cast<float*>(red), acc, p, s0);
+  reduce_store<MT, NS, MAXW>(reinterpret_cast<float*>(red), acc, p, s0, bb);
 }
 
 // Persistent form, for more rows (each workgroup of the form above re-reads
 // all M activation rows of its K-run, bytes that grow with M while the
 // weights do not): one workgroup per compute unit walks the strips
 // s = blockIdx.x + k * gridDim.x, one scale group (4 K-steps) per wave; a
-// wave loads its group's activation operands and scales once (from either
-// activation layout, AROW as above), and they stay in registers; the weights of the next D strips are in flight in a ring of
-// registers while the current strip's MFMAs and reduction run.  Per strip a
+// wave loads its group's activation operands and scales once (from any of
+// the sources above; bf16 rows are encoded here), and they stay in
+// registers; the weights of the next D strips (with their scales and the
+// bias of their columns) are in flight in a ring of registers while the
+// current strip's MFMAs and reduction run.  Per strip a
 // wave's partial tile is the one gemm_decode_kernel forms with one group per
 // wave, and reduce_store sums them in the same order: bitwise the same
 // output.  The reduction areas alternate between strips, so the one barrier
 // inside reduce_store also orders a strip's LDS reads before the writes two
 // strips later.
-// Where the persistent form takes its activations from.
-constexpr int kASrcGemm = 0;  // quantised, GEMM layouts
-constexpr int kASrcRow = 1;   // quantised, row-major (AROW above)
-constexpr int kASrcBf16 = 2;  // bf16 rows, quantised here (one row tile)
-
 template <int MT, int MAXW, int D, int ASRC>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
-  constexpr bool AROW = ASRC == kASrcRow;
+  constexpr bool AROW = ASRC == kASrcRow16 || ASRC == kASrcRow8;
   static_assert(ASRC != kASrcBf16 || MT == 1, "bf16 activations: one row tile");
   extern __shared__ v4f red[];
   constexpr size_t kRedFloats = reduce_lds_bytes<MT, 1, MAXW>() / sizeof(float);
@@ -338,7 +385,7 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
       const int row = i * 16 + (lane & 15);
       const bool ok = gv && row < p.M;
       uint32_t word = 0;
-      if (p.scales_vec) {
+      if constexpr (ASRC == kASrcRow16) {
         const int4 v = buf_load16(ras, ok ? (uint32_t)row * p.lds + (uint32_t)(g * 16) : kOOB);
         const uint32_t sh = (uint32_t)(lane >> 4) * 8u;
         word = ((uint32_t)v.x >> sh & 0xFFu) | ((uint32_t)v.y >> sh & 0xFFu) << 8 |
@@ -359,10 +406,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
 
   const int nk = (int)blockIdx.x < p.Ns ? (p.Ns - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   int4 bf[D][4];
-  uint32_t sb[D];
-  // Weights and scale of this wave's group of the k-th strip into ring slot
-  // `slot` (strips past the end load zeros).
-  auto issue = [&](int k, int4 (&b)[4], uint32_t& sc) {
+  uint32_t sb[D], bb[D][1];
+  // Weights and scale of this wave's group of the k-th strip, and the bias
+  // of the strip's columns that reduce_store gives this thread, into ring
+  // slot `slot` (strips past the end load zeros).
+  auto issue = [&](int k, int4 (&b)[4], uint32_t& sc, uint32_t (&bias)[1]) {
     const int s = (int)blockIdx.x + k * (int)gridDim.x;
     const bool sv = k < nk && gv;
 #pragma unroll
@@ -372,9 +420,10 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
       b[u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
     }
     sc = buf_load4(rws, sv ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
+    load_bias<1>(p, k < nk ? s : p.Ns, bias);
   };
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue(d, bf[d], sb[d]);
+  for (int d = 0; d < D; ++d) issue(d, bf[d], sb[d], bb[d]);
   if constexpr (ASRC == kASrcBf16) {
     // the encoding waits for x only: the ring's loads stay in flight
     __builtin_amdgcn_sched_barrier(0);
@@ -406,9 +455,10 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
             default: acc[i][0] = mfma_sel<3>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
           }
         }
-      issue(k + D, bf[d], sb[d]);
+      const uint32_t bias[1] = {bb[d][0]};
+      issue(k + D, bf[d], sb[d], bb[d]);
       reduce_store<MT, 1, MAXW>(reinterpret_cast<float*>(red) + (size_t)(k & 1) * kRedFloats, acc, p,
-                                (int)blockIdx.x + k * (int)gridDim.x);
+                                (int)blockIdx.x + k * (int)gridDim.x, bias);
     }
   }
   // the ring's last loads (past the end: zeros) land before the waves end
@@ -461,6 +511,8 @@ __global__ __launch_bounds__(64 * MAXW) void linear_decode_kernel(GemmArgs p, in
   v4f acc[1][NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[0][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  uint32_t bb[NS];
+  load_bias<NS>(p, s0, bb);
 
   const int g_begin = wv * gpw;
   const int g_end = min(g_begin + gpw, p.G);
@@ -532,7 +584,7 @@ __global__ __launch_bounds__(64 * MAXW) void linear_decode_kernel(GemmArgs p, in
       }
   }
 
-  reduce_store<1, NS, MAXW>(reinterpret_cast<float*>(red), acc, p, s0);
+  reduce_store<1, NS, MAXW>(reinterpret_cast<float*>(red), acc, p, s0, bb);
 }
 
 template <int MT, int NS, int GPR, int MAXW>
@@ -541,10 +593,15 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
   // partial tiles (MXFP4 output: KW of them, plus the bf16 staging rows)
   const size_t lds = p.out_fp4 ? (size_t)kw * MT * NS * 64 * sizeof(v4f) + (size_t)MT * 16 * 32 * 2
                                : reduce_lds_bytes<MT, NS, MAXW>();
-  if (p.a_rowmajor)
-    gemm_decode_kernel<MT, NS, GPR, MAXW, true><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  // (the 16-byte scale loads' registers make two strips of two groups per
+  // round spill at one row tile: the byte loads there)
+  constexpr bool kRow16 = !(MT == 1 && NS == 2 && GPR == 2);
+  if (p.a_rowmajor && p.scales_vec && kRow16)
+    gemm_decode_kernel<MT, NS, GPR, MAXW, kRow16 ? kASrcRow16 : kASrcRow8><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  else if (p.a_rowmajor)
+    gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcRow8><<<grid, 64 * kw, lds, stream>>>(p, gpw);
   else
-    gemm_decode_kernel<MT, NS, GPR, MAXW, false><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+    gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcGemm><<<grid, 64 * kw, lds, stream>>>(p, gpw);
   return hipGetLastError();
 }
 
@@ -595,8 +652,10 @@ static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t s
   constexpr int D = MT == 4 ? 3 : 4;
   const int grid = p.Ns < p.cus ? p.Ns : p.cus;
   const size_t lds = 2 * reduce_lds_bytes<MT, 1, MAXW>();
-  if (p.a_rowmajor)
-    gemm_decode_persist_kernel<MT, MAXW, D, kASrcRow><<<grid, 64 * kw, lds, stream>>>(p);
+  if (p.a_rowmajor && p.scales_vec)
+    gemm_decode_persist_kernel<MT, MAXW, D, kASrcRow16><<<grid, 64 * kw, lds, stream>>>(p);
+  else if (p.a_rowmajor)
+    gemm_decode_persist_kernel<MT, MAXW, D, kASrcRow8><<<grid, 64 * kw, lds, stream>>>(p);
   else
     gemm_decode_persist_kernel<MT, MAXW, D, kASrcGemm><<<grid, 64 * kw, lds, stream>>>(p);
   return hipGetLastError();
