@@ -616,33 +616,36 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // either way, and fewer load rounds per wave win).
 // Where the persistent form pays: many strips per compute unit, the more
 // the fewer activation rows, and at least ten waves (groups) per workgroup.
-// Measured on MI355X with rotated weight copies (us, streaming /
-// persistent), K = 5120: N = 34816 (8.5 strips per CU): M = 17 20.6 / 18.6,
-// M = 32 21.8 / 19.3, M = 48 25.2 / 21.2, M = 64 31.6 / 24.1; N = 24576 (6
-// per CU): M = 32 14.7 / 14.5, M = 33 18.8 / 15.6, M = 64 21.0 / 17.9;
-// N = 14336 (3.5 per CU): M = 32 10.3 / 10.9, M = 64 14.1 / 13.4; N = 8192:
-// 7-11% slower at every M.  With M <= 8 it is 9-25% slower everywhere (the
-// streaming form keeps more loads in flight per compute unit); with fewer
-// waves too (K = 4096, M = 64, N = 16384: 12.50 / 12.85).
+// Measured on MI355X with a bf16 bias, rotated weight copies (us,
+// streaming / persistent), K = 5120: N = 34816 (8.5 strips per CU): M = 8
+// 17.0 / 18.1, M = 12 18.9 / 18.1, M = 16 19.0 / 18.2, M = 32 22.5 / 19.9,
+// M = 64 31.7 / 23.9; N = 24576 (6 per CU): M = 16 13.1 / 13.6, M = 17
+// 16.3 / 14.5, M = 64 21.0 / 17.8; N = 14336 (3.5 per CU): M = 48 11.5 /
+// 12.3, M = 64 14.1 / 13.1; N = 8192: 10-19% slower at every M; with M <= 8
+// 3-19% slower everywhere (the streaming form keeps more loads in flight per
+// compute unit); with fewer waves too (K = 4096, N = 16384: 12-19% slower
+// up to M = 48, 2% faster at 64).
 static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
-  if (kw < 10 || M < 16) return false;
+  if (kw < 10 || M < 12) return false;
   if (M > 48) return Ns >= 3 * cus;
-  if (M > 32) return Ns >= 6 * cus;
+  if (M > 16) return Ns >= 6 * cus;
   return Ns >= 8 * cus;
 }
 
 // Row-major (prequantised) activations: every workgroup of the streaming form
 // gathers its rows' 16-byte pieces afresh, so loading them once per wave pays
 // sooner than from the GEMM layout.  Measured as above (us, streaming /
-// persistent), K = 5120: N = 24576 (6 strips per CU): M = 1 14.5 / 13.4,
-// M = 16 14.7 / 14.0, M = 64 31.2 / 21.4; N = 34816: M = 32 28.9 / 20.8,
-// M = 64 48.7 / 27.5; N = 14336 (3.5 per CU): M = 1 8.4 / 10.0, M = 32
-// 12.9 / 12.6, M = 33 16.8 / 13.8, M = 64 20.6 / 17.0; N = 8192 (two per
-// CU): M = 64 11.5 / 12.6.
+// persistent), K = 5120: N = 24576 (6 strips per CU): M = 1 14.4 / 13.4,
+// M = 16 14.6 / 14.0, M = 17 17.7 / 14.9, M = 64 30.7 / 21.2; N = 34816:
+// M = 1 19.3 / 17.8, M = 64 48.1 / 27.0; N = 14336 (3.5 per CU): M = 16
+// 9.96 / 10.1, M = 17 10.5 / 10.9, M = 32 13.0 / 12.3, M = 64 20.4 / 16.6;
+// N = 8192 (two per CU): 8-16% slower at every M; K = 4096 (eight waves),
+// N = 16384 (four per CU): M = 17 9.8 / 10.3, M = 32 11.3 / 11.2, M = 33
+// 14.2 / 12.0, M = 64 18.8 / 14.6.
 static bool decode_persist_pays_rowmajor(int M, int Ns, int cus, int kw) {
-  if (kw < 10) return false;
-  if (M > 32) return Ns >= 3 * cus;
-  return Ns >= 6 * cus;
+  if (kw < 8) return false;
+  if (M >= 32) return Ns >= 3 * cus;
+  return kw >= 10 && Ns >= 6 * cus;
 }
 
 template <int MT, int MAXW>
