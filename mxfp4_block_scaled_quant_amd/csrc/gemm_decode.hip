@@ -613,7 +613,18 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // three (at their register counts a compute unit holds several workgroups
 // of a few waves, which beat fewer workgroups of more waves with fewer
 // load rounds each); 12 with four (a compute unit holds 12 of those waves
-// either way, and fewer load rounds per wave win).
+// either way, and fewer load rounds per wave win).  Where every strip fits
+// in one round of compute units (N/16 <= CUs) one strip per workgroup, so
+// that all of them stream: two strips per workgroup left half of them idle
+// (us, bias, two strips -> one; K = 5120, M = 1 / 16 / 64: N = 1024 4.41 /
+// 4.70 / 6.60 -> 3.57 / 3.90 / 5.14, N = 4096 4.88 / 5.17 / 7.09 -> 4.16 /
+// 4.52 / 5.93; K = 14336: N = 2048 8.10 / 8.83 / 13.82 -> 5.77 / 6.16 /
+// 10.79, N = 4096 8.82 / 9.57 / 14.57 -> 7.58 / 7.91 / 11.76), and at one
+// row tile with more than 16 groups at most 8 waves of four groups in one
+// round (14 waves of two groups put one workgroup on a compute unit at a
+// time).  Just past one round (N = 5120, 320 strips) the two-strip
+// workgroups stay: one strip in 7 waves took 10.96 us against 9.19 (M = 1,
+// K = 14336; 64 compute units stream twice).
 // Where the persistent form pays: many strips per compute unit, the more
 // the fewer activation rows, and at least ten waves (groups) per workgroup.
 // Measured on MI355X with a bf16 bias, rotated weight copies (us,
@@ -682,8 +693,11 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
       persist_ok && (ov == 7 || (ov != 8 && (p.a_rowmajor ? decode_persist_pays_rowmajor(p.M, p.Ns, p.cus, p.G)
                                                           : decode_persist_pays(p.M, p.Ns, p.cus, p.G))));
   if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
-  const bool one_strip = p.Ns >= 1024 && p.M <= 8 && !p.out_fp4;  // MXFP4 output: 32 columns per workgroup
+  // (MXFP4 output: 32 columns per workgroup)
+  const bool one_round = p.Ns <= p.cus && !p.out_fp4;
+  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round) && !p.out_fp4;
   if constexpr (MT == 1) {
+    if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
     if (gpw >= 2)
       return one_strip ? launch_decode_t<MT, 1, 2, MAXW>(p, kw, gpw, stream)
                        : launch_decode_t<MT, 2, 2, MAXW>(p, kw, gpw, stream);

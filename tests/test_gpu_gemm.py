@@ -87,6 +87,10 @@ SMALL = [
     ("tiny_1x16x32", 1, 16, 32, dict(seed=9)),
     ("tiny_5x17x96", 5, 17, 96, dict(seed=9, with_bias=True)),
     ("ragged_257x257x2080", 257, 257, 2080, dict(seed=10, outliers=True)),
+    # one row tile, more than 16 scale groups, every strip in one round of
+    # compute units: one strip and four groups per wave in the small-M kernel
+    ("widek_5x1000x8704", 5, 1000, 8704, dict(seed=14, outliers=True, with_bias=True)),
+    ("widek_16x272x14336", 16, 272, 14336, dict(seed=15, with_bias=True)),
 ]
 
 
@@ -122,7 +126,7 @@ def test_decode_widest_wave_split(M, K):
     # largest LDS reduction; bf16 / fp32 output against the oracle, and the
     # MXFP4 output bitwise the quantisation of the bf16 output.
     need_gpu()
-    N = 320
+    N = 4128  # past one round of compute units in strips: two per workgroup
     prob = inputs.linear_problem(M, N, K, 12, outliers=True, with_bias=True)
     y32, y16 = _run(prob, 0)
     _check(prob, y32, y16)

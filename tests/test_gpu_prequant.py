@@ -54,10 +54,12 @@ CASES = [
     ("m64_300x640", 64, 300, 640, dict(seed=6, with_bias=True), (0, 0)),
     ("m65_257x2080", 65, 257, 2080, dict(seed=10, outliers=True), (16, 2)),      # tiled path
     ("m300_128x256_edge", 300, 128, 256, dict(seed=5, edge=True), (0, 0)),
-    # two strips and two groups per round at one row tile (K > 8192): the
-    # byte scale loads even where the 16-byte ones would be allowed
-    ("m5_1000x8704_bias", 5, 1000, 8704, dict(seed=12, outliers=True, with_bias=True), (0, 0)),
-    ("m16_1000x8704_pad", 16, 1000, 8704, dict(seed=13, with_bias=True), (16, 1)),
+    # one row tile, K > 8192: two strips and two groups per round past one
+    # round of compute units (the byte scale loads even where the 16-byte
+    # ones would be allowed), one strip and four groups per round within one
+    ("m5_5120x8704_bias", 5, 5120, 8704, dict(seed=12, outliers=True, with_bias=True), (0, 0)),
+    ("m16_1000x8704", 16, 1000, 8704, dict(seed=13, with_bias=True), (0, 0)),
+    ("m9_1000x8704_pad", 9, 1000, 8704, dict(seed=13, with_bias=True), (16, 1)),
 ]
 
 
