@@ -622,9 +622,13 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // 10.79, N = 4096 8.82 / 9.57 / 14.57 -> 7.58 / 7.91 / 11.76), and at one
 // row tile with more than 16 groups at most 8 waves of four groups in one
 // round (14 waves of two groups put one workgroup on a compute unit at a
-// time).  Just past one round (N = 5120, 320 strips) the two-strip
-// workgroups stay: one strip in 7 waves took 10.96 us against 9.19 (M = 1,
-// K = 14336; 64 compute units stream twice).
+// time); with more row tiles and 16-32 groups likewise at most 8 waves,
+// loading four groups per round at two row tiles and two at three or four
+// (K = 14336, N = 2048, M = 17 / 32 / 64: 7.46 / 8.22 / 10.79 -> 6.91 /
+// 7.17 / 9.79 us; K = 8192: 5.35 / 5.79 / 7.09 -> 5.04 / 5.07 / 6.65; at
+// K = 6144 no faster).  Just past one round (N = 5120, 320 strips) the
+// two-strip workgroups stay: one strip in 7 waves took 10.96 us against
+// 9.19 (M = 1, K = 14336; 64 compute units stream twice).
 // Where the persistent form pays: many strips per compute unit, the more
 // the fewer activation rows, and at least ten waves (groups) per workgroup.
 // Measured on MI355X with a bf16 bias, rotated weight copies (us,
@@ -701,6 +705,15 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
     if (gpw >= 2)
       return one_strip ? launch_decode_t<MT, 1, 2, MAXW>(p, kw, gpw, stream)
                        : launch_decode_t<MT, 2, 2, MAXW>(p, kw, gpw, stream);
+  }
+  if constexpr (MT > 1) {
+    // one round of compute units and 16-32 groups: at most 8 waves, each
+    // loading four groups (two row tiles) or two (three and four) per round
+    if (one_round && p.G >= 16 && p.G <= 32) {
+      const int g8 = (p.G + 7) / 8;
+      const int gp = MT == 2 ? (g8 < 4 ? 4 : g8) : (g8 + 1) / 2 * 2;
+      return launch_decode_t<MT, 1, MT == 2 ? 4 : 2, 8>(p, (p.G + gp - 1) / gp, gp, stream);
+    }
   }
   return one_strip ? launch_decode_t<MT, 1, 1, MAXW>(p, kw, gpw, stream)
                    : launch_decode_t<MT, 2, 1, MAXW>(p, kw, gpw, stream);

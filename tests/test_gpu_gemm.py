@@ -91,6 +91,11 @@ SMALL = [
     # compute units: one strip and four groups per wave in the small-M kernel
     ("widek_5x1000x8704", 5, 1000, 8704, dict(seed=14, outliers=True, with_bias=True)),
     ("widek_16x272x14336", 16, 272, 14336, dict(seed=15, with_bias=True)),
+    # more row tiles there: four groups per round at two tiles, two at three
+    # and four (ragged last round, ragged last scale group)
+    ("widek_20x272x8192", 20, 272, 8192, dict(seed=16, outliers=True)),
+    ("widek_40x300x10272", 40, 300, 10272, dict(seed=17, with_bias=True)),
+    ("widek_64x96x14336_bias", 64, 96, 14336, dict(seed=18, edge=True, with_bias=True)),
 ]
 
 

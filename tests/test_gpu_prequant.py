@@ -60,6 +60,8 @@ CASES = [
     ("m5_5120x8704_bias", 5, 5120, 8704, dict(seed=12, outliers=True, with_bias=True), (0, 0)),
     ("m16_1000x8704", 16, 1000, 8704, dict(seed=13, with_bias=True), (0, 0)),
     ("m9_1000x8704_pad", 9, 1000, 8704, dict(seed=13, with_bias=True), (16, 1)),
+    ("m40_300x10240", 40, 300, 10240, dict(seed=14, outliers=True, with_bias=True), (16, 16)),
+    ("m64_96x14336_pad", 64, 96, 14336, dict(seed=15, with_bias=True), (0, 3)),
 ]
 
 
