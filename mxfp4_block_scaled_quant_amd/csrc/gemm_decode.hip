@@ -633,18 +633,19 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // the fewer activation rows, and at least ten waves (groups) per workgroup.
 // Measured on MI355X with a bf16 bias, rotated weight copies (us,
 // streaming / persistent), K = 5120: N = 34816 (8.5 strips per CU): M = 8
-// 17.0 / 18.1, M = 12 18.9 / 18.1, M = 16 19.0 / 18.2, M = 32 22.5 / 19.9,
-// M = 64 31.7 / 23.9; N = 24576 (6 per CU): M = 16 13.1 / 13.6, M = 17
+// 17.0 / 18.1, M = 9 18.8 / 18.1, M = 12 18.9 / 18.1, M = 16 19.0 / 18.2,
+// M = 32 22.5 / 19.9, M = 64 31.7 / 23.9; N = 28672 (7 per CU): M = 8 14.6 /
+// 15.2, M = 9 16.8 / 15.2; N = 24576 (6 per CU): M = 16 13.1 / 13.6, M = 17
 // 16.3 / 14.5, M = 64 21.0 / 17.8; N = 14336 (3.5 per CU): M = 48 11.5 /
 // 12.3, M = 64 14.1 / 13.1; N = 8192: 10-19% slower at every M; with M <= 8
 // 3-19% slower everywhere (the streaming form keeps more loads in flight per
 // compute unit); with fewer waves too (K = 4096, N = 16384: 12-19% slower
 // up to M = 48, 2% faster at 64).
 static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
-  if (kw < 10 || M < 12) return false;
+  if (kw < 10 || M <= 8) return false;
   if (M > 48) return Ns >= 3 * cus;
   if (M > 16) return Ns >= 6 * cus;
-  return Ns >= 8 * cus;
+  return Ns >= 7 * cus;
 }
 
 // Row-major (prequantised) activations: every workgroup of the streaming form
