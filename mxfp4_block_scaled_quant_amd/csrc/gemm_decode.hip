@@ -700,7 +700,11 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
   // (MXFP4 output: 32 columns per workgroup)
   const bool one_round = p.Ns <= p.cus && !p.out_fp4;
-  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round) && !p.out_fp4;
+  // (and at K <= 2048 with one or four row tiles: N = 14336, K = 2048, M = 1
+  // / 16 / 64: 5.24 / 5.53 / 10.36 -> 5.01 / 5.37 / 8.50 us; K = 1024, M = 64:
+  // 11.56 -> 8.52; two and three row tiles, or K >= 3072, were slower)
+  const bool small_k = p.G <= 4 && (MT == 1 || MT == 4);
+  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k) && !p.out_fp4;
   if constexpr (MT == 1) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
     if (gpw >= 2)

@@ -96,6 +96,11 @@ SMALL = [
     ("widek_20x272x8192", 20, 272, 8192, dict(seed=16, outliers=True)),
     ("widek_40x300x10272", 40, 300, 10272, dict(seed=17, with_bias=True)),
     ("widek_64x96x14336_bias", 64, 96, 14336, dict(seed=18, edge=True, with_bias=True)),
+    # past one round of compute units in strips, K <= 2048: one strip per
+    # workgroup at one and four row tiles, two at two
+    ("smallk_3x4200x2048", 3, 4200, 2048, dict(seed=19, with_bias=True)),
+    ("smallk_64x4200x1056", 64, 4200, 1056, dict(seed=20, outliers=True)),
+    ("smallk_30x4200x2048", 30, 4200, 2048, dict(seed=21, with_bias=True)),
 ]
 
 
