@@ -755,12 +755,16 @@ bool linear_fused_pays(int M, int N, int K) {
 hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
   if (p.M > kFusedRows) return hipErrorInvalidValue;
   // Up to 8192-wide K: at most 16 waves of one group each, one strip per
-  // workgroup when strips are plentiful.  Wider K: at most 8 waves of two
+  // workgroup when strips are plentiful or all fit in one round of compute
+  // units (N = 4096, K = 5120, M = 1 / 4: 5.01 / 5.56 -> 4.41 / 4.88 us;
+  // K = 8192: 6.41 / 7.26 -> 5.45 / 6.09).  Wider K: at most 8 waves of two
   // groups per round and one strip (fewer waves re-encoding the rows, and
-  // two strips would not fit the registers).
+  // two strips would not fit the registers; four groups per round in 7
+  // waves measured slower: K = 14336, N = 5120, M = 1: 12.14 against 10.66).
   if (p.G <= 16) {
     const int kw = p.G;
-    return p.Ns >= 1024 ? launch_linear_t<1, 1>(p, kw, 1, stream) : launch_linear_t<2, 1>(p, kw, 1, stream);
+    return (p.Ns >= 1024 || p.Ns <= p.cus) ? launch_linear_t<1, 1>(p, kw, 1, stream)
+                                           : launch_linear_t<2, 1>(p, kw, 1, stream);
   }
   const int gpw = (p.G + 7) / 8;
   const int kw = (p.G + gpw - 1) / gpw;
