@@ -685,20 +685,20 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   constexpr int MAXW = MT == 1 ? 16 : MT == 4 ? 12 : 8;
   const int gpw = (p.G + MAXW - 1) / MAXW;
   const int kw = (p.G + gpw - 1) / gpw;
-  // persistent form: one group per wave, bf16 / fp32 output from the GEMM
-  // layout (path 7 of the test hook forces it where it applies, 8 keeps the
-  // form above)
-  // (one group per wave there: the same K split as above wherever that has
-  // one group per wave too, so the same bits; two or three row tiles above
-  // 4096 of K split K in two groups per wave above, so their sums differ in
-  // order)
+  // persistent form: one group per wave, bf16 / fp32 output, activations in
+  // the GEMM layout or row-major (path 7 of the test hook forces it where it
+  // applies, 8 keeps the streaming form); the same K split as the streaming
+  // form wherever that has one group per wave too, so the same bits (two or
+  // three row tiles above 4096 of K give each streaming wave two groups, so
+  // their sums differ in order)
   const bool persist_ok = p.G <= 12 && !p.out_fp4;
   const int ov = get_gemm_path_override();
   const bool persist =
       persist_ok && (ov == 7 || (ov != 8 && (p.a_rowmajor ? decode_persist_pays_rowmajor(p.M, p.Ns, p.cus, p.G)
                                                           : decode_persist_pays(p.M, p.Ns, p.cus, p.G))));
   if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
-  // (MXFP4 output: 32 columns per workgroup)
+  // one strip per workgroup never with MXFP4 output (a workgroup encodes
+  // whole 32-column blocks)
   const bool one_round = p.Ns <= p.cus && !p.out_fp4;
   // (and at K <= 2048 with one or four row tiles: N = 14336, K = 2048, M = 1
   // / 16 / 64: 5.24 / 5.53 / 10.36 -> 5.01 / 5.37 / 8.50 us; K = 1024, M = 64:
