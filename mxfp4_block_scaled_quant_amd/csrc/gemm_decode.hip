@@ -747,9 +747,16 @@ bool linear_fused_pays(int M, int N, int K) {
   // call beats quantisation + GEMM (about 2 us for the extra launch) only
   // while that traffic is small: measured on MI355X, at M = 1 for every
   // decode shape, and up to M = 4 when there are few workgroups (N < 16384)
-  // and one round of groups per wave (K <= 8192).
+  // and one round of groups per wave (K <= 8192).  With two rounds
+  // (K <= 16384) it still pays at M = 2, and up to M = 4 while the strips
+  // fit in about one round of compute units (N <= 4096): K = 14336,
+  // N = 4096, M = 2 / 4: 9.76 / 9.85 -> 7.56 / 8.86 us; N = 14336, M = 2:
+  // 22.36 -> 20.68 us; but N = 5120, M = 4: 11.63 -> 13.03 us.
   if (M < 1 || M > kFusedRows) return false;
-  return M == 1 || (N < 16384 && K <= 8192);
+  if (M == 1) return true;
+  if (N >= 16384) return false;
+  if (K <= 8192) return true;
+  return K <= 16384 && (M == 2 || N <= 4096);
 }
 
 hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {

@@ -40,9 +40,11 @@ def _linear(x_bits, W, N, bias_bits, ldx_pad=0):
 
 
 def _same_split(M, N, K):
-    """The fused kernel (M = 1, or M <= 4 at N < 16384, K <= 8192) splits K
-    like the small-M GEMM except beyond 16 scale groups (K > 8192)."""
-    fused = M == 1 or (M <= 4 and N < 16384 and K <= 8192)
+    """The fused kernel (M = 1; M <= 4 at N < 16384, K <= 8192; M = 2 at
+    N < 16384, K <= 16384; M <= 4 at N <= 4096, K <= 16384) splits K like
+    the small-M GEMM except beyond 16 scale groups (K > 8192)."""
+    wide_k = K <= 16384 and (M == 2 or N <= 4096)
+    fused = M == 1 or (M <= 4 and N < 16384 and (K <= 8192 or wide_k))
     groups = -(-(-(-K // 128)) // 4)
     return not (fused and groups > 16)
 
@@ -62,12 +64,16 @@ def _two_launch(x_bits, W, N, bias_bits):
 
 
 CASES = [
-    # name, M, N, K, problem kwargs, ldx padding (fused quantisation at M = 1
-    # and at M <= 4 for N < 16384, K <= 8192; else through the workspace)
+    # name, M, N, K, problem kwargs, ldx padding (fused quantisation at M = 1,
+    # at M <= 4 for N < 16384, K <= 8192, and up to K = 16384 at M = 2 or
+    # N <= 4096; else through the workspace)
     ("m1_1024x5120", 1, 1024, 5120, dict(seed=0, outliers=True), 0),
     ("m2_96x4128_edge", 2, 96, 4128, dict(seed=5, edge=True), 16),
     ("m1_1056x14336_bias", 1, 1056, 14336, dict(seed=4, with_bias=True), 0),    # fused, wide K
-    ("m3_1056x14336_bias", 3, 1056, 14336, dict(seed=4, with_bias=True), 0),
+    ("m3_1056x14336_bias", 3, 1056, 14336, dict(seed=4, with_bias=True), 0),   # fused, two rounds
+    ("m2_2000x16384_bias", 2, 2000, 16384, dict(seed=12, with_bias=True), 0),   # fused, 32 groups
+    ("m4_1000x10240_edge", 4, 1000, 10240, dict(seed=13, edge=True), 16),      # fused, ragged rounds
+    ("m3_4112x9216", 3, 4112, 9216, dict(seed=14, outliers=True), 0),          # workspace (N > 4096)
     ("m1_17x8320", 1, 17, 8320, dict(seed=11, outliers=True), 8),               # fused, 17 groups
     ("m4_300x640_bias", 4, 300, 640, dict(seed=6, with_bias=True), 0),
     ("m4_16x32", 4, 16, 32, dict(seed=9), 8),
