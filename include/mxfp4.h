@@ -53,6 +53,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbols by default; the entry points
+ * declared here are its only exports. */
+#pragma GCC visibility push(default)
+
 typedef enum {
   MXFP4_OK = 0,
   MXFP4_ERR_NULL = 1,      /* a required pointer is NULL                        */
@@ -315,6 +319,8 @@ int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm,
                 const void* w_pre, const void* ws_pre,
                 void* out, int64_t sob, int64_t som, int out_dtype,
                 int64_t B, int64_t M, int64_t N, int64_t K, void* stream);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,9 @@ extern "C" {
  * only.
  * Returns MXFP4_OK, or MXFP4_ERR_ARG for other values.
  */
+#pragma GCC visibility push(default)
 int mxfp4_testing_set_gemm_path(int path);
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,8 @@ FLAGS = [
     # Keep the compiler from forming packed fp32 arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # Only the entry points the headers declare are exported.
+    "-fvisibility=hidden",
 ]
 
 

@@ -41,6 +41,33 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) <= set(mx._SIGNATURES), "binding lacks a declared function"
 
 
+def _exported_functions(path):
+    """Names of the defined global/weak FUNC symbols of an ELF64 shared
+    library's dynamic symbol table (read directly, no external tool)."""
+    import struct
+    data = open(path, "rb").read()
+    assert data[:4] == b"\x7fELF" and data[4] == 2, "not an ELF64 file"
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum = struct.unpack_from("<HH", data, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    dynsym = next(s for s in secs if s[1] == 11)  # SHT_DYNSYM
+    strtab = secs[dynsym[6]]
+    names = set()
+    for off in range(dynsym[4], dynsym[4] + dynsym[5], 24):
+        st_name, st_info, _other, st_shndx = struct.unpack_from("<IBBH", data, off)
+        if (st_info & 0xF) == 2 and (st_info >> 4) in (1, 2) and st_shndx != 0:
+            end = data.index(b"\0", strtab[4] + st_name)
+            names.add(data[strtab[4] + st_name:end].decode())
+    return names
+
+
+def test_only_declared_functions_are_exported(lib):
+    # the library is built with hidden symbols: its host functions are
+    # exactly the C entry points the headers declare (kernel handles and the
+    # HIP runtime's registration data are objects, not functions)
+    assert _exported_functions(mx.LIB_PATH) == set(_declared_functions())
+
+
 def test_status_strings_and_version(lib):
     assert lib.mxfp4_abi_version() == 103
     for s in range(8):
