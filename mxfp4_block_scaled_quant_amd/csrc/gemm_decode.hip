@@ -168,7 +168,7 @@ __device__ __forceinline__ void reduce_store_fp4(v4f* red, const v4f (&acc)[MT][
   }
 }
 
-template <int MT, int NS, int GPR, int MAXW, int ASRC>
+template <int MT, int NS, int GPR, int MAXW, int ASRC, bool HOLDA>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int gpw) {
   constexpr bool AROW = ASRC == kASrcRow16 || ASRC == kASrcRow8;
   static_assert(ASRC != kASrcBf16, "bf16 activations: the persistent form only");
@@ -246,13 +246,14 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
         }
       }
     }
-    if constexpr (AROW && GPR == 1) {
+    if constexpr (AROW && GPR == 1 && HOLDA) {
       // Row-major rows are a few KiB that every workgroup reads piece by
       // piece; requested alongside the weights they slowed the stream
       // (N = 14336, K = 5120, M = 1 / 4 / 16: 9.13 / 9.33 / 10.72 us),
       // requested once the weights and scales are in they do not (8.47 /
-      // 8.67 / 9.93).  With two groups per round the concurrent form is the
-      // faster (K = 14336, N = 5120, M = 1: 9.58 against 9.75).
+      // 8.67 / 9.93).  Where one row tile's waves have several groups the
+      // launch holds nothing (K = 14336, N = 5120, M = 1 / 4 / 16: 9.31 /
+      // 9.70 / 11.45 us with the wait, 9.03 / 9.30 / 11.09 without).
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
@@ -587,21 +588,29 @@ __global__ __launch_bounds__(64 * MAXW) void linear_decode_kernel(GemmArgs p, in
   reduce_store<1, NS, MAXW>(reinterpret_cast<float*>(red), acc, p, s0, bb);
 }
 
-template <int MT, int NS, int GPR, int MAXW>
+// HOLDA: row-major activation loads wait for the round's weights (one group
+// per round only).
+template <int MT, int NS, int GPR, int MAXW, bool HOLDA = true>
 static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_t stream) {
   const dim3 grid((unsigned)((p.Ns + NS - 1) / NS));
   // partial tiles (MXFP4 output: KW of them, plus the bf16 staging rows)
   const size_t lds = p.out_fp4 ? (size_t)kw * MT * NS * 64 * sizeof(v4f) + (size_t)MT * 16 * 32 * 2
                                : reduce_lds_bytes<MT, NS, MAXW>();
-  // (the 16-byte scale loads' registers make two strips of two groups per
-  // round spill at one row tile: the byte loads there)
-  constexpr bool kRow16 = !(MT == 1 && NS == 2 && GPR == 2);
-  if (p.a_rowmajor && p.scales_vec && kRow16)
-    gemm_decode_kernel<MT, NS, GPR, MAXW, kRow16 ? kASrcRow16 : kASrcRow8><<<grid, 64 * kw, lds, stream>>>(p, gpw);
-  else if (p.a_rowmajor)
-    gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcRow8><<<grid, 64 * kw, lds, stream>>>(p, gpw);
-  else
-    gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcGemm><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  // Row-major activations at one row tile are never loaded two groups per
+  // round (launch_decode_mt gives them one: two strips of two groups spill
+  // with the 16-byte scale loads), so those forms are not built.
+  constexpr bool kRowForms = !(MT == 1 && GPR == 2);
+  if constexpr (kRowForms) {
+    if (p.a_rowmajor && p.scales_vec)
+      gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcRow16, HOLDA><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+    else if (p.a_rowmajor)
+      gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcRow8, HOLDA><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+    else
+      gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcGemm, false><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  } else {
+    if (p.a_rowmajor) return hipErrorInvalidValue;
+    gemm_decode_kernel<MT, NS, GPR, MAXW, kASrcGemm, false><<<grid, 64 * kw, lds, stream>>>(p, gpw);
+  }
   return hipGetLastError();
 }
 
@@ -707,6 +716,13 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k) && !p.out_fp4;
   if constexpr (MT == 1) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
+    // (row-major activations: one group per round, so the 16-byte scale
+    // loads fit the registers, and no hold on them — K = 14336, N = 5120 /
+    // 14336, M = 16: 12.97 / 26.59 -> 11.09 / 22.97 us; the same K split and
+    // order, so the same bits as the GEMM layout's two groups per round)
+    if (gpw >= 2 && p.a_rowmajor)
+      return one_strip ? launch_decode_t<MT, 1, 1, MAXW, false>(p, kw, gpw, stream)
+                       : launch_decode_t<MT, 2, 1, MAXW, false>(p, kw, gpw, stream);
     if (gpw >= 2)
       return one_strip ? launch_decode_t<MT, 1, 2, MAXW>(p, kw, gpw, stream)
                        : launch_decode_t<MT, 2, 2, MAXW>(p, kw, gpw, stream);

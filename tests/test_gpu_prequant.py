@@ -138,3 +138,42 @@ def test_linear_prequantized_persistent_form(name, M, N, K, pads):
     assert any(np.array_equal(d32, res[f][0].cpu().numpy().view(np.uint32)) for f in (7, 8))
     _check(prob, y32, res[7][1].cpu().view(torch.int16).numpy().view(np.uint16),
            cols=_sample(N, 96, N) if N > 4096 else None)
+
+
+WIDE_K = [
+    # name, M, N, K, (data, scale) row padding: more than 16 scale groups on
+    # more strips than compute units, so each wave of the streaming form
+    # loads its groups one per round over several rounds
+    ("m1_4112x9216_lds3", 1, 4112, 9216, (0, 3)),          # byte scale loads
+    ("m16_4112x12800", 16, 4112, 12800, (0, 0)),           # 16-byte loads, 25 groups on 13 waves
+    ("m4_5120x14336_pad", 4, 5120, 14336, (16, 16)),
+    ("m24_4112x9216_pad", 24, 4112, 9216, (16, 1)),        # two row tiles, byte loads
+]
+
+
+@pytest.mark.parametrize("name,M,N,K,pads", WIDE_K, ids=[c[0] for c in WIDE_K])
+def test_linear_prequantized_wide_k(name, M, N, K, pads):
+    # bitwise the GEMM-layout path through the streaming form over every
+    # output (the same K split and order), and the oracle bar on sampled
+    # columns
+    need_gpu()
+    from tests.test_gpu_gemm import _sample
+    prob = inputs.linear_problem(M, N, K, 22, outliers=True, with_bias=True)
+    W = mx.quantize_weight(dev_bf16(prob["w"]))
+    q_rm, s_rm = Q.quant_1x32(prob["x"])
+    xq, xs = _strided_u8(q_rm, pads[0]), _strided_u8(s_rm, pads[1])
+    b = dev_bf16(prob["bias"])
+    y32 = mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.float32)
+    y16 = mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.bfloat16)
+    q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
+    mx.set_gemm_path(8)
+    try:
+        r32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
+        r16 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.bfloat16)
+    finally:
+        mx.set_gemm_path(0)
+    torch.cuda.synchronize()
+    y32n = y32.cpu().numpy()
+    assert np.array_equal(y32n.view(np.uint32), r32.cpu().numpy().view(np.uint32))
+    assert torch.equal(y16.cpu().view(torch.int16), r16.cpu().view(torch.int16))
+    _check(prob, y32n, y16.cpu().view(torch.int16).numpy().view(np.uint16), cols=_sample(N, 96, N))
