@@ -718,9 +718,13 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
     // (row-major activations: one group per round, so the 16-byte scale
     // loads fit the registers, and no hold on them — K = 14336, N = 5120 /
-    // 14336, M = 16: 12.97 / 26.59 -> 11.09 / 22.97 us; the same K split and
-    // order, so the same bits as the GEMM layout's two groups per round)
-    if (gpw >= 2 && p.a_rowmajor)
+    // 14336, M = 16: 12.97 / 26.59 -> 11.09 / 22.97 us; the GEMM layout
+    // likewise once the two-strip workgroups fill a round of compute units —
+    // N = 14336, K = 14336, M = 1 / 16: 19.94 / 21.02 -> 19.14 / 20.35;
+    // N = 12288, K = 10240: 14.86 / 15.56 -> 13.68 / 14.80; but N = 5120,
+    // 160 workgroups: 9.18 -> 9.43.  One group or two per round, the same K
+    // split and order, so the same bits)
+    if (gpw >= 2 && (p.a_rowmajor || p.Ns >= 2 * p.cus))
       return one_strip ? launch_decode_t<MT, 1, 1, MAXW, false>(p, kw, gpw, stream)
                        : launch_decode_t<MT, 2, 1, MAXW, false>(p, kw, gpw, stream);
     if (gpw >= 2)

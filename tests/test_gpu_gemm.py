@@ -241,6 +241,27 @@ def test_decode_sweep_full_size(N, K):
         _check(prob, y32, y16, cols=cols)
 
 
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_group_rounds_same_bits(M):
+    # More than 16 scale groups at one row tile: with 513 strips (two-strip
+    # workgroups filling a round of compute units) each wave loads its groups
+    # one per round, with 320 strips two per round; the K split and order are
+    # the same, so the first 5120 columns agree bitwise.  The oracle bar on
+    # sampled columns of the wide product.
+    need_gpu()
+    N, K = 8208, 8704
+    w, W = _weight(N, K, 4)
+    b = inputs.bias(N, 4)
+    x = inputs.activations(M, K, 4, outliers=True)
+    prob = {"x": x, "w": w, "bias": b}
+    y32, y16 = _run(prob, 0, weight=W)
+    part = {"x": x, "w": w[:5120], "bias": b[:5120]}
+    p32, p16 = _run(part, 0)
+    assert np.array_equal(y32[:, :5120].view(np.uint32), p32.view(np.uint32))
+    assert np.array_equal(y16[:, :5120], p16)
+    _check(prob, y32, y16, cols=_sample(N, 96, N))
+
+
 @pytest.mark.parametrize("N,K", NK, ids=[f"{n}x{k}" for n, k in NK])
 def test_prefill_sweep_full_size(N, K):
     # M in {512, 2048, 8192}, 1% outlier channels x20, no bias.
