@@ -713,7 +713,15 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   // / 16 / 64: 5.24 / 5.53 / 10.36 -> 5.01 / 5.37 / 8.50 us; K = 1024, M = 64:
   // 11.56 -> 8.52; two and three row tiles, or K >= 3072, were slower)
   const bool small_k = p.G <= 4 && (MT == 1 || MT == 4);
-  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k) && !p.out_fp4;
+  // (and at one row tile between two and three strips per compute unit:
+  // two-strip workgroups leave some units four strips, one-strip ones at
+  // most three — K = 8192, N = 10240 / 12288, M = 1: 11.33 / 11.89 -> 9.44 /
+  // 10.27 us, M = 16: 11.81 / 12.38 -> 10.59 / 11.15; K = 5120, N = 10240,
+  // M = 1 / 16: 7.93 / 8.66 -> 6.92 / 7.83.  Where both forms give each unit
+  // the same number of strips two per workgroup share the activations:
+  // N = 6144 and 14336 stay, 0.3-0.8 us faster at M = 16)
+  const bool balance = MT == 1 && p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus;
+  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k || balance) && !p.out_fp4;
   if constexpr (MT == 1) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
     // (row-major activations: one group per round, so the 16-byte scale
