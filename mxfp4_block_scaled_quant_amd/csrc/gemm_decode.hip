@@ -796,10 +796,16 @@ hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
   // groups per round and one strip (fewer waves re-encoding the rows, and
   // two strips would not fit the registers; four groups per round in 7
   // waves measured slower: K = 14336, N = 5120, M = 1: 12.14 against 10.66).
+  // As the GEMM, one strip between two and three strips per compute unit,
+  // where each workgroup's re-encoding of x is cheap (M <= 2: K = 5120,
+  // N = 10240 / 12288, M = 1: 8.83 / 9.08 -> 7.27 / 7.78 us; K = 8192,
+  // N = 10240, M = 1 / 2: 11.81 / 12.15 -> 9.63 / 10.20; at M = 4 mixed,
+  // N = 12288: 9.85 -> 10.59).
   if (p.G <= 16) {
     const int kw = p.G;
-    return (p.Ns >= 1024 || p.Ns <= p.cus) ? launch_linear_t<1, 1>(p, kw, 1, stream)
-                                           : launch_linear_t<2, 1>(p, kw, 1, stream);
+    const bool balance = p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus && p.M <= 2;
+    return (p.Ns >= 1024 || p.Ns <= p.cus || balance) ? launch_linear_t<1, 1>(p, kw, 1, stream)
+                                                      : launch_linear_t<2, 1>(p, kw, 1, stream);
   }
   const int gpw = (p.G + 7) / 8;
   const int kw = (p.G + gpw - 1) / gpw;

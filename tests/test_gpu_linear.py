@@ -221,3 +221,19 @@ def test_persistent_encoding_every_bf16_value():
             assert np.array_equal(unsigned(y32), unsigned(dq[r0:r0 + M])), (r0, M)
     finally:
         mx.set_gemm_path(0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8208, 5120), (2, 10240, 8192)], ids=["m1_8208x5120", "m2_10240x8192"])
+def test_linear_fused_one_strip_per_workgroup(M, N, K):
+    # Between two and three strips per compute unit the fused kernel runs one
+    # strip per workgroup at M <= 2: bitwise quantisation + GEMM, and the
+    # oracle bar on sampled columns.
+    need_gpu()
+    w, W = _weight(N, K, 5)
+    b = inputs.bias(N, 5)
+    x = inputs.activations(M, K, 5, outliers=True)
+    y32, y16 = _linear(x, W, N, b)
+    r32, r16 = _two_launch(x, W, N, b)
+    assert np.array_equal(y32.view(np.uint32), r32.view(np.uint32))
+    assert np.array_equal(y16, r16)
+    _check({"x": x, "w": w, "bias": b}, y32, y16, cols=_sample(N, 96, N))
