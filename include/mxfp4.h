@@ -93,8 +93,9 @@ size_t mxfp4_weight_bytes(int64_t batch, int64_t N, int64_t K);
 size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K);
 
 /* Workspace bytes mxfp4_gemm_a4w4 and mxfp4_gemm_a4w4_mxfp4_out need for
- * this shape: 0 where the GEMM runs on whole output tiles (every M <= 64
- * call, and most larger ones), else the split schedule's (see
+ * this shape: 0 where the GEMM needs none (every M <= 64 call, calls of up
+ * to 256 rows on few columns, and most larger ones on whole output tiles),
+ * else the split schedule's (see
  * mxfp4_gemm_a4w4), sized for up to 256 compute units: a give-up word, 4
  * bytes per split tile and per workgroup (these rounded up to 256 bytes),
  * then one fp32 output tile per workgroup (256 KiB, or 128 KiB with
@@ -170,7 +171,9 @@ int mxfp4_preshuffle_weight(const void* w_fp4, const void* w_scales,
  *             that tile is then not to be trusted).  Calls that overlap in
  *             time (other streams) need workspaces of their own.
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
- * For M > 64 the output is cut into 256 x 256 tiles, or 256 x 128 where the
+ * For 64 < M <= 256 with ceil(M/64) * N <= 16384 the small-M kernel runs
+ * once per 64 rows (each launch as a call on those rows alone would be).
+ * Otherwise, for M > 64 the output is cut into 256 x 256 tiles, or 256 x 128 where the
  * wider ones would leave most compute units idle (measured rule).  Where
  * whole tiles would leave the last round of compute units at most half full
  * and K is long enough to pay for it,
@@ -279,14 +282,17 @@ int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t 
  *   out[m, n] = round(sum_k dq(x)[m,k] dq(W)[n,k] + bias[n])
  * For M <= 64 the GEMM kernel reads the row-major operands directly (one
  * launch; bitwise the result of mxfp4_gemm_a4w4 on the same values in the
- * GEMM layouts); for larger M they are permuted into `workspace` first.
+ * GEMM layouts), and so it does once per 64 rows where mxfp4_gemm_a4w4 runs
+ * the small-M kernel per 64 rows (M <= 256, ceil(M/64) * N <= 16384); for
+ * larger M they are permuted into `workspace` first.
  *
  *   x_fp4     packed FP4 [M, K/2], row stride ldq BYTES (ldq >= K/2,
  *             ldq % 16 == 0, 16-byte aligned)
  *   x_scales  E8M0 [M, K/32], row stride lds BYTES (lds >= K/32)
  *   w_pre, ws_pre, bias, out, ldo, out_dtype: as for mxfp4_gemm_a4w4
  *   workspace mxfp4_linear_prequantized_workspace_bytes(M, N, K) bytes (0
- *             for M <= 64: may be NULL), 16-byte aligned, caller-owned
+ *             where the small-M kernel reads the operands: may be NULL),
+ *             16-byte aligned, caller-owned
  *   M >= 0 (M == 0 enqueues nothing), N >= 1, K > 0, K % 32 == 0.
  */
 size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K);

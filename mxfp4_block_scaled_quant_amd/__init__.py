@@ -178,7 +178,9 @@ def weight_scale_bytes(batch: int, N: int, K: int) -> int:
 
 def set_gemm_path(path: int) -> None:
     """Test hook (include/mxfp4_testing.h), for the calling thread only: 1
-    forces the small-M kernel (M <= 64), 2 the tiled kernel, 0 = by M; 3 the
+    forces the small-M kernel (M <= 64), 2 the tiled kernel, 0 = by M and N
+    (the small-M kernel up to 64 rows, and once per 64 rows up to 256 rows
+    where ceil(M/64) * N <= 16384); 3 the
     tiled kernel on whole 256-wide tiles only, 4 with the split (split-K)
     schedule; 5 and 6 the same with 128-wide tiles."""
     _check("mxfp4_testing_set_gemm_path", lib().mxfp4_testing_set_gemm_path(path))

@@ -29,6 +29,31 @@ constexpr int64_t kFusedMaxM = 4;          // mxfp4_linear quantises inside the 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Which GEMM kernel a call of M rows and N columns takes: 1 = small-M,
+// 2 = large-M, 3 = small-M once per 64 rows.  Up to 256 rows the large-M
+// kernel runs a single row of 256-row tiles, one per 128 (or 256) columns
+// on few compute units, its K-steps latency-bound; the small-M kernel
+// streams the weights on all of them, once per 64 rows, so it wins while
+// those c = ceil(M/64) passes move few weight bytes: c * N <= 16384.
+// Measured on MI355X (us, one tile row -> c launches): N = 4096, K = 4096,
+// M = 65 / 128 / 192 18.7 / 18.7 / 18.7 -> 8.7 / 10.3 / 15.0; N = 8192,
+// K = 14336, M = 65 / 128 34.4 / 35.0 -> 27.8 / 32.8; N = 4096, K = 14336,
+// M = 192 / 256 51.9 / 52.3 -> 31.8 / 42.4; N = 1024, K = 4096, M = 256
+// 18.6 -> 17.9.  Past that bound the tile row wins (N = 8192, M = 192:
+// 19.0 -> 20.5 at K = 4096; N = 14336, K = 8192, M = 128: 28.1 -> 36.0).
+int gemm_path(int64_t M, int64_t N) {
+  const int path = get_gemm_path_override();
+  if ((path == 1 || path == 7 || path == 8) && M <= 64) return 1;
+  if (path >= 2 && path <= 6) return 2;
+  if (M <= 64) return 1;
+  const int64_t c = (M + 63) / 64;
+  return c <= 4 && c * N <= 16384 ? 3 : 2;
+}
+
+hipError_t launch_gemm_path(int path, const GemmArgs& p, hipStream_t s) {
+  return path == 1 ? launch_gemm_decode(p, s) : path == 3 ? launch_gemm_decode_rows(p, s) : launch_gemm_prefill(p, s);
+}
+
 int64_t gemm_scale_bytes(int64_t rows, int64_t K) {
   const int64_t kt = cdiv(K, 128), g = cdiv(kt, 4);
   return cdiv(rows, 16) * g * 256;
@@ -145,7 +170,7 @@ int linear_run(const void* x, int64_t ldx, const void* w_pre, const void* ws_pre
     p.work = q + act_gemm_offset(M, K);
     p.work_bytes = workspace_bytes - act_gemm_offset(M, K);
   }
-  return launched(M <= 64 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+  return launched(launch_gemm_path(M <= 64 ? 1 : gemm_path(M, N), p, s));
 }
 
 }  // namespace mxfp4
@@ -194,17 +219,9 @@ size_t mxfp4_weight_scale_bytes(int64_t batch, int64_t N, int64_t K) {
   return (size_t)(batch * gemm_scale_bytes(N, K));
 }
 
-// Which GEMM kernel a call of M rows takes: 1 = small-M, 2 = large-M.
-static int gemm_path(int64_t M) {
-  const int path = get_gemm_path_override();
-  if ((path == 1 || path == 7 || path == 8) && M <= 64) return 1;
-  if (path >= 2 && path <= 6) return 2;
-  return M <= 64 ? 1 : 2;
-}
-
 size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 32 || K > kMaxK || N > kMaxBuf || M > kMaxBuf) return 0;
-  return gemm_path(M) == 2 ? gemm_prefill_workspace_bytes(M, N, K) : 0;
+  return gemm_path(M, N) == 2 ? gemm_prefill_workspace_bytes(M, N, K) : 0;
 }
 
 
@@ -292,7 +309,7 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales, const void* w_pre,
   p.work = (uint8_t*)workspace;
   p.work_bytes = workspace ? workspace_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
-  return launched(gemm_path(M) == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+  return launched(launch_gemm_path(gemm_path(M, N), p, s));
 }
 
 size_t mxfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -370,7 +387,7 @@ int mxfp4_gemm_a4w4_mxfp4_out(const void* a_fp4, const void* a_scales, const voi
   p.work = (uint8_t*)workspace;
   p.work_bytes = workspace ? workspace_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
-  return launched(gemm_path(M) == 1 ? launch_gemm_decode(p, s) : launch_gemm_prefill(p, s));
+  return launched(launch_gemm_path(gemm_path(M, N), p, s));
 }
 
 int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t K, void* out,
@@ -388,7 +405,7 @@ int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t 
 
 size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
-  if (M <= 64) return 0;
+  if (M <= 64 || gemm_path(M, N) == 3) return 0;
   const size_t g = gemm_prefill_workspace_bytes(M, N, K);
   return g ? act_gemm_offset(M, K) + g : act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K);
 }
@@ -405,8 +422,11 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   if (weight_bytes_one(N, K) > kMaxBuf || gemm_scale_bytes(N, K) > kMaxBuf ||
       gemm_data_bytes(M, K) > kMaxBuf || gemm_scale_bytes(M, K) > kMaxBuf)
     return MXFP4_ERR_SHAPE;
-  // the small-M kernel addresses the row-major operands through 32-bit ranges
-  if (M > 0 && M <= 64 && ((M - 1) * ldq + K / 2 > kMaxBuf || (M - 1) * lds + K / 32 > kMaxBuf))
+  // the small-M kernel reads the row-major operands itself (M <= 64, or 64
+  // rows per launch), through 32-bit ranges
+  const bool rows_direct = M <= 64 || gemm_path(M, N) == 3;
+  const int64_t mr = M < 64 ? M : 64;
+  if (M > 0 && rows_direct && ((mr - 1) * ldq + K / 2 > kMaxBuf || (mr - 1) * lds + K / 32 > kMaxBuf))
     return MXFP4_ERR_SHAPE;
   const size_t need = mxfp4_linear_prequantized_workspace_bytes(M, N, K);
   if (workspace_bytes < need) return MXFP4_ERR_WORKSPACE;
@@ -439,15 +459,16 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   p.out_fp4 = 0;
   p.out_scales = nullptr;
   p.ldos = 0;
-  if (M <= 64) {
+  if (rows_direct) {
     // the small-M kernel gathers the row-major operands itself: one launch
+    // per 64 rows
     p.a = (const uint8_t*)x_fp4;
     p.as = (const uint8_t*)x_scales;
     p.a_rowmajor = 1;
     p.lda = (uint32_t)ldq;
     p.lds = (uint32_t)lds;
     p.scales_vec = lds % 16 == 0 && aligned(x_scales, 16) && (K / 32) % 16 == 0;
-    return launched(launch_gemm_decode(p, s));
+    return launched(launch_gemm_decode_rows(p, s));
   }
   // larger M: permute into the GEMM layouts in the workspace, then the GEMM
   uint8_t* q = (uint8_t*)workspace;

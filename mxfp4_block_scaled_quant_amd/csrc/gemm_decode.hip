@@ -761,6 +761,30 @@ hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream) {
   }
 }
 
+hipError_t launch_gemm_decode_rows(const GemmArgs& p0, hipStream_t stream) {
+  for (int r0 = 0; r0 < p0.M; r0 += 64) {
+    GemmArgs p = p0;
+    p.M = p0.M - r0 < 64 ? p0.M - r0 : 64;
+    if (p0.a_rowmajor) {
+      p.a = p0.a + (size_t)r0 * p0.lda;
+      p.as = p0.as + (size_t)r0 * p0.lds;
+    } else {
+      // 64 rows are four whole 16-row tiles of both GEMM layouts
+      p.a = p0.a + (size_t)(r0 / 16) * p0.Kt * 1024;
+      p.as = p0.as + (size_t)(r0 / 16) * p0.G * 256;
+    }
+    if (p0.out_fp4) {
+      p.out = (uint8_t*)p0.out + (size_t)r0 * p0.ldo;
+      p.out_scales = p0.out_scales + (size_t)r0 * p0.ldos;
+    } else {
+      p.out = (uint8_t*)p0.out + (size_t)r0 * p0.ldo * (p0.out_f32 ? 4 : 2);
+    }
+    const hipError_t e = launch_gemm_decode(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // Fused form (M <= 4): the K split of the one-row-tile decode kernel.
 template <int NS, int GPR>
 static hipError_t launch_linear_t(const GemmArgs& p, int kw, int gpw, hipStream_t stream) {

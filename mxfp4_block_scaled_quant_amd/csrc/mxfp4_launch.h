@@ -42,6 +42,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_decode(const GemmArgs& p, hipStream_t stream);
+// The small-M kernel over any M: one launch per 64 rows (rows 64c .. 64c+63
+// of the activations and the output), each as launch_gemm_decode of those
+// rows alone.
+hipError_t launch_gemm_decode_rows(const GemmArgs& p, hipStream_t stream);
 hipError_t launch_gemm_prefill(const GemmArgs& p, hipStream_t stream);
 // The large-M kernel's split (split-K) schedule of one launch: tiles [0, r)
 // cut into s K slices (r = 0: whole tiles); in the workspace, in this order:

@@ -94,6 +94,7 @@ def test_size_queries_reject_bad_shapes(lib):
     assert lib.mxfp4_scale_bytes(4, 64, 7) == 0
     assert lib.mxfp4_weight_bytes(0, 16, 64) == 0
     assert lib.mxfp4_gemm_workspace_bytes(16, 1024, 5120) == 0
+    assert lib.mxfp4_gemm_workspace_bytes(128, 8192, 14336) == 0       # 64 rows per small-M launch
 
 
 # Fake, suitably aligned addresses: every call below fails validation before
@@ -198,8 +199,14 @@ def test_shuffle_scales_and_prequantized_validation(lib):
     assert f(None, 4, 0, 128, None, None) == 0  # no rows
     g = lib.mxfp4_linear_prequantized
     assert lib.mxfp4_linear_prequantized_workspace_bytes(64, 96, 4128) == 0
-    need = lib.mxfp4_linear_prequantized_workspace_bytes(65, 96, 4128)
-    assert need >= L.weight_geometry(65, 4128)[2] + L.gemm_scale_geometry(65, 4128)[3]
+    # up to 256 rows on few columns (ceil(M/64) * N <= 16384) the small-M
+    # kernel reads the row-major operands itself, 64 rows per launch: no
+    # workspace
+    assert lib.mxfp4_linear_prequantized_workspace_bytes(128, 8192, 4128) == 0
+    assert lib.mxfp4_linear_prequantized_workspace_bytes(256, 4096, 4128) == 0
+    for M, N in [(257, 96), (65, 8208), (192, 6144)]:
+        need = lib.mxfp4_linear_prequantized_workspace_bytes(M, N, 4128)
+        assert need >= L.weight_geometry(M, 4128)[2] + L.gemm_scale_geometry(M, 4128)[3]
 
     def call(x=P, ldq=32, s=P, lds=2, w=P, ws=P, bias=None, out=P, ldo=16, dt=0, M=4, N=16, K=64,
              work=None, work_bytes=0):
@@ -209,7 +216,8 @@ def test_shuffle_scales_and_prequantized_validation(lib):
     assert call(K=48) == 2
     assert call(ldq=16) == 2          # ldq < K/2
     assert call(lds=1) == 2           # lds < K/32
-    assert call(M=65) == 4            # workspace missing
+    assert call(M=257) == 4           # workspace missing
+    assert call(M=65, N=8208, ldo=8208) == 4
     assert call(s=None) == 1
     assert call(ldq=40) == 3          # ldq % 16
     assert call(x=P_ODD) == 3

@@ -116,13 +116,13 @@ def test_linear_small_shapes(name, M, N, K, kw, path):
     _check(prob, y32, y16)
 
 
-@pytest.mark.parametrize("M", [17, 32, 33, 48, 49, 63, 65, 256])
+@pytest.mark.parametrize("M", [17, 32, 33, 48, 49, 63, 65, 128, 129, 193, 256])
 def test_linear_row_boundaries(M):
     # The automatic kernel choice on each side of its row boundaries: each
-    # row-tile count (16 rows) of the small-M kernel up to 64 rows, then the
-    # large-M kernel from 65 rows to one full 256-row tile (257 rows is a
-    # small-shape case above); 17 strips of 16 columns, a ragged last scale
-    # group and a ragged last K-step.
+    # row-tile count (16 rows) of the small-M kernel up to 64 rows, then (on
+    # these few columns) the small-M kernel once per 64 rows up to 256 rows
+    # (257 rows, the large-M kernel, is a small-shape case above); 17 strips
+    # of 16 columns, a ragged last scale group and a ragged last K-step.
     need_gpu()
     prob = inputs.linear_problem(M, 272, 1056, 11, outliers=True, with_bias=True)
     y32, y16 = _run(prob, 0)
@@ -260,6 +260,35 @@ def test_decode_group_rounds_same_bits(M):
     assert np.array_equal(y32[:, :5120].view(np.uint32), p32.view(np.uint32))
     assert np.array_equal(y16[:, :5120], p16)
     _check(prob, y32, y16, cols=_sample(N, 96, N))
+
+
+ROWS = [
+    # M, N, K, bias: up to 256 rows on few columns (ceil(M/64) * N <= 16384)
+    # run the small-M kernel once per 64 rows
+    (65, 4096, 4096, False),
+    (100, 1000, 5120, True),
+    (128, 8192, 8192, True),
+    (192, 4096, 4128, True),
+    (250, 2000, 1056, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,bias", ROWS, ids=[f"{m}x{n}x{k}" for m, n, k, _ in ROWS])
+def test_gemm_rows_per_launch(M, N, K, bias):
+    # bitwise the small-M kernel called on rows 0-63 and on the rest
+    # separately, and the oracle bar (sampled columns at the widest)
+    need_gpu()
+    w, W = _weight(N, K, 6)
+    b = inputs.bias(N, 6) if bias else None
+    x = inputs.activations(M, K, 6, outliers=True)
+    prob = {"x": x, "w": w, "bias": b}
+    y32, y16 = _run(prob, 0, weight=W)
+    for r0 in range(0, M, 64):
+        part = {"x": x[r0:r0 + 64], "w": w, "bias": b}
+        p32, p16 = _run(part, 0, weight=W)
+        assert np.array_equal(y32[r0:r0 + 64].view(np.uint32), p32.view(np.uint32)), r0
+        assert np.array_equal(y16[r0:r0 + 64], p16), r0
+    _check(prob, y32, y16, cols=_sample(N, 96, N) if N > 4096 else None)
 
 
 @pytest.mark.parametrize("N,K", NK, ids=[f"{n}x{k}" for n, k in NK])

@@ -84,6 +84,8 @@ CASES = [
     ("m16_16x32", 16, 16, 32, dict(seed=9), 0),
     ("m17_257x2080", 17, 257, 2080, dict(seed=10, outliers=True), 0),      # workspace + small-M
     ("m37_96x4128_edge_bias", 37, 96, 4128, dict(seed=5, edge=True, with_bias=True), 8),
+    ("m100_1000x5120_bias", 100, 1000, 5120, dict(seed=7, outliers=True, with_bias=True), 8),  # 64 rows per launch
+    ("m200_96x1056", 200, 96, 1056, dict(seed=8, edge=True), 0),
     ("m300_520x1056_bias", 300, 520, 1056, dict(seed=6, outliers=True, with_bias=True), 0),  # tiled
 ]
 

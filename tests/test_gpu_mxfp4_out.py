@@ -41,6 +41,9 @@ CASES = [
     ("smallM_1x64x640", 1, 64, 640, 1, dict(pads=(4, 3))),
     ("smallM_37x96x4128", 37, 96, 4128, 1, dict(seed=5, pads=(8, 1))),
     ("smallM_64x320x1056", 64, 320, 1056, 1, dict(bias=False)),
+    # up to 256 rows on few columns: the small-M kernel once per 64 rows
+    ("rows_100x512x1056", 100, 512, 1056, 0, dict(outliers=True, pads=(4, 5))),
+    ("rows_65x96x2080", 65, 96, 2080, 1, dict(seed=10)),
     ("tiled_300x512x1056", 300, 512, 1056, 2, dict(outliers=True, pads=(4, 5))),
     ("tiled256_300x512x1056", 300, 512, 1056, 3, dict(outliers=True, pads=(4, 5))),
     ("tiled_257x96x2080", 257, 96, 2080, 2, dict(seed=10)),

@@ -6,8 +6,9 @@ producer arrive as row-major packed FP4 + row-major E8M0 scales.
 * mxfp4_linear_prequantized: the oracle's GEMM tolerance, and bitwise the
   result of mxfp4_gemm_a4w4 on the same values in the GEMM layouts through
   the same kernel (small-M kernel reading the row-major operands directly
-  for M <= 64, in either of its forms; permutation into the workspace, then
-  the tiled kernel, above)."""
+  for M <= 64, in either of its forms, and once per 64 rows up to 256 rows
+  on few columns; permutation into the workspace, then the tiled kernel,
+  above)."""
 
 import numpy as np
 import pytest
@@ -52,7 +53,7 @@ CASES = [
     ("m16_520x1056_bias", 16, 520, 1056, dict(seed=6, outliers=True, with_bias=True), (0, 0)),
     ("m37_96x4128_edge", 37, 96, 4128, dict(seed=5, edge=True, with_bias=True), (32, 5)),
     ("m64_300x640", 64, 300, 640, dict(seed=6, with_bias=True), (0, 0)),
-    ("m65_257x2080", 65, 257, 2080, dict(seed=10, outliers=True), (16, 2)),      # tiled path
+    ("m65_257x2080", 65, 257, 2080, dict(seed=10, outliers=True), (16, 2)),      # 64 rows per launch
     ("m300_128x256_edge", 300, 128, 256, dict(seed=5, edge=True), (0, 0)),
     # one row tile, K > 8192: two strips and two groups per round past one
     # round of compute units (the byte scale loads even where the 16-byte
@@ -62,6 +63,9 @@ CASES = [
     ("m9_1000x8704_pad", 9, 1000, 8704, dict(seed=13, with_bias=True), (16, 1)),
     ("m40_300x10240", 40, 300, 10240, dict(seed=14, outliers=True, with_bias=True), (16, 16)),
     ("m64_96x14336_pad", 64, 96, 14336, dict(seed=15, with_bias=True), (0, 3)),
+    ("m129_1000x4128_pad", 129, 1000, 4128, dict(seed=16, outliers=True, with_bias=True), (16, 5)),  # 64 rows per launch
+    ("m200_4200x1056_pad", 200, 4200, 1056, dict(seed=18, with_bias=True), (16, 3)),  # tiled path
+    ("m128_8192x1056", 128, 8192, 1056, dict(seed=17, with_bias=True), (0, 0)),  # 64 rows per launch
 ]
 
 
@@ -75,8 +79,8 @@ def test_linear_prequantized(name, M, N, K, kw, pads):
     b = None if prob["bias"] is None else dev_bf16(prob["bias"])
     y32 = mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.float32)
     y16 = mx.mxfp4_linear_prequantized(xq, xs, W.w_pre, W.ws_pre, N, b, torch.bfloat16)
-    # the same values in the GEMM layouts through the same kernel
-    mx.set_gemm_path(1 if M <= 64 else 2)
+    # the same values in the GEMM layouts through the same kernel (and plan)
+    mx.set_gemm_path(1 if M <= 64 else 0)
     try:
         q, s = mx.mxfp4_quant_1x32(dev_bf16(prob["x"]), mx.MXFP4_LAYOUT_GEMM)
         r32 = mx.mxfp4_gemm_a4w4(q, s, W.w_pre, W.ws_pre, M, N, K, b, torch.float32)
