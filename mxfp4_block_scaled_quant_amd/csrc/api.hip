@@ -50,6 +50,21 @@ int gemm_path(int64_t M, int64_t N) {
   return c <= 4 && c * N <= 16384 ? 3 : 2;
 }
 
+// Row-major operands for the small-M kernel (per launch of up to 64 rows):
+// at three or four row tiles on long K every workgroup gathers all its rows
+// in 64-byte pieces, which costs more than permuting them once into the
+// GEMM layouts (one more launch).  Measured on MI355X (us, gathered ->
+// permuted first): K = 14336, N = 5120, M = 48 / 64 20.1 / 25.3 -> 18.1 /
+// 20.0; N = 14336, M = 32 / 64 29.8 / 48.9 -> 27.8 / 35.5; K = 8192,
+// N = 10240, M = 48 / 64 23.0 / 28.3 -> 19.7 / 22.6; but K = 8192,
+// N = 8192, M = 48 13.3 -> 14.5 and K = 14336, N = 5120, M = 32 15.0 ->
+// 16.8.
+bool prequant_permute(int64_t M, int64_t K) {
+  const int64_t rows = M < 64 ? M : 64;
+  const int64_t G = cdiv(cdiv(K, 128), 4);
+  return (rows > 48 && G > 12) || (rows > 32 && G > 16);
+}
+
 hipError_t launch_gemm_path(int path, const GemmArgs& p, hipStream_t s) {
   return path == 1 ? launch_gemm_decode(p, s) : path == 3 ? launch_gemm_decode_rows(p, s) : launch_gemm_prefill(p, s);
 }
@@ -405,7 +420,8 @@ int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t 
 
 size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
-  if (M <= 64 || gemm_path(M, N) == 3) return 0;
+  const int path = M <= 64 ? 1 : gemm_path(M, N);
+  if (path != 2) return prequant_permute(M, K) ? act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K) : 0;
   const size_t g = gemm_prefill_workspace_bytes(M, N, K);
   return g ? act_gemm_offset(M, K) + g : act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K);
 }
@@ -424,7 +440,8 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
     return MXFP4_ERR_SHAPE;
   // the small-M kernel reads the row-major operands itself (M <= 64, or 64
   // rows per launch), through 32-bit ranges
-  const bool rows_direct = M <= 64 || gemm_path(M, N) == 3;
+  const int path = M <= 64 ? 1 : gemm_path(M, N);
+  const bool rows_direct = path != 2 && !prequant_permute(M, K);
   const int64_t mr = M < 64 ? M : 64;
   if (M > 0 && rows_direct && ((mr - 1) * ldq + K / 2 > kMaxBuf || (mr - 1) * lds + K / 32 > kMaxBuf))
     return MXFP4_ERR_SHAPE;
@@ -470,7 +487,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
     p.scales_vec = lds % 16 == 0 && aligned(x_scales, 16) && (K / 32) % 16 == 0;
     return launched(launch_gemm_decode_rows(p, s));
   }
-  // larger M: permute into the GEMM layouts in the workspace, then the GEMM
+  // else: permute into the GEMM layouts in the workspace, then the GEMM
   uint8_t* q = (uint8_t*)workspace;
   uint8_t* sc = q + act_scales_offset(M, K);
   st = launched(launch_preshuffle_strided(x_fp4, ldq, x_scales, lds, 1, M, K, q, sc, s));
@@ -482,7 +499,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   p.scales_vec = 0;
   p.work = q + act_gemm_offset(M, K);
   p.work_bytes = workspace_bytes > act_gemm_offset(M, K) ? workspace_bytes - act_gemm_offset(M, K) : 0;
-  return launched(launch_gemm_prefill(p, s));
+  return launched(launch_gemm_path(path, p, s));
 }
 
 int a16wfp4_bmm(const void* x, int64_t sxb, int64_t sxm, const void* w_pre, const void* ws_pre,

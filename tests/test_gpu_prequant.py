@@ -7,8 +7,8 @@ producer arrive as row-major packed FP4 + row-major E8M0 scales.
   result of mxfp4_gemm_a4w4 on the same values in the GEMM layouts through
   the same kernel (small-M kernel reading the row-major operands directly
   for M <= 64, in either of its forms, and once per 64 rows up to 256 rows
-  on few columns; permutation into the workspace, then the tiled kernel,
-  above)."""
+  on few columns, except above 32 rows per launch on long K; permutation
+  into the workspace, then the GEMM kernel, otherwise)."""
 
 import numpy as np
 import pytest
@@ -66,6 +66,7 @@ CASES = [
     ("m129_1000x4128_pad", 129, 1000, 4128, dict(seed=16, outliers=True, with_bias=True), (16, 5)),  # 64 rows per launch
     ("m200_4200x1056_pad", 200, 4200, 1056, dict(seed=18, with_bias=True), (16, 3)),  # tiled path
     ("m128_8192x1056", 128, 8192, 1056, dict(seed=17, with_bias=True), (0, 0)),  # 64 rows per launch
+    ("m100_2000x8704_pad", 100, 2000, 8704, dict(seed=19, with_bias=True), (16, 3)),  # permuted, 64 rows per launch
 ]
 
 
