@@ -197,10 +197,11 @@ int mxfp4_gemm_a4w4(const void* a_fp4, const void* a_scales,
  * the FP4 GEMM, bias added after).  Same result as mxfp4_quant_1x32 (GEMM
  * layout) followed by mxfp4_gemm_a4w4:
  *   out[m, n] = round(sum_k dq(Q(x))[m,k] dq(W)[n,k] + bias[n]).
- * Where it is faster (M = 1; M <= 4 for N < 16384 and K <= 8192; for
- * N < 16384 and 8192 < K <= 16384, M = 2, or M <= 4 with N <= 4096; 2 <= M
- * <= 4 with 4608 < K <= 6144 and at least six 16-column weight strips per
- * compute unit) the quantisation runs inside the GEMM kernel: one launch, no
+ * Where it is faster (M = 1; M = 2 for K <= 16384; M <= 4 for N < 16384
+ * and K <= 8192, except M >= 3 for 8192 < N <= 12288; M <= 4 for N <= 4096
+ * and K <= 16384; 2 <= M <= 4 with 4608 < K <= 6144 and at least six
+ * 16-column weight strips per compute unit) the quantisation runs inside
+ * the GEMM kernel: one launch, no
  * quantised copy of x, bitwise the same output as the two-call form.
  * Otherwise x is quantised into `workspace` and the GEMM kernel for that M
  * then reads it.

@@ -13,9 +13,10 @@ Entry points (same names as the C ABI):
 * :func:`mxfp4_gemm_a4w4` -- W4A4 GEMM with optional bias, bf16/fp32 out
 * :func:`mxfp4_linear` -- bf16 activations -> quant + GEMM (+ bias) in one call,
   the quantisation fused into the GEMM kernel (one launch) at M = 1, at
-  M <= 4 where N < 16384 and K <= 8192 (up to K = 16384 at M = 2, or with
-  N <= 4096), and at 2 <= M <= 4 on wide N with 4608 < K <= 6144; otherwise
-  quantised into a workspace first (two launches)
+  M = 2 up to K = 16384, at M <= 4 where N < 16384 and K <= 8192 (but not
+  3-4 rows at 8192 < N <= 12288) or N <= 4096 and K <= 16384, and at
+  2 <= M <= 4 on wide N with 4608 < K <= 6144; otherwise quantised into a
+  workspace first (two launches)
 * :func:`mxfp4_gemm_a4w4_mxfp4_out` -- the GEMM writing MXFP4 (row-major FP4 +
   E8M0) for the next layer
 * :func:`mxfp4_shuffle_scales` -- row-major E8M0 scales -> the GEMM scale layout
@@ -288,10 +289,8 @@ def mxfp4_linear(x: torch.Tensor, w_pre: torch.Tensor, ws_pre: torch.Tensor, N: 
     """out[M, N] = round(dq(Q(x)) dq(W)^T (+ bias)) from bf16 x [M, K] (unit stride along K).
 
     ``workspace`` (uint8, >= :func:`linear_workspace_bytes` bytes) is
-    allocated here when needed and not given; the fused shapes (M = 1, and
-    M <= 4 where N < 16384 and K <= 8192, up to K = 16384 at M = 2 or
-    N <= 4096) need none (2 <= M <= 4 on wide N with 4608 < K <= 6144 is
-    fused too, and leaves it untouched).
+    allocated here when needed and not given; the fused shapes (see the
+    module docstring) need none and leave it untouched.
     """
     _require_cuda(x, "x")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:

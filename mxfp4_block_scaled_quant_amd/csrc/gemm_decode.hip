@@ -803,10 +803,17 @@ bool linear_fused_pays(int M, int N, int K) {
   // (K <= 16384) it still pays at M = 2, and up to M = 4 while the strips
   // fit in about one round of compute units (N <= 4096): K = 14336,
   // N = 4096, M = 2 / 4: 9.76 / 9.85 -> 7.56 / 8.86 us; N = 14336, M = 2:
-  // 22.36 -> 20.68 us; but N = 5120, M = 4: 11.63 -> 13.03 us.
+  // 22.36 -> 20.68 us; but N = 5120, M = 4: 11.63 -> 13.03 us.  On many
+  // strips (N >= 16384) only at M = 2 (K = 4096, N = 24576 / 28672:
+  // 12.45 / 13.62 -> 10.87 / 12.11 us; K = 8192, N = 20480: 17.44 ->
+  // 15.84), and not at M >= 3 between two and three strips per compute
+  // unit (N = 8192-12288), where the GEMM runs one strip per workgroup and
+  // the fused kernel two (K = 8192, N = 10240, M = 3 / 4: 12.57 / 13.00 ->
+  // 11.64 / 11.66 us through quantisation + GEMM).
   if (M < 1 || M > kFusedRows) return false;
   if (M == 1) return true;
-  if (N >= 16384) return false;
+  if (N >= 16384) return M == 2 && K <= 16384;
+  if (M >= 3 && N > 8192 && N <= 12288) return false;
   if (K <= 8192) return true;
   return K <= 16384 && (M == 2 || N <= 4096);
 }

@@ -40,11 +40,13 @@ def _linear(x_bits, W, N, bias_bits, ldx_pad=0):
 
 
 def _same_split(M, N, K):
-    """The fused kernel (M = 1; M <= 4 at N < 16384, K <= 8192; M = 2 at
-    N < 16384, K <= 16384; M <= 4 at N <= 4096, K <= 16384) splits K like
-    the small-M GEMM except beyond 16 scale groups (K > 8192)."""
+    """The fused kernel (M = 1; M = 2 at K <= 16384; M <= 4 at N < 16384,
+    K <= 8192, except M >= 3 at 8192 < N <= 12288; M <= 4 at N <= 4096,
+    K <= 16384) splits K like the small-M GEMM except beyond 16 scale
+    groups (K > 8192)."""
     wide_k = K <= 16384 and (M == 2 or N <= 4096)
-    fused = M == 1 or (M <= 4 and N < 16384 and (K <= 8192 or wide_k))
+    fused = M == 1 or (M <= 4 and N < 16384 and not (M >= 3 and 8192 < N <= 12288)
+                       and (K <= 8192 or wide_k)) or (M == 2 and K <= 16384)
     groups = -(-(-(-K // 128)) // 4)
     return not (fused and groups > 16)
 
@@ -225,17 +227,23 @@ def test_persistent_encoding_every_bf16_value():
         mx.set_gemm_path(0)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 8208, 5120), (2, 10240, 8192)], ids=["m1_8208x5120", "m2_10240x8192"])
-def test_linear_fused_one_strip_per_workgroup(M, N, K):
+WIDE = [(1, 8208, 5120), (2, 10240, 8192), (3, 10240, 5120), (2, 16400, 4096), (2, 20480, 8704)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE, ids=[f"m{m}_{n}x{k}" for m, n, k in WIDE])
+def test_linear_wide_shapes(M, N, K):
     # Between two and three strips per compute unit the fused kernel runs one
-    # strip per workgroup at M <= 2: bitwise quantisation + GEMM, and the
+    # strip per workgroup at M <= 2, and M >= 3 goes through quantisation +
+    # GEMM; on many strips M = 2 is fused (past 16 groups with its own K
+    # split): bitwise quantisation + GEMM where the K splits agree, and the
     # oracle bar on sampled columns.
     need_gpu()
     w, W = _weight(N, K, 5)
     b = inputs.bias(N, 5)
     x = inputs.activations(M, K, 5, outliers=True)
     y32, y16 = _linear(x, W, N, b)
-    r32, r16 = _two_launch(x, W, N, b)
-    assert np.array_equal(y32.view(np.uint32), r32.view(np.uint32))
-    assert np.array_equal(y16, r16)
+    if _same_split(M, N, K):
+        r32, r16 = _two_launch(x, W, N, b)
+        assert np.array_equal(y32.view(np.uint32), r32.view(np.uint32))
+        assert np.array_equal(y16, r16)
     _check({"x": x, "w": w, "bias": b}, y32, y16, cols=_sample(N, 96, N))
