@@ -285,10 +285,10 @@ int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t 
  * launch; bitwise the result of mxfp4_gemm_a4w4 on the same values in the
  * GEMM layouts), and so it does once per 64 rows where mxfp4_gemm_a4w4 runs
  * the small-M kernel per 64 rows (M <= 256, ceil(M/64) * N <= 16384) --
- * except with more than 32 rows per launch on long K (more than 48 rows
- * and K > 6144, or K > 8192), where they are first permuted into the GEMM
- * layouts in `workspace` (one more launch, faster there); for larger M
- * they are permuted into `workspace` first, then the tiled kernel runs.
+ * except with K > 4608 and more than 32 rows per launch, or more than 8
+ * with K > 6144 and N >= 10240, where they are first permuted into the
+ * GEMM layouts in `workspace` (one more launch, faster there); for larger
+ * M they are permuted into `workspace` first, then the tiled kernel runs.
  *
  *   x_fp4     packed FP4 [M, K/2], row stride ldq BYTES (ldq >= K/2,
  *             ldq % 16 == 0, 16-byte aligned)

@@ -51,18 +51,21 @@ int gemm_path(int64_t M, int64_t N) {
 }
 
 // Row-major operands for the small-M kernel (per launch of up to 64 rows):
-// at three or four row tiles on long K every workgroup gathers all its rows
-// in 64-byte pieces, which costs more than permuting them once into the
-// GEMM layouts (one more launch).  Measured on MI355X (us, gathered ->
-// permuted first): K = 14336, N = 5120, M = 48 / 64 20.1 / 25.3 -> 18.1 /
-// 20.0; N = 14336, M = 32 / 64 29.8 / 48.9 -> 27.8 / 35.5; K = 8192,
-// N = 10240, M = 48 / 64 23.0 / 28.3 -> 19.7 / 22.6; but K = 8192,
-// N = 8192, M = 48 13.3 -> 14.5 and K = 14336, N = 5120, M = 32 15.0 ->
-// 16.8.
-bool prequant_permute(int64_t M, int64_t K) {
+// every workgroup gathers all its rows in 64-byte pieces, which on long K
+// with many rows, or on many strips, costs more than permuting them once
+// into the GEMM layouts (one more launch, data and scales together).
+// Measured on MI355X (us, gathered -> permuted first): K = 5120, N = 10240 /
+// 14336, M = 48 16.5 / 14.7 -> 13.3 / 14.0; K = 8192, N = 28672, M = 16 /
+// 32 / 64 27.5 / 32.0 / 55.8 -> 26.0 / 27.7 / 37.6; N = 10240, M = 16
+// 13.4 -> 13.0; K = 14336, N = 5120, M = 48 / 64 20.0 / 25.1 -> 16.1 /
+// 17.9.  Not with K <= 4096 (N = 28672, M = 64: 20.0 -> 25.2), nor with
+// fewer rows on fewer strips (K = 8192, N = 8192, M = 16 / 32: 9.1 / 11.0
+// -> 10.6 / 11.8); the rule's worst miss is 0.36 us (K = 5120, N = 6144,
+// M = 48).
+bool prequant_permute(int64_t M, int64_t N, int64_t K) {
   const int64_t rows = M < 64 ? M : 64;
   const int64_t G = cdiv(cdiv(K, 128), 4);
-  return (rows > 48 && G > 12) || (rows > 32 && G > 16);
+  return G >= 10 && (rows > 32 || (rows > 8 && G > 12 && N >= 10240));
 }
 
 hipError_t launch_gemm_path(int path, const GemmArgs& p, hipStream_t s) {
@@ -421,7 +424,7 @@ int mxfp4_shuffle_scales(const void* scales, int64_t lds, int64_t rows, int64_t 
 size_t mxfp4_linear_prequantized_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
   const int path = M <= 64 ? 1 : gemm_path(M, N);
-  if (path != 2) return prequant_permute(M, K) ? act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K) : 0;
+  if (path != 2) return prequant_permute(M, N, K) ? act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K) : 0;
   const size_t g = gemm_prefill_workspace_bytes(M, N, K);
   return g ? act_gemm_offset(M, K) + g : act_scales_offset(M, K) + (size_t)gemm_scale_bytes(M, K);
 }
@@ -441,7 +444,7 @@ int mxfp4_linear_prequantized(const void* x_fp4, int64_t ldq, const void* x_scal
   // the small-M kernel reads the row-major operands itself (M <= 64, or 64
   // rows per launch), through 32-bit ranges
   const int path = M <= 64 ? 1 : gemm_path(M, N);
-  const bool rows_direct = path != 2 && !prequant_permute(M, K);
+  const bool rows_direct = path != 2 && !prequant_permute(M, N, K);
   const int64_t mr = M < 64 ? M : 64;
   if (M > 0 && rows_direct && ((mr - 1) * ldq + K / 2 > kMaxBuf || (mr - 1) * lds + K / 32 > kMaxBuf))
     return MXFP4_ERR_SHAPE;

@@ -16,13 +16,10 @@
 
 namespace mxfp4 {
 
-// One thread per 16-byte slot of the preshuffled data; source row (b, n) at
-// byte (b*N + n)*ldw.
-__global__ __launch_bounds__(256) void preshuffle_data_kernel(
-    const uint8_t* __restrict__ w, int64_t ldw, int N, int K, uint8_t* __restrict__ out, int Ns,
-    int Kt, int64_t total_slots) {
-  const int64_t slot = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (slot >= total_slots) return;
+// One 16-byte slot of the preshuffled data; source row (b, n) at byte
+// (b*N + n)*ldw.
+__device__ __forceinline__ void preshuffle_data_slot(const uint8_t* __restrict__ w, int64_t ldw, int N, int K,
+                                                     uint8_t* __restrict__ out, int Ns, int Kt, int64_t slot) {
   const int l = (int)(slot & 63);
   const int kb = l >> 4, r = l & 15;
   const int64_t unit = slot >> 6;
@@ -37,13 +34,10 @@ __global__ __launch_bounds__(256) void preshuffle_data_kernel(
   *reinterpret_cast<int4*>(out + slot * 16) = v;
 }
 
-// One thread per 4-byte scale dword of the GEMM scale layout (per batch);
-// source row (b, n) at byte (b*N + n)*lds.
-__global__ __launch_bounds__(256) void preshuffle_scale_kernel(
-    const uint8_t* __restrict__ ws, int64_t lds, int N, int K, uint8_t* __restrict__ out, int Ns,
-    int G, int64_t total_dwords) {
-  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (d >= total_dwords) return;
+// One 4-byte scale dword of the GEMM scale layout (per batch); source row
+// (b, n) at byte (b*N + n)*lds.
+__device__ __forceinline__ void preshuffle_scale_dword(const uint8_t* __restrict__ ws, int64_t lds, int N, int K,
+                                                       uint8_t* __restrict__ out, int Ns, int G, int64_t d) {
   const int l = (int)(d & 63);
   const int kb = l >> 4, r = l & 15;
   const int64_t unit = d >> 6;
@@ -64,6 +58,27 @@ __global__ __launch_bounds__(256) void preshuffle_scale_kernel(
   *reinterpret_cast<uint32_t*>(out + d * 4) = word;
 }
 
+// One thread per data slot, then one per scale dword: both permutations in
+// one launch (a launch costs about 2 us of fixed time at decode sizes).
+__global__ __launch_bounds__(256) void preshuffle_kernel(const uint8_t* __restrict__ w, int64_t ldw,
+                                                         const uint8_t* __restrict__ ws, int64_t lds, int N, int K,
+                                                         uint8_t* __restrict__ out, uint8_t* __restrict__ sout,
+                                                         int Ns, int Kt, int G, int64_t slots, int64_t dwords) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < slots)
+    preshuffle_data_slot(w, ldw, N, K, out, Ns, Kt, i);
+  else if (i - slots < dwords)
+    preshuffle_scale_dword(ws, lds, N, K, sout, Ns, G, i - slots);
+}
+
+// The scales alone.
+__global__ __launch_bounds__(256) void preshuffle_scale_kernel(const uint8_t* __restrict__ ws, int64_t lds, int N,
+                                                               int K, uint8_t* __restrict__ out, int Ns, int G,
+                                                               int64_t total_dwords) {
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (d < total_dwords) preshuffle_scale_dword(ws, lds, N, K, out, Ns, G, d);
+}
+
 hipError_t launch_preshuffle_strided(const void* w_fp4, int64_t ldw, const void* w_scales,
                                      int64_t lds, int64_t batch, int64_t N, int64_t K,
                                      void* w_out, void* ws_out, hipStream_t stream) {
@@ -73,10 +88,11 @@ hipError_t launch_preshuffle_strided(const void* w_fp4, int64_t ldw, const void*
   const int64_t slots = batch * Ns * (int64_t)Kt * 64;
   const int64_t dwords = batch * Ns * (int64_t)G * 64;
   if (w_fp4) {
-    preshuffle_data_kernel<<<dim3((unsigned)((slots + 255) / 256)), 256, 0, stream>>>(
-        (const uint8_t*)w_fp4, ldw, (int)N, (int)K, (uint8_t*)w_out, Ns, Kt, slots);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const int64_t total = slots + dwords;
+    preshuffle_kernel<<<dim3((unsigned)((total + 255) / 256)), 256, 0, stream>>>(
+        (const uint8_t*)w_fp4, ldw, (const uint8_t*)w_scales, lds, (int)N, (int)K, (uint8_t*)w_out,
+        (uint8_t*)ws_out, Ns, Kt, G, slots, dwords);
+    return hipGetLastError();
   }
   preshuffle_scale_kernel<<<dim3((unsigned)((dwords + 255) / 256)), 256, 0, stream>>>(
       (const uint8_t*)w_scales, lds, (int)N, (int)K, (uint8_t*)ws_out, Ns, G, dwords);

@@ -204,12 +204,13 @@ def test_shuffle_scales_and_prequantized_validation(lib):
     # workspace
     assert lib.mxfp4_linear_prequantized_workspace_bytes(128, 8192, 4128) == 0
     assert lib.mxfp4_linear_prequantized_workspace_bytes(256, 4096, 4128) == 0
-    # ... except at 33-64 rows per launch on long K, where the operands are
-    # permuted into the GEMM layouts first
+    # ... except with many rows per launch on long K, or on many strips,
+    # where the operands are permuted into the GEMM layouts first
     assert lib.mxfp4_linear_prequantized_workspace_bytes(32, 96, 14336) == 0
-    assert lib.mxfp4_linear_prequantized_workspace_bytes(48, 96, 6144) == 0
-    for M, K in [(64, 14336), (33, 8704), (100, 6656)]:
-        need = lib.mxfp4_linear_prequantized_workspace_bytes(M, 96, K)
+    assert lib.mxfp4_linear_prequantized_workspace_bytes(48, 96, 4096) == 0
+    assert lib.mxfp4_linear_prequantized_workspace_bytes(16, 8192, 8192) == 0
+    for M, N, K in [(64, 96, 14336), (33, 96, 8704), (100, 96, 6656), (48, 96, 5120), (16, 10240, 8192)]:
+        need = lib.mxfp4_linear_prequantized_workspace_bytes(M, N, K)
         assert need >= L.weight_geometry(M, K)[2] + L.gemm_scale_geometry(M, K)[3]
     for M, N in [(257, 96), (65, 8208), (192, 6144)]:
         need = lib.mxfp4_linear_prequantized_workspace_bytes(M, N, 4128)

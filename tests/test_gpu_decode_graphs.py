@@ -36,7 +36,8 @@ CASES = [
     # name, M, N, K, prequantised input
     ("persist_linear_m20", 20, 24576, 5120, False),
     ("persist_fused_m3", 3, 24576, 5120, False),
-    ("persist_rowmajor_m40", 40, 24576, 5120, True),
+    ("persist_rowmajor_m32", 32, 24576, 5120, True),
+    ("permuted_rowmajor_m48", 48, 24576, 5120, True),   # permuted into the GEMM layouts first
     ("one_round_m5", 5, 1000, 8704, False),
 ]
 
