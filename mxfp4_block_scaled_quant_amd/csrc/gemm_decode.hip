@@ -324,8 +324,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
 // wave, and reduce_store sums them in the same order: bitwise the same
 // output.  The reduction areas alternate between strips, so the one barrier
 // inside reduce_store also orders a strip's LDS reads before the writes two
-// strips later.
-template <int MT, int MAXW, int D, int ASRC>
+// strips later.  With MXFP4 output (NS = 2) a step is a pair of adjacent
+// strips (one 1x32 block per row), walked the same way, and
+// reduce_store_fp4 reduces it in one area: its second barrier already
+// orders every read of a step before the next step's writes.
+template <int MT, int MAXW, int D, int ASRC, int NS = 1>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
   constexpr bool AROW = ASRC == kASrcRow16 || ASRC == kASrcRow8;
   static_assert(ASRC != kASrcBf16 || MT == 1, "bf16 activations: one row tile");
@@ -405,23 +408,29 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
     }
   }
 
-  const int nk = (int)blockIdx.x < p.Ns ? (p.Ns - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-  int4 bf[D][4];
-  uint32_t sb[D], bb[D][1];
-  // Weights and scale of this wave's group of the k-th strip, and the bias
-  // of the strip's columns that reduce_store gives this thread, into ring
-  // slot `slot` (strips past the end load zeros).
-  auto issue = [&](int k, int4 (&b)[4], uint32_t& sc, uint32_t (&bias)[1]) {
-    const int s = (int)blockIdx.x + k * (int)gridDim.x;
-    const bool sv = k < nk && gv;
+  static_assert(NS == 1 || (NS == 2 && ASRC == kASrcGemm), "pairs of strips: MXFP4 output from the GEMM layout");
+  const int Nu = (p.Ns + NS - 1) / NS;  // steps of NS strips
+  const int nk = (int)blockIdx.x < Nu ? (Nu - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  int4 bf[D][NS][4];
+  uint32_t sb[D][NS], bb[D][NS];
+  // Weights and scale of this wave's group of the k-th step's strips, and
+  // the bias of their columns that the reduction gives this thread, into
+  // ring slot `slot` (strips past the end load zeros).
+  auto issue = [&](int k, int4 (&b)[NS][4], uint32_t (&sc)[NS], uint32_t (&bias)[NS]) {
+    const int s0 = ((int)blockIdx.x + k * (int)gridDim.x) * NS;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = g * 4 + u;
-      const uint32_t off = (sv && t < p.Kt) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
-      b[u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+    for (int j = 0; j < NS; ++j) {
+      const int s = s0 + j;
+      const bool sv = k < nk && gv && s < p.Ns;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = g * 4 + u;
+        const uint32_t off = (sv && t < p.Kt) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
+        b[j][u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+      }
+      sc[j] = buf_load4(rws, sv ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
     }
-    sc = buf_load4(rws, sv ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
-    load_bias<1>(p, k < nk ? s : p.Ns, bias);
+    load_bias<NS>(p, k < nk ? s0 : p.Ns, bias);
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, bf[d], sb[d], bb[d]);
@@ -442,24 +451,33 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
     for (int d = 0; d < D; ++d) {
       const int k = k0 + d;
       if (k >= nk) break;  // the same for every wave of the workgroup
-      v4f acc[MT][1];
+      v4f acc[MT][NS];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) acc[i][0] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          switch (u) {
-            case 0: acc[i][0] = mfma_sel<0>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
-            case 1: acc[i][0] = mfma_sel<1>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
-            case 2: acc[i][0] = mfma_sel<2>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
-            default: acc[i][0] = mfma_sel<3>(af[u][i], bf[d][u], sa[i], sb[d], acc[i][0]); break;
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            switch (u) {
+              case 0: acc[i][j] = mfma_sel<0>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
+              case 1: acc[i][j] = mfma_sel<1>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
+              case 2: acc[i][j] = mfma_sel<2>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
+              default: acc[i][j] = mfma_sel<3>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
+            }
           }
-        }
-      const uint32_t bias[1] = {bb[d][0]};
+      uint32_t bias[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) bias[j] = bb[d][j];
       issue(k + D, bf[d], sb[d], bb[d]);
-      reduce_store<MT, 1, MAXW>(reinterpret_cast<float*>(red) + (size_t)(k & 1) * kRedFloats, acc, p,
-                                (int)blockIdx.x + k * (int)gridDim.x, bias);
+      const int s0 = ((int)blockIdx.x + k * (int)gridDim.x) * NS;
+      if constexpr (NS == 2)
+        reduce_store_fp4<MT>(red, acc, p, s0, bias);
+      else
+        reduce_store<MT, 1, MAXW>(reinterpret_cast<float*>(red) + (size_t)(k & 1) * kRedFloats, acc, p, s0, bias);
     }
   }
   // the ring's last loads (past the end: zeros) land before the waves end
@@ -673,6 +691,16 @@ static bool decode_persist_pays_rowmajor(int M, int Ns, int cus, int kw) {
   return kw >= 10 && Ns >= 6 * cus;
 }
 
+// MXFP4 output: the persistent form in steps of two strips pays with more
+// than one row tile (measured, us, one-workgroup-per-two-strips form ->
+// persistent, K = 5120: N = 34816, M = 64 37.28 -> 32.74; N = 24576, M = 32 /
+// 64 19.03 / 24.48 -> 16.59 / 22.56; N = 14336, M = 64 16.40 -> 15.57), not
+// with one (N = 34816, M = 16: 19.89 -> 21.62; its ring holds one step,
+// as registers allow).
+static bool decode_persist_fp4_pays(int M, int Ns, int cus, int kw) {
+  return M > 16 && decode_persist_pays(M, Ns, cus, kw);
+}
+
 template <int MT, int MAXW>
 static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t stream) {
   // strips in flight per wave, as registers allow at 12 waves (six at one
@@ -686,6 +714,18 @@ static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t s
     gemm_decode_persist_kernel<MT, MAXW, D, kASrcRow8><<<grid, 64 * kw, lds, stream>>>(p);
   else
     gemm_decode_persist_kernel<MT, MAXW, D, kASrcGemm><<<grid, 64 * kw, lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+// MXFP4 output in the persistent form: steps of two strips (one 1x32
+// block per row), one reduction area (two barriers per step).
+template <int MT>
+static hipError_t launch_decode_persist_fp4(const GemmArgs& p, int kw, hipStream_t stream) {
+  constexpr int D = 1;  // steps in flight per wave (two strips each)
+  const int Nu = (p.Ns + 1) / 2;
+  const int grid = Nu < p.cus ? Nu : p.cus;
+  const size_t lds = (size_t)kw * MT * 2 * 64 * sizeof(v4f) + (size_t)MT * 16 * 32 * 2;
+  gemm_decode_persist_kernel<MT, 12, D, kASrcGemm, 2><<<grid, 64 * kw, lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -706,6 +746,10 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
       persist_ok && (ov == 7 || (ov != 8 && (p.a_rowmajor ? decode_persist_pays_rowmajor(p.M, p.Ns, p.cus, p.G)
                                                           : decode_persist_pays(p.M, p.Ns, p.cus, p.G))));
   if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
+  // MXFP4 output (GEMM-layout activations): the same form in steps of two
+  // strips
+  if (p.out_fp4 && !p.a_rowmajor && p.G <= 12 && (ov == 7 || (ov != 8 && decode_persist_fp4_pays(p.M, p.Ns, p.cus, p.G))))
+    return launch_decode_persist_fp4<MT>(p, p.G, stream);
   // one strip per workgroup never with MXFP4 output (a workgroup encodes
   // whole 32-column blocks)
   const bool one_round = p.Ns <= p.cus && !p.out_fp4;

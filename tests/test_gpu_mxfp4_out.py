@@ -41,6 +41,12 @@ CASES = [
     ("smallM_1x64x640", 1, 64, 640, 1, dict(pads=(4, 3))),
     ("smallM_37x96x4128", 37, 96, 4128, 1, dict(seed=5, pads=(8, 1))),
     ("smallM_64x320x1056", 64, 320, 1056, 1, dict(bias=False)),
+    # the small-M kernel's persistent form, in steps of two strips
+    ("persist_16x1024x5120", 16, 1024, 5120, 7, dict(seed=0, outliers=True)),
+    ("persist_1x64x640", 1, 64, 640, 7, dict(pads=(4, 3))),
+    ("persist_37x96x4128", 37, 96, 4128, 7, dict(seed=5, pads=(8, 1))),
+    ("persist_64x320x1056", 64, 320, 1056, 7, dict(bias=False)),
+    ("persist_20x8224x6144", 20, 8224, 6144, 7, dict(seed=3)),
     # up to 256 rows on few columns: the small-M kernel once per 64 rows
     ("rows_100x512x1056", 100, 512, 1056, 0, dict(outliers=True, pads=(4, 5))),
     ("rows_65x96x2080", 65, 96, 2080, 1, dict(seed=10)),
