@@ -328,14 +328,15 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
 // strips (one 1x32 block per row), walked the same way, and
 // reduce_store_fp4 reduces it in one area: its second barrier already
 // orders every read of a step before the next step's writes.
-template <int MT, int MAXW, int D, int ASRC, int NS = 1>
+template <int MT, int MAXW, int D, int ASRC, int NS = 1, int GPW = 1>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
   constexpr bool AROW = ASRC == kASrcRow16 || ASRC == kASrcRow8;
   static_assert(ASRC != kASrcBf16 || MT == 1, "bf16 activations: one row tile");
+  static_assert(GPW == 1 || (GPW == 2 && ASRC == kASrcGemm && NS == 1), "two groups per wave: GEMM layout, one strip");
   extern __shared__ v4f red[];
   constexpr size_t kRedFloats = reduce_lds_bytes<MT, 1, MAXW>() / sizeof(float);
   const int lane = threadIdx.x & 63;
-  const int g = threadIdx.x >> 6;  // this wave's scale group
+  const int g = (threadIdx.x >> 6) * GPW;  // this wave's (first) scale group
   const bool gv = g < p.G;
   const int nblk = p.K >> 5;
   const auto ra = make_rsrc(p.a, AROW ? (uint32_t)(p.M - 1) * p.lda + (uint32_t)(p.K >> 1)
@@ -350,8 +351,8 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
   // bf16 rows, each lane loads the whole 1x32 block its operand of K-step u
   // holds (row lane % 16, block (4g + u) * 4 + lane / 16: 64 bytes) and
   // encodes it below, once the weight ring is in flight.
-  int4 af[4][MT];
-  uint32_t sa[MT];
+  int4 af[GPW][4][MT];
+  uint32_t sa[GPW][MT];
   int4 xv[ASRC == kASrcBf16 ? 4 : 1][4];
   if constexpr (ASRC == kASrcBf16) {
     const auto rx = make_rsrc(p.x, p.x_bytes);
@@ -366,9 +367,11 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
     }
   }
 #pragma unroll
+  for (int q = 0; q < GPW; ++q)
+#pragma unroll
   for (int u = 0; u < 4 && ASRC != kASrcBf16; ++u) {
-    const int t = g * 4 + u;
-    const bool tv = gv && t < p.Kt;
+    const int t = (g + q) * 4 + u;
+    const bool tv = g + q < p.G && t < p.Kt;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       // rows past M are zero padding: skip their bytes
@@ -376,13 +379,15 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
       const bool rv = row < p.M;
       if constexpr (AROW) {
         const bool cv = t * 4 + (lane >> 4) < nblk;
-        af[u][i] = buf_load16(ra, (tv && rv && cv) ? (uint32_t)row * p.lda + (uint32_t)(t * 64 + (lane >> 4) * 16)
-                                                     : kOOB);
+        af[q][u][i] = buf_load16(ra, (tv && rv && cv) ? (uint32_t)row * p.lda + (uint32_t)(t * 64 + (lane >> 4) * 16)
+                                                        : kOOB);
       } else {
-        af[u][i] = buf_load16(ra, (tv && rv) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
+        af[q][u][i] = buf_load16(ra, (tv && rv) ? (uint32_t)((i * p.Kt + t) * 1024 + lane * 16) : kOOB);
       }
     }
   }
+#pragma unroll
+  for (int q = 0; q < GPW; ++q)
 #pragma unroll
   for (int i = 0; i < MT && ASRC != kASrcBf16; ++i) {
     if constexpr (AROW) {
@@ -402,34 +407,36 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
           word |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ras, off, 0, 0) << (8 * j);
         }
       }
-      sa[i] = word;
+      sa[q][i] = word;
     } else {
-      sa[i] = buf_load4(ras, gv ? (uint32_t)((i * p.G + g) * 256 + lane * 4) : kOOB);
+      sa[q][i] = buf_load4(ras, g + q < p.G ? (uint32_t)((i * p.G + g + q) * 256 + lane * 4) : kOOB);
     }
   }
 
   static_assert(NS == 1 || (NS == 2 && ASRC == kASrcGemm), "pairs of strips: MXFP4 output from the GEMM layout");
   const int Nu = (p.Ns + NS - 1) / NS;  // steps of NS strips
   const int nk = (int)blockIdx.x < Nu ? (Nu - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-  int4 bf[D][NS][4];
-  uint32_t sb[D][NS], bb[D][NS];
+  int4 bf[D][NS][GPW][4];
+  uint32_t sb[D][NS][GPW], bb[D][NS];
   // Weights and scale of this wave's group of the k-th step's strips, and
   // the bias of their columns that the reduction gives this thread, into
   // ring slot `slot` (strips past the end load zeros).
-  auto issue = [&](int k, int4 (&b)[NS][4], uint32_t (&sc)[NS], uint32_t (&bias)[NS]) {
+  auto issue = [&](int k, int4 (&b)[NS][GPW][4], uint32_t (&sc)[NS][GPW], uint32_t (&bias)[NS]) {
     const int s0 = ((int)blockIdx.x + k * (int)gridDim.x) * NS;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int s = s0 + j;
-      const bool sv = k < nk && gv && s < p.Ns;
+    for (int j = 0; j < NS; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = g * 4 + u;
-        const uint32_t off = (sv && t < p.Kt) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
-        b[j][u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+      for (int q = 0; q < GPW; ++q) {
+        const int s = s0 + j;
+        const bool sv = k < nk && g + q < p.G && s < p.Ns;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = (g + q) * 4 + u;
+          const uint32_t off = (sv && t < p.Kt) ? (uint32_t)((s * p.Kt + t) * 1024 + lane * 16) : kOOB;
+          b[j][q][u] = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kAuxNT));
+        }
+        sc[j][q] = buf_load4(rws, sv ? (uint32_t)((s * p.G + g + q) * 256 + lane * 4) : kOOB);
       }
-      sc[j] = buf_load4(rws, sv ? (uint32_t)((s * p.G + g) * 256 + lane * 4) : kOOB);
-    }
     load_bias<NS>(p, k < nk ? s0 : p.Ns, bias);
   };
 #pragma unroll
@@ -437,12 +444,12 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
   if constexpr (ASRC == kASrcBf16) {
     // the encoding waits for x only: the ring's loads stay in flight
     __builtin_amdgcn_sched_barrier(0);
-    sa[0] = 0;
+    sa[0][0] = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       uint32_t b;
-      af[u][0] = quant_block32(xv[u], b);
-      sa[0] |= b << (8 * u);
+      af[0][u][0] = quant_block32(xv[u], b);
+      sa[0][0] |= b << (8 * u);
     }
   }
 
@@ -457,18 +464,22 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int q = 0; q < GPW; ++q)
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            switch (u) {
-              case 0: acc[i][j] = mfma_sel<0>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
-              case 1: acc[i][j] = mfma_sel<1>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
-              case 2: acc[i][j] = mfma_sel<2>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
-              default: acc[i][j] = mfma_sel<3>(af[u][i], bf[d][j][u], sa[i], sb[d][j], acc[i][j]); break;
+          for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+              const int4& av = af[q][u][i];
+              const int4& wv4 = bf[d][j][q][u];
+              switch (u) {
+                case 0: acc[i][j] = mfma_sel<0>(av, wv4, sa[q][i], sb[d][j][q], acc[i][j]); break;
+                case 1: acc[i][j] = mfma_sel<1>(av, wv4, sa[q][i], sb[d][j][q], acc[i][j]); break;
+                case 2: acc[i][j] = mfma_sel<2>(av, wv4, sa[q][i], sb[d][j][q], acc[i][j]); break;
+                default: acc[i][j] = mfma_sel<3>(av, wv4, sa[q][i], sb[d][j][q], acc[i][j]); break;
+              }
             }
-          }
       uint32_t bias[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) bias[j] = bb[d][j];
@@ -717,6 +728,36 @@ static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t s
   return hipGetLastError();
 }
 
+// The persistent form with two scale groups per wave (13-24 groups, one or
+// two row tiles, GEMM-layout activations, bf16 / fp32 output), on at least
+// five strips per compute unit.  Measured on MI355X (us, streaming ->
+// persistent, N = 28672): K = 6656 / 7680 / 8704 / 10240 / 11264, M = 16:
+// 21.5 / 23.4 / 26.7 / 30.2 / 29.6 -> 21.0 / 22.4 / 25.1 / 27.0 / 29.1;
+// M = 32: 22.3 / 24.5 / 32.0 / 31.7 / 34.4 -> 20.6 / 22.6 / 27.0 / 29.6 /
+// 31.6; K = 12288, M = 32: 36.5 -> 33.5.  Not at M <= 8 (K = 8192, N =
+// 28672, M = 1 / 8: 20.1 / 20.6 -> 23.1 / 24.1), nor at M <= 16 with many
+// strips per unit (N = 57344, K = 7168: 39.9 -> 41.6), nor at 16 groups
+// below 25 rows, where the streaming form's 16 waves of one group do well
+// (N = 28672, K = 8192, M = 16 / 24: 23.6 / 23.6 -> 24.5 / 24.0).
+static bool decode_persist2_pays(int M, int Ns, int cus, int G) {
+  if (Ns < 5 * cus) return false;
+  if (M > 16) return G != 16 || M > 24;
+  if (M > 8) return Ns <= 8 * cus && G != 16;
+  return false;
+}
+
+template <int MT>
+static hipError_t launch_decode_persist2(const GemmArgs& p, hipStream_t stream) {
+  const int kw = (p.G + 1) / 2;
+  const int grid = p.Ns < p.cus ? p.Ns : p.cus;
+  if (kw <= 8) {
+    gemm_decode_persist_kernel<MT, 8, 2, kASrcGemm, 1, 2><<<grid, 64 * kw, 2 * reduce_lds_bytes<MT, 1, 8>(), stream>>>(p);
+  } else {
+    gemm_decode_persist_kernel<MT, 12, 1, kASrcGemm, 1, 2><<<grid, 64 * kw, 2 * reduce_lds_bytes<MT, 1, 12>(), stream>>>(p);
+  }
+  return hipGetLastError();
+}
+
 // MXFP4 output in the persistent form: steps of two strips (one 1x32
 // block per row), one reduction area (two barriers per step).
 template <int MT>
@@ -746,6 +787,11 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
       persist_ok && (ov == 7 || (ov != 8 && (p.a_rowmajor ? decode_persist_pays_rowmajor(p.M, p.Ns, p.cus, p.G)
                                                           : decode_persist_pays(p.M, p.Ns, p.cus, p.G))));
   if (persist) return launch_decode_persist<MT, 12>(p, p.G, stream);
+  if constexpr (MT <= 2) {
+    if (p.G > 12 && p.G <= 24 && !p.out_fp4 && !p.a_rowmajor &&
+        (ov == 7 || (ov != 8 && decode_persist2_pays(p.M, p.Ns, p.cus, p.G))))
+      return launch_decode_persist2<MT>(p, stream);
+  }
   // MXFP4 output (GEMM-layout activations): the same form in steps of two
   // strips
   if (p.out_fp4 && !p.a_rowmajor && p.G <= 12 && (ov == 7 || (ov != 8 && decode_persist_fp4_pays(p.M, p.Ns, p.cus, p.G))))

@@ -164,15 +164,27 @@ PERSIST = [
     ("41x4100x6144", 41, 4100, 6144),
     ("64x2064x6144", 64, 2064, 6144),
     ("64x34816x5120", 64, 34816, 5120),
+    # 13-24 groups at one or two row tiles: two groups per wave
+    ("1x1040x8192", 1, 1040, 8192),
+    ("9x17x6656", 9, 17, 6656),
+    ("16x5000x12288", 16, 5000, 12288),
+    ("20x2064x8704", 20, 2064, 8704),
+    ("32x4100x7168", 32, 4100, 7168),
 ]
 
 
 def _same_k_split(M, K):
     # the streaming form's groups per wave (at most 16 / 8 / 8 / 12 waves for
-    # one to four row tiles) is one, as in the persistent form
+    # one to four row tiles) is that of the persistent form: one up to 12
+    # groups, two for 13-24 groups at one or two row tiles (beyond that the
+    # persistent form does not apply and both calls stream)
     mt = -(-M // 16)
     groups = -(-(-(-K // 128)) // 4)
-    return groups <= (16 if mt == 1 else 12 if mt == 4 else 8)
+    if groups <= 12:
+        return groups <= (16 if mt == 1 else 12 if mt == 4 else 8)
+    if groups > 24 or mt > 2:
+        return True
+    return groups > 16 if mt == 1 else groups <= 16
 
 
 @pytest.mark.parametrize("name,M,N,K", PERSIST, ids=[c[0] for c in PERSIST])
