@@ -773,7 +773,12 @@ static hipError_t launch_decode_persist_fp4(const GemmArgs& p, int kw, hipStream
 template <int MT>
 static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   constexpr int MAXW = MT == 1 ? 16 : MT == 4 ? 12 : 8;
-  const int gpw = (p.G + MAXW - 1) / MAXW;
+  // (29-32 groups at 9-16 rows on many strips: three groups per wave in at
+  // most 11 waves, as 16 waves of two leave a compute unit one workgroup at
+  // a time — K = 16384, M = 16, N = 16384 / 24576 / 32768: 27.3 / 38.8 /
+  // 50.2 -> 24.1 / 34.4 / 45.1 us; K = 15360, N = 16384: 23.3 -> 22.8)
+  const bool three = MT == 1 && p.M > 8 && p.G > 28 && p.G <= 32 && p.Ns >= 4 * p.cus;
+  const int gpw = three ? (p.G + 11) / 12 : (p.G + MAXW - 1) / MAXW;
   const int kw = (p.G + gpw - 1) / gpw;
   // persistent form: one group per wave, bf16 / fp32 output, activations in
   // the GEMM layout or row-major (path 7 of the test hook forces it where it

@@ -253,6 +253,19 @@ def test_decode_sweep_full_size(N, K):
         _check(prob, y32, y16, cols=cols)
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 16400, 16384), (12, 16400, 15360)], ids=["16x16400x16384", "12x16400x15360"])
+def test_decode_three_groups_per_wave(M, N, K):
+    # 29-32 groups at 9-16 rows on many strips: three groups per wave; the
+    # oracle bar on sampled columns
+    need_gpu()
+    w, W = _weight(N, K, 7)
+    b = inputs.bias(N, 7)
+    x = inputs.activations(M, K, 7, outliers=True)
+    prob = {"x": x, "w": w, "bias": b}
+    y32, y16 = _run(prob, 0, weight=W)
+    _check(prob, y32, y16, cols=_sample(N, 96, N))
+
+
 @pytest.mark.parametrize("M", [1, 16])
 def test_decode_group_rounds_same_bits(M):
     # More than 16 scale groups at one row tile: with 513 strips (two-strip
