@@ -680,6 +680,10 @@ static hipError_t launch_decode_t(const GemmArgs& p, int kw, int gpw, hipStream_
 // compute unit); with fewer waves too (K = 4096, N = 16384: 12-19% slower
 // up to M = 48, 2% faster at 64).
 static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
+  // (at four row tiles eight waves suffice on six strips per unit: K = 4096,
+  // M = 64, N = 24576 / 32768 / 57344: 17.8 / 22.9 / 38.0 -> 16.2 / 19.7 /
+  // 30.9 us)
+  if (kw >= 8 && kw < 10 && M > 48) return Ns >= 6 * cus;
   if (kw < 10 || M <= 8) return false;
   if (M > 48) return Ns >= 3 * cus;
   if (M > 16) return Ns >= 6 * cus;
@@ -740,9 +744,17 @@ static hipError_t launch_decode_persist(const GemmArgs& p, int kw, hipStream_t s
 // below 25 rows, where the streaming form's 16 waves of one group do well
 // (N = 28672, K = 8192, M = 16 / 24: 23.6 / 23.6 -> 24.5 / 24.0).
 static bool decode_persist2_pays(int M, int Ns, int cus, int G) {
-  if (Ns < 5 * cus) return false;
-  if (M > 16) return G != 16 || M > 24;
-  if (M > 8) return Ns <= 8 * cus && G != 16;
+  // Two row tiles between two and three strips per unit, where two-strip
+  // workgroups leave some units four strips and the persistent walk at most
+  // three: K = 11008, M = 24, N = 10240 / 11264: 17.3 / 17.6 -> 14.8 / 15.2
+  // us; K = 8192, N = 10240, M = 32: 13.3 -> 12.3; at exactly three (N =
+  // 12288) only with 18 or more groups (K = 11008, M = 24: 18.0 -> 15.8;
+  // K = 8192, M = 20: 13.07 -> 13.20); not at two (N = 8192, K = 8192: 8.9
+  // -> 10.4) nor at 3.25-4 (N = 13312, K = 9216: 15.0 -> 15.9).
+  if (M > 16)
+    return (Ns > 2 * cus && (Ns < 3 * cus || (Ns == 3 * cus && G >= 18))) ||
+           (Ns >= 5 * cus && (G != 16 || M > 24));
+  if (M > 8) return Ns >= 5 * cus && Ns <= 8 * cus && G != 16;
   return false;
 }
 
