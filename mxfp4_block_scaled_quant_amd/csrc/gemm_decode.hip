@@ -683,8 +683,14 @@ static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
   // (at four row tiles eight waves suffice on six strips per unit: K = 4096,
   // M = 64, N = 24576 / 32768 / 57344: 17.8 / 22.9 / 38.0 -> 16.2 / 19.7 /
   // 30.9 us)
-  if (kw >= 8 && kw < 10 && M > 48) return Ns >= 6 * cus;
+  if (kw >= 8 && kw < 10 && M > 48) return Ns >= 6 * cus || (Ns > 2 * cus && Ns < 3 * cus);
   if (kw < 10 || M <= 8) return false;
+  // (and from two row tiles between two and three strips per unit, where
+  // two-strip workgroups leave some units four: N = 10240, K = 5120, M =
+  // 20 / 32 / 40 / 64: 9.3 / 9.7 / 10.5 / 13.3 -> 9.0 / 9.1 / 10.1 / 10.8
+  // us; N = 11264, K = 6144, M = 20 / 64: 10.8 / 14.6 -> 10.1 / 12.2; with
+  // 8 waves (K = 4096) only at M = 64: 11.3 -> 9.8)
+  if (M > 16 && Ns > 2 * cus && Ns < 3 * cus) return true;
   if (M > 48) return Ns >= 3 * cus;
   if (M > 16) return Ns >= 6 * cus;
   return Ns >= 7 * cus;
