@@ -692,7 +692,9 @@ static bool decode_persist_pays(int M, int Ns, int cus, int kw) {
   // 8 waves (K = 4096) only at M = 64: 11.3 -> 9.8)
   if (M > 16 && Ns > 2 * cus && Ns < 3 * cus) return true;
   if (M > 48) return Ns >= 3 * cus;
-  if (M > 16) return Ns >= 6 * cus;
+  // (between four and five strips per unit, too: K = 5120, N = 18432, M =
+  // 20 / 32 / 48: 13.6 / 14.2 / 15.7 -> 12.9 / 13.2 / 14.8 us)
+  if (M > 16) return Ns > 4 * cus;
   return Ns >= 7 * cus;
 }
 
@@ -718,8 +720,12 @@ static bool decode_persist_pays_rowmajor(int M, int Ns, int cus, int kw) {
 // 64 19.03 / 24.48 -> 16.59 / 22.56; N = 14336, M = 64 16.40 -> 15.57), not
 // with one (N = 34816, M = 16: 19.89 -> 21.62; its ring holds one step,
 // as registers allow).
+// (Steps of two strips are what the streaming form's workgroups hold, so
+// the persistent walk evens nothing out there: the rule measured before
+// the balance cases above.)
 static bool decode_persist_fp4_pays(int M, int Ns, int cus, int kw) {
-  return M > 16 && decode_persist_pays(M, Ns, cus, kw);
+  if (M <= 16 || kw < 10) return false;
+  return M > 48 ? Ns >= 3 * cus : Ns >= 6 * cus;
 }
 
 template <int MT, int MAXW>
