@@ -839,7 +839,11 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   // M = 1 / 16: 7.93 / 8.66 -> 6.92 / 7.83.  Where both forms give each unit
   // the same number of strips two per workgroup share the activations:
   // N = 6144 and 14336 stay, 0.3-0.8 us faster at M = 16)
-  const bool balance = MT == 1 && p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus;
+  // The same between four and four and a half strips per unit at 9-16 rows
+  // (K = 5120 / 8192 / 14336, N = 18432, M = 16: 11.9 / 17.4 / 28.0 ->
+  // 11.3 / 16.1 / 27.4 us; neutral at 4.75, slower at exactly five).
+  const bool balance = MT == 1 && ((p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus) ||
+                                   (p.Ns > 4 * p.cus && 2 * p.Ns <= 9 * p.cus));
   const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k || balance) && !p.out_fp4;
   if constexpr (MT == 1) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
