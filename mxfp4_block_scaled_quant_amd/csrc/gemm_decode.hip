@@ -841,9 +841,12 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   // N = 6144 and 14336 stay, 0.3-0.8 us faster at M = 16)
   // The same between four and four and a half strips per unit at 9-16 rows
   // (K = 5120 / 8192 / 14336, N = 18432, M = 16: 11.9 / 17.4 / 28.0 ->
-  // 11.3 / 16.1 / 27.4 us; neutral at 4.75, slower at exactly five).
+  // 11.3 / 16.1 / 27.4 us; neutral at 4.75, slower at exactly five), and
+  // between six and six and a half with at most 16 groups (K = 8192,
+  // N = 25088, M = 9 / 16: 22.2 / 22.3 -> 20.8 / 21.3; at K = 14336 slower).
   const bool balance = MT == 1 && ((p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus) ||
-                                   (p.Ns > 4 * p.cus && 2 * p.Ns <= 9 * p.cus));
+                                   (p.Ns > 4 * p.cus && 2 * p.Ns <= 9 * p.cus) ||
+                                   (p.G <= 16 && p.Ns > 6 * p.cus && 2 * p.Ns <= 13 * p.cus));
   const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k || balance) && !p.out_fp4;
   if constexpr (MT == 1) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
