@@ -964,9 +964,15 @@ hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
     return (p.Ns >= 1024 || p.Ns <= p.cus || balance) ? launch_linear_t<1, 1>(p, kw, 1, stream)
                                                       : launch_linear_t<2, 1>(p, kw, 1, stream);
   }
-  const int gpw = (p.G + 7) / 8;
+  // From 20 groups on, at most 12 waves (two or three groups each, the
+  // latter one per round) beat 8 waves of three or four: K = 14336, M = 1,
+  // N = 5120 / 8192 / 14336: 10.71 / 12.52 / 19.82 -> 10.45 / 11.74 /
+  // 19.06 us; K = 10240, N = 2048: 5.82 -> 5.21 (at 17 groups, K = 8704,
+  // N = 20480, 8 waves stay: 19.52 against 20.22).
+  const int gpw = p.G >= 20 ? (p.G + 11) / 12 : (p.G + 7) / 8;
   const int kw = (p.G + gpw - 1) / gpw;
-  return launch_linear_t<1, 2>(p, kw, gpw, stream);
+  return (p.G >= 20 && gpw == 3) ? launch_linear_t<1, 1>(p, kw, gpw, stream)
+                                 : launch_linear_t<1, 2>(p, kw, gpw, stream);
 }
 // Fused quantisation in the persistent form (M <= 16, at most 12 scale
 // groups): each wave encodes its group's blocks of the 16 rows once.  The
