@@ -957,10 +957,12 @@ hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
   // where each workgroup's re-encoding of x is cheap (M <= 2: K = 5120,
   // N = 10240 / 12288, M = 1: 8.83 / 9.08 -> 7.27 / 7.78 us; K = 8192,
   // N = 10240, M = 1 / 2: 11.81 / 12.15 -> 9.63 / 10.20; at M = 4 mixed,
-  // N = 12288: 9.85 -> 10.59).
+  // N = 12288: 9.85 -> 10.59).  At M = 1 one strip everywhere (one row to
+  // encode): K = 5120, N = 13312 / 14336: 9.20 / 9.44 -> 8.52 / 8.74 us;
+  // K = 8192, N = 14336: 13.07 -> 12.13.
   if (p.G <= 16) {
     const int kw = p.G;
-    const bool balance = p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus && p.M <= 2;
+    const bool balance = (p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus && p.M <= 2) || p.M == 1;
     return (p.Ns >= 1024 || p.Ns <= p.cus || balance) ? launch_linear_t<1, 1>(p, kw, 1, stream)
                                                       : launch_linear_t<2, 1>(p, kw, 1, stream);
   }
