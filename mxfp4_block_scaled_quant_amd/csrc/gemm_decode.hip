@@ -847,7 +847,11 @@ static hipError_t launch_decode_mt(const GemmArgs& p, hipStream_t stream) {
   const bool balance = MT == 1 && ((p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus) ||
                                    (p.Ns > 4 * p.cus && 2 * p.Ns <= 9 * p.cus) ||
                                    (p.G <= 16 && p.Ns > 6 * p.cus && 2 * p.Ns <= 13 * p.cus));
-  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k || balance) && !p.out_fp4;
+  // (and at M <= 4 up to 16 groups from two strips per unit: K = 8192,
+  // N = 8192 / 14336, M = 1: 7.95 / 12.64 -> 7.66 / 12.03 us; K = 5120,
+  // N = 8192: 6.01 -> 5.83; neutral at N = 13312-14336, K = 5120)
+  const bool few_rows = MT == 1 && p.M <= 4 && p.G <= 16 && p.Ns >= 2 * p.cus;
+  const bool one_strip = ((p.Ns >= 1024 && p.M <= 8) || one_round || small_k || balance || few_rows) && !p.out_fp4;
   if constexpr (MT == 1) {
     if (one_round && p.G > 16 && p.G <= 32) return launch_decode_t<1, 1, 4, 8>(p, (p.G + 3) / 4, 4, stream);
     // (row-major activations: one group per round, so the 16-byte scale
