@@ -331,7 +331,6 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_kernel(GemmArgs p, int 
 template <int MT, int MAXW, int D, int ASRC, int NS = 1, int GPW = 1>
 __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs p) {
   constexpr bool AROW = ASRC == kASrcRow16 || ASRC == kASrcRow8;
-  static_assert(ASRC != kASrcBf16 || MT == 1, "bf16 activations: one row tile");
   static_assert(GPW == 1 || (GPW == 2 && ASRC == kASrcGemm && NS == 1), "two groups per wave: GEMM layout, one strip");
   extern __shared__ v4f red[];
   constexpr size_t kRedFloats = reduce_lds_bytes<MT, 1, MAXW>() / sizeof(float);
@@ -349,22 +348,24 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
   // This wave's activation operands and scales, as gemm_decode_kernel reads
   // them (from the GEMM layout, or gathered from the row-major form); from
   // bf16 rows, each lane loads the whole 1x32 block its operand of K-step u
-  // holds (row lane % 16, block (4g + u) * 4 + lane / 16: 64 bytes) and
-  // encodes it below, once the weight ring is in flight.
+  // in row tile i holds (row 16i + lane % 16, block (4g + u) * 4 + lane / 16:
+  // 64 bytes) and encodes it below: the first tile once the weight ring is
+  // in flight, the others after it, two blocks at a time (registers).
   int4 af[GPW][4][MT];
   uint32_t sa[GPW][MT];
   int4 xv[ASRC == kASrcBf16 ? 4 : 1][4];
+  [[maybe_unused]] const auto rx = make_rsrc(p.x, ASRC == kASrcBf16 ? p.x_bytes : 0u);
+  [[maybe_unused]] auto load_x = [&](int i, int u, int4 (&v)[4]) {
+    const int row = i * 16 + (lane & 15);
+    const int kb = (g * 4 + u) * 4 + (lane >> 4);
+    const bool ok = gv && row < p.M && kb < nblk;
+    const uint32_t off = (uint32_t)row * (uint32_t)p.ldx * 2u + (uint32_t)kb * 64u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = buf_load16(rx, ok ? off + (uint32_t)c * 16u : kOOB);
+  };
   if constexpr (ASRC == kASrcBf16) {
-    const auto rx = make_rsrc(p.x, p.x_bytes);
-    const int row = lane & 15;
-    const bool rv = gv && row < p.M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kb = (g * 4 + u) * 4 + (lane >> 4);
-      const uint32_t off = (uint32_t)row * (uint32_t)p.ldx * 2u + (uint32_t)kb * 64u;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) xv[u][c] = buf_load16(rx, (rv && kb < nblk) ? off + (uint32_t)c * 16u : kOOB);
-    }
+    for (int u = 0; u < 4; ++u) load_x(0, u, xv[u]);
   }
 #pragma unroll
   for (int q = 0; q < GPW; ++q)
@@ -442,7 +443,8 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d, bf[d], sb[d], bb[d]);
   if constexpr (ASRC == kASrcBf16) {
-    // the encoding waits for x only: the ring's loads stay in flight
+    // the first tile's encoding waits for x only: the ring's loads stay in
+    // flight (the later tiles' loads queue behind them)
     __builtin_amdgcn_sched_barrier(0);
     sa[0][0] = 0;
 #pragma unroll
@@ -450,6 +452,24 @@ __global__ __launch_bounds__(64 * MAXW) void gemm_decode_persist_kernel(GemmArgs
       uint32_t b;
       af[0][u][0] = quant_block32(xv[u], b);
       sa[0][0] |= b << (8 * u);
+    }
+#pragma unroll
+    for (int i = 1; i < MT; ++i) {
+      sa[0][i] = 0;
+#pragma unroll
+      for (int h = 0; h < 4; h += 2) {
+        // one pair of blocks in registers at a time (no load hoisted above)
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(i, h, xv[0]);
+        load_x(i, h + 1, xv[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          uint32_t b;
+          af[0][h + u][i] = quant_block32(xv[u], b);
+          sa[0][i] |= b << (8 * (h + u));
+        }
+      }
     }
   }
 
@@ -980,13 +1000,15 @@ hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
   return (p.G >= 20 && gpw == 3) ? launch_linear_t<1, 1>(p, kw, gpw, stream)
                                  : launch_linear_t<1, 2>(p, kw, gpw, stream);
 }
-// Fused quantisation in the persistent form (M <= 16, at most 12 scale
-// groups): each wave encodes its group's blocks of the 16 rows once.  The
-// same operands, K split and order as quantisation + the persistent GEMM,
-// so the same bits.
+// Fused quantisation in the persistent form (M <= 32: one or two row
+// tiles, at most 12 scale groups): each wave encodes its group's blocks of
+// the rows once.  The same operands, K split and order as quantisation +
+// the persistent GEMM, so the same bits.  (Three or four tiles of encoded
+// operands beside the weight ring spill at the 12-wave register budget, so
+// those forms are not built.)
 bool linear_persist_applies(int M, int K, int64_t x_bytes) {
   const int G = (K / 32 + 15) / 16;
-  return M >= 1 && M <= 16 && G <= 12 && x_bytes <= (int64_t)0x7FFFFFFF;  // 31-bit buffer offsets
+  return M >= 1 && M <= 32 && G <= 12 && x_bytes <= (int64_t)0x7FFFFFFF;  // 31-bit buffer offsets
 }
 
 // Every workgroup encodes the bf16 rows itself (4x the bytes of their FP4
@@ -1008,10 +1030,20 @@ bool linear_persist_pays(int M, int N, int K, int cus) {
   return M >= 2 && M <= 4 && G >= 10 && Ns >= 6 * cus;
 }
 
-hipError_t launch_linear_persist(const GemmArgs& p, hipStream_t stream) {
-  if (p.M > 16 || p.G > 12) return hipErrorInvalidValue;
+template <int MT, int D>
+static void launch_linear_persist_mt(const GemmArgs& p, hipStream_t stream) {
   const int grid = p.Ns < p.cus ? p.Ns : p.cus;
-  gemm_decode_persist_kernel<1, 12, 4, kASrcBf16><<<grid, 64 * p.G, 2 * reduce_lds_bytes<1, 1, 12>(), stream>>>(p);
+  gemm_decode_persist_kernel<MT, 12, D, kASrcBf16><<<grid, 64 * p.G, 2 * reduce_lds_bytes<MT, 1, 12>(), stream>>>(p);
+}
+
+hipError_t launch_linear_persist(const GemmArgs& p, hipStream_t stream) {
+  if (p.M < 1 || p.M > 32 || p.G > 12) return hipErrorInvalidValue;
+  // ring depth: as the GEMM-layout form at one row tile; at two, the
+  // encoding's registers are live beside the ring, which holds one step
+  if (p.M <= 16)
+    launch_linear_persist_mt<1, 4>(p, stream);
+  else
+    launch_linear_persist_mt<2, 1>(p, stream);
   return hipGetLastError();
 }
 

@@ -2,7 +2,7 @@
 FP4 GEMM (+ bias) in one call, the quantisation fused into the GEMM kernel
 for M <= 4 (the streaming small-M form, or its persistent form on wide N)
 and done through a workspace above that; the persistent form's fusion is
-also forced at M <= 16.
+also forced at M <= 32 (one or two row tiles).
 
 Bars: the oracle's GEMM tolerance (as for mxfp4_gemm_a4w4); the output is
 bitwise that of mxfp4_quant_1x32 followed by the small-M mxfp4_gemm_a4w4 up
@@ -162,7 +162,7 @@ def test_linear_deterministic_and_empty():
 
 PERSIST = [
     # name, M, N, K, problem kwargs, ldx padding: the quantisation fused into
-    # the small-M kernel's persistent form (M <= 16, at most 12 scale groups)
+    # the small-M kernel's persistent form (M <= 32, at most 12 scale groups)
     ("m1_1024x5120", 1, 1024, 5120, dict(seed=0, outliers=True), 0),
     ("m2_96x4128_edge", 2, 96, 4128, dict(seed=5, edge=True), 16),       # ragged K tile
     ("m5_17x96_bias", 5, 17, 96, dict(seed=9, with_bias=True), 8),
@@ -170,6 +170,12 @@ PERSIST = [
     ("m15_520x1056_edge", 15, 520, 1056, dict(seed=5, edge=True), 24),
     ("m16_5000x6144_bias", 16, 5000, 6144, dict(seed=3, outliers=True, with_bias=True), 0),  # 12 groups
     ("m16_34816x5120", 16, 34816, 5120, dict(seed=2, with_bias=True), 0),
+    # two row tiles
+    ("m17_300x640_bias", 17, 300, 640, dict(seed=6, with_bias=True), 8),
+    ("m24_520x4128_edge", 24, 520, 4128, dict(seed=5, edge=True), 16),   # 9 groups, ragged K tile
+    ("m31_96x1056_edge", 31, 96, 1056, dict(seed=4, edge=True), 24),
+    ("m32_5000x6144_bias", 32, 5000, 6144, dict(seed=3, outliers=True, with_bias=True), 0),  # 12 groups
+    ("m32_14336x4096", 32, 14336, 4096, dict(seed=1, with_bias=True), 0),
 ]
 
 
@@ -177,9 +183,11 @@ PERSIST = [
 def test_linear_persistent_form(name, M, N, K, kw, pad):
     # mxfp4_linear with the quantisation inside the persistent form (forced):
     # bitwise quantisation + the persistent GEMM and quantisation + the
-    # one-workgroup-per-strip GEMM (one group per wave in both), and the
-    # oracle bar (sampled columns at the widest shape).
+    # one-workgroup-per-strip GEMM (one group per wave in both; the latter
+    # only while it keeps one group per wave: at two row tiles up to 8
+    # groups), and the oracle bar (sampled columns at the widest shape).
     need_gpu()
+    G = -(-(-(-K // 128)) // 4)
     prob = inputs.linear_problem(M, N, K, **kw)
     W = mx.quantize_weight(dev_bf16(prob["w"]))
     mx.set_gemm_path(7)
@@ -187,7 +195,7 @@ def test_linear_persistent_form(name, M, N, K, kw, pad):
         y32, y16 = _linear(prob["x"], W, N, prob["bias"], ldx_pad=pad)
     finally:
         mx.set_gemm_path(0)
-    for path in (7, 8):
+    for path in ((7, 8) if M <= 16 or G <= 8 else (7,)):
         b = None if prob["bias"] is None else dev_bf16(prob["bias"])
         mx.set_gemm_path(path)
         try:
@@ -204,14 +212,15 @@ def test_linear_persistent_form(name, M, N, K, kw, pad):
 
 def test_persistent_encoding_every_bf16_value():
     # As the fused-encoding test above, through the persistent form's encoder
-    # (forced), 16, 5 and 1 rows at a time.
+    # (forced), 32, 20, 16, 5 and 1 rows at a time (every finite value in
+    # each 16-row half).
     need_gpu()
     u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     finite = u[(u & 0x7F80) != 0x7F80]
     rng = np.random.default_rng(8)
     K = 4096
-    vals = np.concatenate([rng.permutation(finite), np.zeros(16 * K - finite.size, np.uint16)])
-    x = vals.reshape(16, K)
+    half = lambda: np.concatenate([rng.permutation(finite), np.zeros(16 * K - finite.size, np.uint16)])
+    x = np.concatenate([half(), half()]).reshape(32, K)
     eye = np.zeros((K, K), dtype=np.uint16)
     eye[np.arange(K), np.arange(K)] = 0x3F80
     W = mx.quantize_weight(dev_bf16(eye))
@@ -220,7 +229,7 @@ def test_persistent_encoding_every_bf16_value():
     unsigned = lambda a: np.where(a == 0, np.float32(0), a)
     mx.set_gemm_path(7)
     try:
-        for r0, M in [(0, 16), (3, 5), (11, 5), (15, 1)]:
+        for r0, M in [(0, 32), (7, 20), (0, 16), (16, 16), (3, 5), (11, 5), (15, 1)]:
             y32, _ = _linear(x[r0:r0 + M], W, K, None)
             assert np.array_equal(unsigned(y32), unsigned(dq[r0:r0 + M])), (r0, M)
     finally:
