@@ -983,10 +983,17 @@ hipError_t launch_linear_decode(const GemmArgs& p, hipStream_t stream) {
   // N = 10240, M = 1 / 2: 11.81 / 12.15 -> 9.63 / 10.20; at M = 4 mixed,
   // N = 12288: 9.85 -> 10.59).  At M = 1 one strip everywhere (one row to
   // encode): K = 5120, N = 13312 / 14336: 9.20 / 9.44 -> 8.52 / 8.74 us;
-  // K = 8192, N = 14336: 13.07 -> 12.13.
+  // K = 8192, N = 14336: 13.07 -> 12.13.  At M = 2 past three strips per
+  // unit also one strip with 12 or 16 groups (waves even over the four
+  // SIMDs): K = 6144, N = 12800 / 16128: 10.45 / 11.31 -> 10.31 / 10.90 us;
+  // K = 8192, N = 12800 / 14336 / 16128: 12.78 / 13.30 / 14.15 -> 12.11 /
+  // 12.68 / 13.26; not with 10, 11 or 14 groups (K = 7168, N = 14336 /
+  // 16128: 12.27 / 12.99 -> 13.32 / 14.19; K = 5120, N = 16128: 10.15 ->
+  // 10.89).
   if (p.G <= 16) {
     const int kw = p.G;
-    const bool balance = (p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus && p.M <= 2) || p.M == 1;
+    const bool balance = (p.Ns > 2 * p.cus && p.Ns <= 3 * p.cus && p.M <= 2) || p.M == 1 ||
+                         (p.M == 2 && p.Ns > 3 * p.cus && p.G >= 12 && p.G % 4 == 0);
     return (p.Ns >= 1024 || p.Ns <= p.cus || balance) ? launch_linear_t<1, 1>(p, kw, 1, stream)
                                                       : launch_linear_t<2, 1>(p, kw, 1, stream);
   }
